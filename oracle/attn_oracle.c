@@ -1,0 +1,481 @@
+/*
+ * attn_oracle.c -- plain, slow, fp64 CPU oracle for tiled online-softmax attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, calls or
+ * includes this file; only the test-suite, the smoke check and the CPU-baseline
+ * leg of the benchmark load it (through oracle/__init__.py).  It shares no code,
+ * header, table or constant with the HIP kernels.
+ *
+ * What it computes (sources are the four web pages on tiled attention):
+ *   - "Sequence length doubles, inference time quadruples" (answer.freetools.me),
+ *     section "The mathematical nature of attention", displayed equation:
+ *         Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V
+ *   - "Flash Attention and Paged Attention" (ipipp.com), section 1: the forward
+ *     pass is three steps -- S = Q K^T, P = row-softmax(S), O = P V -- and
+ *     section 2: the method only keeps O and the softmax normalisation
+ *     statistics (here: LSE = log-sum-exp of each masked, scaled score row).
+ *   - same page, section 2, PyTorch call: is_causal=True (query i may attend
+ *     keys j <= i).  When the query rows are the last Nq of Nk positions (a
+ *     decode step or an appended chunk) the causal limit is aligned to the
+ *     bottom-right: query i sits at absolute position Nk - Nq + i.
+ *   - same page, section 3, PagedKVCache: the physical pool is
+ *     [num_blocks, 2, num_heads, block_size, head_dim], K at index 0, V at 1;
+ *     and "Chunked attention ... 70x slower" (cf-1.com), section 2.1: logical
+ *     block = token / block_size, physical block = block_table[logical block],
+ *     offset = token % block_size.
+ *   - same ipipp.com page, section 2, the block-wise forward with running
+ *     max m and running sum l: oracle_tiled_online() follows that algorithm
+ *     step by step in fp64 (plus the mask); it exists only to pin the online
+ *     algebra against the two-pass definition.
+ *
+ * Every result is the plain definition, materialised: the full masked score
+ * matrix S (-inf outside the allowed set), a two-pass softmax P, then P V.
+ * Inputs are upcast exactly (bf16 -> fp64 and fp32 -> fp64 are exact).
+ *
+ * Preconditions (the definition is undefined otherwise): every query row has
+ * at least one allowed key.  A row with none yields NaN, as the definition does.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_BF16 0
+#define ORACLE_F32 1
+#define ORACLE_F64 2
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG -1
+#define ORACLE_ERR_TABLE -2
+#define ORACLE_ERR_ALLOC -3
+
+/* ---- element access: exact upcast of one stored element to fp64 ---------- */
+static double elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == ORACLE_BF16) {
+        /* bf16 is the top half of an IEEE binary32: shift into place. */
+        uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
+    return ((const double*)base)[idx];
+}
+
+static int elem_size(int dtype)
+{
+    return dtype == ORACLE_BF16 ? 2 : (dtype == ORACLE_F32 ? 4 : 8);
+}
+
+/* Number of keys query row i may attend.
+ * mask_mode 0: none (all nk keys).
+ * mask_mode 1: causal, bottom-right aligned: key j allowed iff j <= nk - nq + i.
+ *              For nq == nk this is the square is_causal rule j <= i. */
+static int64_t allowed_keys(int mask_mode, int64_t i, int64_t nq, int64_t nk)
+{
+    if (mask_mode == 0) return nk;
+    int64_t lim = nk - nq + i + 1;
+    if (lim < 0) lim = 0;
+    if (lim > nk) lim = nk;
+    return lim;
+}
+
+/*
+ * The definition for a block of query rows against one key/value set.
+ *   S[i][j] = scale * sum_c Q[i][c] K[j][c]          (j allowed) else -inf
+ *   P[i][j] = exp(S[i][j] - m_i) / sum_j' exp(S[i][j'] - m_i),  m_i = max_j S[i][j]
+ *   O[i][c] = sum_j P[i][j] V[j][c]
+ *   LSE[i]  = m_i + ln sum_j exp(S[i][j] - m_i)
+ * Q: [nq][d], K, V: [nk][d], all fp64, row-major.  S and P are materialised
+ * as full nq x nk matrices in the caller-provided scratch.
+ */
+static void attention_dense(const double* Q, const double* K, const double* V,
+                            int64_t nq, int64_t nk, int d, double scale,
+                            const int64_t* n_allowed, double* S, double* P,
+                            double* O, double* LSE)
+{
+    /* step 1: S = scale * Q K^T, masked */
+    for (int64_t i = 0; i < nq; ++i)
+        for (int64_t j = 0; j < nk; ++j) {
+            if (j < n_allowed[i]) {
+                double acc = 0.0;
+                for (int c = 0; c < d; ++c) acc += Q[i * d + c] * K[j * d + c];
+                S[i * nk + j] = scale * acc;
+            } else {
+                S[i * nk + j] = -INFINITY;
+            }
+        }
+    /* step 2: P = row-softmax(S), two passes (max, then exp-sum) */
+    for (int64_t i = 0; i < nq; ++i) {
+        double m = -INFINITY;
+        for (int64_t j = 0; j < nk; ++j)
+            if (S[i * nk + j] > m) m = S[i * nk + j];
+        double l = 0.0;
+        for (int64_t j = 0; j < nk; ++j) l += exp(S[i * nk + j] - m);
+        for (int64_t j = 0; j < nk; ++j) P[i * nk + j] = exp(S[i * nk + j] - m) / l;
+        if (LSE) LSE[i] = m + log(l);
+    }
+    /* step 3: O = P V */
+    for (int64_t i = 0; i < nq; ++i)
+        for (int c = 0; c < d; ++c) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < nk; ++j) acc += P[i * nk + j] * V[j * d + c];
+            O[i * d + c] = acc;
+        }
+}
+
+/* Copy one [rows][d] head slice out of a [B,H,rows,d] tensor into fp64. */
+static void load_head(const void* x, int dtype, int64_t bh, int64_t rows, int d, double* out)
+{
+    int64_t base = bh * rows * d;
+    for (int64_t r = 0; r < rows * d; ++r) out[r] = elem(x, dtype, base + r);
+}
+
+/*
+ * Contiguous attention over [B,H,Nq,d] queries and [B,H,Nk,d] keys/values.
+ * o: fp64 [B,H,Nq,d]; lse: fp64 [B,H,Nq] (may be NULL).
+ */
+int oracle_attention(const void* q, const void* k, const void* v, int dtype,
+                     int B, int H, int Nq, int Nk, int d, double scale, int mask_mode,
+                     double* o, double* lse)
+{
+    if (!q || !k || !v || !o || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ORACLE_ERR_ARG;
+    if (dtype < ORACLE_BF16 || dtype > ORACLE_F64 || mask_mode < 0 || mask_mode > 1) return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)B * H; ++bh) {
+        double* Q = malloc(sizeof(double) * Nq * d);
+        double* K = malloc(sizeof(double) * Nk * d);
+        double* V = malloc(sizeof(double) * Nk * d);
+        double* S = malloc(sizeof(double) * (int64_t)Nq * Nk);
+        double* P = malloc(sizeof(double) * (int64_t)Nq * Nk);
+        int64_t* lim = malloc(sizeof(int64_t) * Nq);
+        if (!Q || !K || !V || !S || !P || !lim) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ALLOC;
+        } else {
+            load_head(q, dtype, bh, Nq, d, Q);
+            load_head(k, dtype, bh, Nk, d, K);
+            load_head(v, dtype, bh, Nk, d, V);
+            for (int64_t i = 0; i < Nq; ++i) lim[i] = allowed_keys(mask_mode, i, Nq, Nk);
+            attention_dense(Q, K, V, Nq, Nk, d, scale, lim, S, P, o + bh * Nq * d,
+                            lse ? lse + bh * Nq : NULL);
+        }
+        free(Q); free(K); free(V); free(S); free(P); free(lim);
+    }
+    return err;
+}
+
+/*
+ * Selected rows only (for workloads too large to evaluate in full): sample s
+ * is query row rows[s] of head (bidx[s], hidx[s]).  o: fp64 [n][d], lse: [n].
+ * Each sample materialises its full masked score row against all Nk keys.
+ */
+int oracle_attention_rows(const void* q, const void* k, const void* v, int dtype,
+                          int B, int H, int Nq, int Nk, int d, double scale, int mask_mode,
+                          int n, const int* bidx, const int* hidx, const int* rows,
+                          double* o, double* lse)
+{
+    if (!q || !k || !v || !o || !bidx || !hidx || !rows || n < 0) return ORACLE_ERR_ARG;
+    for (int s = 0; s < n; ++s)
+        if (bidx[s] < 0 || bidx[s] >= B || hidx[s] < 0 || hidx[s] >= H || rows[s] < 0 || rows[s] >= Nq)
+            return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < n; ++s) {
+        int64_t bh = (int64_t)bidx[s] * H + hidx[s];
+        double* Q = malloc(sizeof(double) * d);
+        double* K = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* V = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* S = malloc(sizeof(double) * Nk);
+        double* P = malloc(sizeof(double) * Nk);
+        if (!Q || !K || !V || !S || !P) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ALLOC;
+        } else {
+            for (int c = 0; c < d; ++c) Q[c] = elem(q, dtype, (bh * Nq + rows[s]) * d + c);
+            load_head(k, dtype, bh, Nk, d, K);
+            load_head(v, dtype, bh, Nk, d, V);
+            int64_t lim = allowed_keys(mask_mode, rows[s], Nq, Nk);
+            attention_dense(Q, K, V, 1, Nk, d, scale, &lim, S, P, o + (int64_t)s * d,
+                            lse ? lse + s : NULL);
+        }
+        free(Q); free(K); free(V); free(S); free(P);
+    }
+    return err;
+}
+
+/* ---- paged KV cache ------------------------------------------------------ */
+
+/* Element index of (physical block pb, kv in {0:K, 1:V}, head h, in-block
+ * offset off, channel c) in the [num_blocks, 2, H, block_size, d] pool. */
+static int64_t pool_index(int64_t pb, int kv, int h, int off, int c, int H, int bs, int d)
+{
+    return (((pb * 2 + kv) * H + h) * bs + off) * (int64_t)d + c;
+}
+
+/* Per-token gather of request r, head h: token t lives in logical block
+ * t / bs, at offset t % bs of physical block block_table[r][t / bs].
+ * Returns ORACLE_ERR_TABLE if an entry needed is outside [0, num_blocks). */
+static int gather_head(const void* pool, int dtype, const int* table, int maxb, int num_blocks,
+                       int r, int h, int64_t ctx, int H, int bs, int d, double* K, double* V)
+{
+    for (int64_t t = 0; t < ctx; ++t) {
+        int64_t lb = t / bs;
+        int off = (int)(t % bs);
+        if (lb >= maxb) return ORACLE_ERR_TABLE;
+        int64_t pb = table[(int64_t)r * maxb + lb];
+        if (pb < 0 || pb >= num_blocks) return ORACLE_ERR_TABLE;
+        for (int c = 0; c < d; ++c) {
+            K[t * d + c] = elem(pool, dtype, pool_index(pb, 0, h, off, c, H, bs, d));
+            V[t * d + c] = elem(pool, dtype, pool_index(pb, 1, h, off, c, H, bs, d));
+        }
+    }
+    return ORACLE_OK;
+}
+
+static int64_t prefix_q(const int* q_lens, int r)
+{
+    int64_t s = 0;
+    for (int i = 0; i < r; ++i) s += q_lens[i];
+    return s;
+}
+
+static int check_paged_args(const int* ctx_lens, const int* q_lens, int num_seqs, int H, int d,
+                            int bs, int maxb)
+{
+    if (num_seqs < 1 || H < 1 || d < 1 || bs < 1 || maxb < 1) return ORACLE_ERR_ARG;
+    for (int r = 0; r < num_seqs; ++r)
+        if (q_lens[r] < 1 || ctx_lens[r] < q_lens[r]) return ORACLE_ERR_ARG;
+    return ORACLE_OK;
+}
+
+/*
+ * Paged attention, all rows.  q: packed [sum(q_lens), H, d] (request r's rows
+ * start at sum_{s<r} q_lens[s]); pool: [num_blocks, 2, H, bs, d];
+ * block_table: int32 [num_seqs][maxb]; ctx_lens includes the q_lens new tokens.
+ * Query row i of request r attends keys j <= ctx_r - q_r + i.
+ * o: fp64 [sum(q_lens), H, d]; lse: fp64 [sum(q_lens), H] (may be NULL).
+ */
+int oracle_paged_attention(const void* q, int q_dtype, const void* pool, int pool_dtype,
+                           const int* block_table, const int* ctx_lens, const int* q_lens,
+                           int num_seqs, int H, int d, int bs, int maxb, int num_blocks,
+                           double scale, double* o, double* lse)
+{
+    if (!q || !pool || !block_table || !ctx_lens || !q_lens || !o) return ORACLE_ERR_ARG;
+    int rc = check_paged_args(ctx_lens, q_lens, num_seqs, H, d, bs, maxb);
+    if (rc) return rc;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t rh = 0; rh < (int64_t)num_seqs * H; ++rh) {
+        int r = (int)(rh / H), h = (int)(rh % H);
+        int64_t ctx = ctx_lens[r], nq = q_lens[r], row0 = prefix_q(q_lens, r);
+        double* Q = malloc(sizeof(double) * nq * d);
+        double* K = malloc(sizeof(double) * ctx * d);
+        double* V = malloc(sizeof(double) * ctx * d);
+        double* S = malloc(sizeof(double) * nq * ctx);
+        double* P = malloc(sizeof(double) * nq * ctx);
+        double* O = malloc(sizeof(double) * nq * d);
+        double* L = malloc(sizeof(double) * nq);
+        int64_t* lim = malloc(sizeof(int64_t) * nq);
+        int my = ORACLE_OK;
+        if (!Q || !K || !V || !S || !P || !O || !L || !lim) my = ORACLE_ERR_ALLOC;
+        if (my == ORACLE_OK)
+            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, h, ctx, H, bs, d, K, V);
+        if (my == ORACLE_OK) {
+            for (int64_t i = 0; i < nq; ++i) {
+                for (int c = 0; c < d; ++c) Q[i * d + c] = elem(q, q_dtype, ((row0 + i) * H + h) * d + c);
+                lim[i] = allowed_keys(1, i, nq, ctx);
+            }
+            attention_dense(Q, K, V, nq, ctx, d, scale, lim, S, P, O, L);
+            for (int64_t i = 0; i < nq; ++i) {
+                for (int c = 0; c < d; ++c) o[((row0 + i) * H + h) * d + c] = O[i * d + c];
+                if (lse) lse[(row0 + i) * H + h] = L[i];
+            }
+        }
+        if (my != ORACLE_OK) {
+#pragma omp atomic write
+            err = my;
+        }
+        free(Q); free(K); free(V); free(S); free(P); free(O); free(L); free(lim);
+    }
+    return err;
+}
+
+/* Paged attention for sampled (request, head, row-in-request) triples.
+ * o: fp64 [n][d]; lse: [n]. */
+int oracle_paged_attention_rows(const void* q, int q_dtype, const void* pool, int pool_dtype,
+                                const int* block_table, const int* ctx_lens, const int* q_lens,
+                                int num_seqs, int H, int d, int bs, int maxb, int num_blocks,
+                                double scale, int n, const int* ridx, const int* hidx,
+                                const int* iidx, double* o, double* lse)
+{
+    if (!q || !pool || !block_table || !ctx_lens || !q_lens || !o || !ridx || !hidx || !iidx || n < 0)
+        return ORACLE_ERR_ARG;
+    int rc = check_paged_args(ctx_lens, q_lens, num_seqs, H, d, bs, maxb);
+    if (rc) return rc;
+    for (int s = 0; s < n; ++s)
+        if (ridx[s] < 0 || ridx[s] >= num_seqs || hidx[s] < 0 || hidx[s] >= H ||
+            iidx[s] < 0 || iidx[s] >= q_lens[ridx[s]])
+            return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < n; ++s) {
+        int r = ridx[s], h = hidx[s];
+        int64_t ctx = ctx_lens[r], nq = q_lens[r], i = iidx[s];
+        int64_t row = prefix_q(q_lens, r) + i;
+        double* Q = malloc(sizeof(double) * d);
+        double* K = malloc(sizeof(double) * ctx * d);
+        double* V = malloc(sizeof(double) * ctx * d);
+        double* S = malloc(sizeof(double) * ctx);
+        double* P = malloc(sizeof(double) * ctx);
+        int my = ORACLE_OK;
+        if (!Q || !K || !V || !S || !P) my = ORACLE_ERR_ALLOC;
+        if (my == ORACLE_OK)
+            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, h, ctx, H, bs, d, K, V);
+        if (my == ORACLE_OK) {
+            for (int c = 0; c < d; ++c) Q[c] = elem(q, q_dtype, (row * H + h) * d + c);
+            int64_t lim = allowed_keys(1, i, nq, ctx);
+            attention_dense(Q, K, V, 1, ctx, d, scale, &lim, S, P, o + (int64_t)s * d,
+                            lse ? lse + s : NULL);
+        }
+        if (my != ORACLE_OK) {
+#pragma omp atomic write
+            err = my;
+        }
+        free(Q); free(K); free(V); free(S); free(P);
+    }
+    return err;
+}
+
+/*
+ * Bit-exact gather: copies the stored bytes of K and V of every request,
+ * tokens [0, ctx_r), into packed token-major [sum(ctx_lens), H, d] outputs
+ * (request r's tokens start at sum_{s<r} ctx_lens[s]).  No arithmetic.
+ */
+int oracle_paged_gather(const void* pool, int dtype, const int* block_table, const int* ctx_lens,
+                        int num_seqs, int H, int d, int bs, int maxb, int num_blocks,
+                        void* k_out, void* v_out)
+{
+    if (!pool || !block_table || !ctx_lens || !k_out || !v_out || num_seqs < 1 || H < 1 || d < 1 ||
+        bs < 1 || maxb < 1)
+        return ORACLE_ERR_ARG;
+    int es = elem_size(dtype);
+    int64_t tok0 = 0;
+    for (int r = 0; r < num_seqs; ++r) {
+        for (int64_t t = 0; t < ctx_lens[r]; ++t) {
+            int64_t lb = t / bs;
+            int off = (int)(t % bs);
+            if (lb >= maxb) return ORACLE_ERR_TABLE;
+            int64_t pb = block_table[(int64_t)r * maxb + lb];
+            if (pb < 0 || pb >= num_blocks) return ORACLE_ERR_TABLE;
+            for (int h = 0; h < H; ++h) {
+                int64_t dst = ((tok0 + t) * H + h) * (int64_t)d;
+                memcpy((char*)k_out + dst * es, (const char*)pool + pool_index(pb, 0, h, off, 0, H, bs, d) * es,
+                       (size_t)d * es);
+                memcpy((char*)v_out + dst * es, (const char*)pool + pool_index(pb, 1, h, off, 0, H, bs, d) * es,
+                       (size_t)d * es);
+            }
+        }
+        tok0 += ctx_lens[r];
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * The block-wise forward with online softmax (ipipp.com page, section 2),
+ * one head, in fp64, with the same mask as above.  Keys are visited in blocks
+ * of block_size; per row it keeps the running max m (start -inf), running sum
+ * l (start 0) and an unnormalised output; each block rescales the old l and O
+ * by exp(m_old - m_new) and adds exp(S - m_new) and exp(S - m_new) V; O is
+ * divided by l once at the end.  Used only to check that this algorithm and
+ * the two-pass definition agree.
+ */
+int oracle_tiled_online(const void* q, const void* k, const void* v, int dtype, int Nq, int Nk, int d,
+                        double scale, int mask_mode, int block_size, double* o, double* lse)
+{
+    if (!q || !k || !v || !o || Nq < 1 || Nk < 1 || d < 1 || block_size < 1) return ORACLE_ERR_ARG;
+    double* m = malloc(sizeof(double) * Nq);
+    double* l = malloc(sizeof(double) * Nq);
+    double* S = malloc(sizeof(double) * (int64_t)Nq * block_size);
+    if (!m || !l || !S) { free(m); free(l); free(S); return ORACLE_ERR_ALLOC; }
+    for (int64_t i = 0; i < Nq; ++i) {
+        m[i] = -INFINITY;
+        l[i] = 0.0;
+        for (int c = 0; c < d; ++c) o[i * d + c] = 0.0;
+    }
+    for (int64_t start = 0; start < Nk; start += block_size) {
+        int64_t end = start + block_size < Nk ? start + block_size : Nk;
+        int64_t nb = end - start;
+        for (int64_t i = 0; i < Nq; ++i) {
+            int64_t lim = allowed_keys(mask_mode, i, Nq, Nk);
+            double bmax = -INFINITY;
+            for (int64_t j = 0; j < nb; ++j) {
+                double s = -INFINITY;
+                if (start + j < lim) {
+                    double acc = 0.0;
+                    for (int c = 0; c < d; ++c) acc += elem(q, dtype, i * d + c) * elem(k, dtype, (start + j) * d + c);
+                    s = acc * scale;
+                }
+                S[i * block_size + j] = s;
+                if (s > bmax) bmax = s;
+            }
+            double m_new = m[i] > bmax ? m[i] : bmax;
+            double alpha = exp(m[i] - m_new);
+            double psum = 0.0;
+            for (int c = 0; c < d; ++c) o[i * d + c] *= alpha;
+            for (int64_t j = 0; j < nb; ++j) {
+                double p = exp(S[i * block_size + j] - m_new);
+                psum += p;
+                for (int c = 0; c < d; ++c) o[i * d + c] += p * elem(v, dtype, (start + j) * d + c);
+            }
+            l[i] = alpha * l[i] + psum;
+            m[i] = m_new;
+        }
+    }
+    for (int64_t i = 0; i < Nq; ++i) {
+        for (int c = 0; c < d; ++c) o[i * d + c] /= l[i];
+        if (lse) lse[i] = m[i] + log(l[i]);
+    }
+    free(m); free(l); free(S);
+    return ORACLE_OK;
+}
+
+/*
+ * Merge of partial results over a partition of one row's keys: part s holds
+ * its normalised output O_s and its log-sum-exp lse_s.  With M = max_s lse_s,
+ * LSE = M + ln sum_s exp(lse_s - M) and O = sum_s exp(lse_s - LSE) O_s.  This
+ * is the same rescaling algebra as the online update above, applied once.
+ */
+int oracle_lse_merge(int nparts, int d, const double* o_parts, const double* lse_parts,
+                     double* o, double* lse)
+{
+    if (nparts < 1 || d < 1 || !o_parts || !lse_parts || !o) return ORACLE_ERR_ARG;
+    double M = -INFINITY;
+    for (int s = 0; s < nparts; ++s)
+        if (lse_parts[s] > M) M = lse_parts[s];
+    double sum = 0.0;
+    for (int s = 0; s < nparts; ++s) sum += exp(lse_parts[s] - M);
+    double L = M + log(sum);
+    for (int c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int s = 0; s < nparts; ++s) acc += exp(lse_parts[s] - L) * o_parts[(int64_t)s * d + c];
+        o[c] = acc;
+    }
+    if (lse) *lse = L;
+    return ORACLE_OK;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
