@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled online-softmax attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * causal prefill, bf16, B=16 H=32 N=8192 d=128 (attn_prefill_fwd, one launch)
+  * paged decode, bf16, 64 requests x 1 query, ctx ~ U[512, 16384], 16-token
+    pages scattered in the pool (paged_attn_fwd: split kernel + combine kernel)
+Inputs are generated on the GPU before timing (resident in HBM).  The line
+printed reports prefill TFLOP/s as `value` (algorithmic FLOPs = 4*d per
+allowed (query, key) pair, per launch, over the launch's average duration
+measured with HIP events on the launch stream) and the decode KV GB/s
+(algorithmic bytes: K and V of every context token read once, plus q, o and
+the block table) under "decode".  The oracle (fp64, CPU) is timed on a
+bounded sample of the same prefill workload as `cpu_baseline`.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+METRIC = "causal prefill TFLOP/s + paged-decode KV GB/s (and % roofline), 1 MI355X"
+KERNEL_SOURCES = ["attn_mfma_core.h", "attn_mfma_kernel.h", "prefill_gfx950.hip", "paged_gfx950.hip",
+                  "attn_api.hip", "attn_internal.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        h.update((ROOT / "tiled_online_softmax_attention_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_key):
+    """HBM bytes per launch from committed PMC summaries (profiles/pmc_*.txt),
+    valid only if they were taken on the current kernel sources."""
+    f = ROOT / "profiles" / ("pmc_%s.txt" % kernel_key)
+    if not f.exists():
+        return None
+    kv = {}
+    for line in f.read_text().splitlines():
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def prefill_flops(B, H, N, d, causal):
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 4.0 * d * pairs * B * H
+
+
+def prefill_bytes(B, H, N, d, elem=2):
+    return B * H * N * d * elem * 4 + B * H * N * 4   # q, k, v read + o written + lse
+
+
+def paged_bytes(ctx_lens, q_lens, H, d, block_size, elem=2):
+    ctx = sum(ctx_lens)
+    tq = sum(q_lens)
+    pages = sum((c + block_size - 1) // block_size for c in ctx_lens)
+    return 2 * ctx * H * d * elem + 2 * tq * H * d * elem + tq * H * 4 + pages * 4
+
+
+def paged_flops(ctx_lens, q_lens, d, H):
+    pairs = 0
+    for c, q in zip(ctx_lens, q_lens):
+        pairs += q * (c - q) + q * (q + 1) // 2
+    return 4.0 * d * pairs * H
+
+
+class EventTimer:
+    """Average duration of one region per step, from HIP events on the stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle):
+    """Oracle on sampled C3 rows until ~budget_s of CPU work; TFLOP/s on the
+    algorithmic FLOPs of those rows."""
+    import torch
+    from tiled_online_softmax_attention_amd import inputs
+    trip = inputs.sample_triples(cfg.seed + 1000, 4096, (cfg.B, cfg.H, cfg.N))
+    done_rows, flops, t_total = 0, 0.0, 0.0
+    batch = 16
+    for s in range(0, len(trip), batch):
+        chunk = trip[s:s + batch]
+        heads = sorted({(b, h) for b, h, _ in chunk})
+        idx = {bh: i for i, bh in enumerate(heads)}
+        qs = torch.stack([q[b, h] for b, h in heads]).unsqueeze(0).cpu()
+        ks = torch.stack([k[b, h] for b, h in heads]).unsqueeze(0).cpu()
+        vs = torch.stack([v[b, h] for b, h in heads]).unsqueeze(0).cpu()
+        t0 = time.perf_counter()
+        oracle.attention_rows(qs, ks, vs, cfg.scale, True, [0] * len(chunk), [idx[(b, h)] for b, h, _ in chunk],
+                              [r for _, _, r in chunk])
+        t_total += time.perf_counter() - t0
+        done_rows += len(chunk)
+        flops += sum(4.0 * cfg.d * (r + 1) for _, _, r in chunk)
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d seeded (b,h,row) rows of the 16x32x8192x128 causal prefill, full-length fp64 rows, "
+                      "%.1f s" % (done_rows, t_total)}
+
+
+def cpu_baseline_decode(pi, budget_s, oracle):
+    """Oracle on the first requests of the C4 batch until ~budget_s; KV GB/s."""
+    import torch
+    ctx = pi.ctx_lens.cpu().tolist()
+    t_total, nbytes, nreq = 0.0, 0.0, 0
+    pool_cpu = None
+    for r in range(len(ctx)):
+        if pool_cpu is None:
+            pool_cpu = pi.pool.cpu()
+        rows = list(range(pi.H))
+        t0 = time.perf_counter()
+        oracle.paged_attention_rows(pi.q.cpu(), pool_cpu, pi.block_table.cpu(), pi.ctx_lens.cpu(), pi.q_lens.cpu(),
+                                    pi.block_size, pi.scale, [r] * pi.H, rows, [0] * pi.H)
+        t_total += time.perf_counter() - t0
+        nbytes += paged_bytes([ctx[r]], [1], pi.H, pi.d, pi.block_size)
+        nreq += 1
+        if t_total >= budget_s:
+            break
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--probe-copy", action="store_true",
+                    help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5"], default="all")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each box has one MI355X); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_online_softmax_attention_amd as attn
+    from tiled_online_softmax_attention_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    c3, c4 = inputs.C3, inputs.C4
+    do_prefill = args.only in ("all", "prefill")
+    do_decode = args.only in ("all", "decode")
+    extra = {}
+
+    if args.probe_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print("probe copy: 1073741824 bytes read and written", file=sys.stderr, flush=True)
+
+    print("generating inputs", file=sys.stderr, flush=True)
+    if do_prefill:
+        q, k, v = inputs.prefill_inputs(c3, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((c3.B, c3.H, c3.N), dtype=torch.float32, device=dev)
+    if do_decode:
+        pi = inputs.paged_inputs(c4, dev)
+        ctx_list = pi.ctx_lens.cpu().tolist()
+        ql_list = pi.q_lens.cpu().tolist()
+        max_ctx = max(ctx_list)
+        ws_bytes = attn.paged_attn_workspace_bytes(pi.num_seqs, pi.H, pi.d, pi.block_size, 1, max_ctx)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        od = torch.empty_like(pi.q)
+        lsed = torch.empty(pi.q.shape[:2], dtype=torch.float32, device=dev)
+    if args.only == "c2":
+        c2 = inputs.C2
+        q2, k2, v2 = inputs.prefill_inputs(c2, dev)
+        o2 = torch.empty_like(q2)
+        l2 = torch.empty((c2.B, c2.H, c2.N), dtype=torch.float32, device=dev)
+    if args.only == "c5":
+        c5 = inputs.C5
+        p5 = inputs.paged_inputs(c5, dev)
+        ctx5 = p5.ctx_lens.cpu().tolist()
+        ql5 = p5.q_lens.cpu().tolist()
+        ws5 = torch.empty(max(1, attn.paged_attn_workspace_bytes(p5.num_seqs, p5.H, p5.d, p5.block_size,
+                                                                  max(ql5), max(ctx5))), dtype=torch.uint8,
+                          device=dev)
+        o5 = torch.empty_like(p5.q)
+        l5 = torch.empty(p5.q.shape[:2], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    t_pre = EventTimer(torch)
+    t_dec = EventTimer(torch)
+    t_aux = EventTimer(torch)
+
+    def step(record):
+        if do_prefill:
+            e = t_pre.start() if record else None
+            attn.prefill(q, k, v, True, c3.scale, out=o, lse=lse)
+            if record:
+                t_pre.stop(e)
+        if do_decode:
+            e = t_dec.start() if record else None
+            attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
+                                 max_q_len=1, max_ctx_len=max_ctx, out=od, lse=lsed, workspace=ws)
+            if record:
+                t_dec.stop(e)
+        if args.only == "c2":
+            e = t_aux.start() if record else None
+            attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
+            if record:
+                t_aux.stop(e)
+        if args.only == "c5":
+            e = t_aux.start() if record else None
+            attn.paged_attention(p5.q, p5.pool, p5.block_table, p5.ctx_lens, p5.q_lens, p5.block_size, p5.scale,
+                                 max_q_len=max(ql5), max_ctx_len=max(ctx5), out=o5, lse=l5, workspace=ws5)
+            if record:
+                t_aux.stop(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "causal prefill bf16 16x32x8192x128 + paged decode bf16 64 req x 1 query, "
+                                  "ctx U[512,16384], 16-token pages, H=32, d=128",
+                      "global_batch": c3.B, "seq_len": c3.N, "parallelism": "none (1 GPU)"}}
+    if do_prefill:
+        ms = t_pre.mean_ms()
+        fl = prefill_flops(c3.B, c3.H, c3.N, c3.d, True)
+        tf = fl / (ms * 1e-3) / 1e12
+        res["value"] = round(tf, 2)
+        traffic = read_traffic("prefill_c3")
+        res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                           "kernel": "prefill_bf16_kernel<128>", "launch_ms": round(ms, 4),
+                           "flops_per_launch": fl, "algorithmic_bytes_per_launch":
+                               prefill_bytes(c3.B, c3.H, c3.N, c3.d)}
+    if do_decode:
+        ms = t_dec.mean_ms()
+        nb = paged_bytes(ctx_list, ql_list, pi.H, pi.d, pi.block_size)
+        gbs = nb / (ms * 1e-3) / 1e9
+        res["decode"] = {"metric": "paged-decode KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
+                         "launch_ms": round(ms, 4), "bytes_per_call": nb, "sum_ctx": sum(ctx_list),
+                         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS,
+                                      "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4),
+                                      "traffic": read_traffic("decode_c4"),
+                                      "kernels": "paged_decode_kernel<128,16> + paged_combine_kernel<128>"}}
+        if not do_prefill:
+            res["value"], res["unit"] = round(gbs, 1), "GB/s"
+    if args.only == "c2":
+        ms = t_aux.mean_ms()
+        c2 = inputs.C2
+        fl = prefill_flops(c2.B, c2.H, c2.N, c2.d, True)
+        res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
+        res["config"]["workload"] = "causal prefill bf16 1x32x2048x128"
+        res["launch_ms"] = round(ms, 4)
+    if args.only == "c5":
+        ms = t_aux.mean_ms()
+        fl = paged_flops(ctx5, ql5, p5.d, p5.H)
+        nb = paged_bytes(ctx5, ql5, p5.H, p5.d, p5.block_size)
+        res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
+        res["config"]["workload"] = "paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], 32-token pages"
+        res["launch_ms"] = round(ms, 4)
+        res["kv_gbps"] = round(nb / (ms * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline and args.only in ("all", "prefill", "decode"):
+        import oracle
+        print("timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+        if do_prefill:
+            res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, c3, args.cpu_seconds, oracle)
+        if do_decode:
+            cb = cpu_baseline_decode(pi, args.cpu_seconds * 0.5, oracle)
+            if do_prefill:
+                res["cpu_baseline"]["decode"] = cb
+            else:
+                res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) tiled online-softmax attention library
+ *           (libattn_gfx950.so).
+ *
+ * What is computed (the four web pages on tiled attention are the source):
+ *   O = softmax(scale * Q K^T) V  row by row, with an optional causal mask
+ *   ("Sequence length doubles, inference time quadruples", section "The
+ *   mathematical nature of attention", attention equation), evaluated tile by
+ *   tile with a running max m and running sum l so that no score matrix ever
+ *   reaches memory ("Flash Attention and Paged Attention", section 2, the
+ *   block-wise forward with online softmax).  Alongside O the library returns
+ *   the per-row softmax statistic LSE = m + ln(l), the natural-log log-sum-exp
+ *   of the row's masked, scaled scores (same page, section 2: the statistics
+ *   kept for the backward pass).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory),
+ *     row-major and contiguous as described per function.  The caller owns all
+ *     buffers.  The library allocates and frees nothing, keeps no pointer after
+ *     it returns and holds no mutable global state besides a cached device
+ *     property query.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Work is enqueued asynchronously; the function returns once the launches
+ *     are issued.  Buffers must stay alive until the stream reaches them.
+ *   - Return value: ATTN_OK (0) or a negative ATTN_ERR_* code.  Arguments are
+ *     validated on the host before anything is launched; on error nothing is
+ *     launched and no output is touched.  No exception or abort ever crosses
+ *     the boundary.  attn_strerror() names a code.
+ *   - Element types: ATTN_BF16 (bfloat16 storage, fp32 accumulation, bf16
+ *     MFMA for the contractions) or ATTN_F32 (fp32 storage and arithmetic).
+ *   - Scores are scaled by `scale` before the softmax; `scale` must be finite
+ *     and >= 0 (the pages use 1/sqrt(d)).
+ *   - head_dim d must be 64 or 128.  Pointers must be 16-byte aligned.
+ */
+#ifndef ATTN_GFX950_H
+#define ATTN_GFX950_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
+
+enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = -1,        /* a required pointer is NULL */
+    ATTN_ERR_SHAPE = -2,       /* a size is < 1, or too large for 32-bit grid indexing */
+    ATTN_ERR_HEAD_DIM = -3,    /* d not in {64, 128} */
+    ATTN_ERR_BLOCK_SIZE = -4,  /* block_size not in {16, 32} */
+    ATTN_ERR_DTYPE = -5,       /* element type not supported by this entry point */
+    ATTN_ERR_ALIGN = -6,       /* a pointer or stride is not 16-byte aligned */
+    ATTN_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
+    ATTN_ERR_LAUNCH = -8,      /* the HIP runtime rejected a launch */
+    ATTN_ERR_SCALE = -9,       /* scale is negative, NaN or infinite */
+    ATTN_ERR_DEVICE = -10      /* the current device is not a gfx950 GPU */
+};
+
+/*
+ * Prefill / dense attention (the block-wise forward of "Flash Attention and
+ * Paged Attention", section 2, with its is_causal flag).
+ *
+ *   q, k, v : [B, H, N, d] contiguous, element type `dtype`.
+ *   o       : [B, H, N, d] output, same type.
+ *   lse     : [B, H, N] fp32 output, natural log; may be NULL.
+ *   causal  : 0 = every query sees all N keys; 1 = query i sees keys j <= i.
+ *
+ * bf16: one launch of the MFMA kernel; key tiles entirely above the diagonal
+ * are skipped.  fp32: one launch of the fp32 vector kernel.
+ * Requires N >= 1 (every causal row sees at least its own key).
+ */
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     attn_dtype_t dtype, void* stream);
+
+/*
+ * Paged attention over a block-table KV cache: decode (q_len = 1) and chunked
+ * prefill (q_len > 1) for a whole batch in one step.
+ *
+ * Pool ("Flash Attention and Paged Attention", section 3): one tensor
+ * [num_blocks, 2, H, block_size, d], K at index 0 and V at index 1 of dim 1.
+ * Address of token t of request r, head h ("Chunked attention ... 70x slower",
+ * section 2.1): logical block lb = t / block_size, physical block
+ * pb = block_table[r][lb], offset t % block_size; element
+ *   k_pool + pb * kv_block_stride + (h * block_size + t % block_size) * d + c
+ * and likewise from v_pool.  For the pages' pool, k_pool = pool,
+ * v_pool = pool + H * block_size * d and kv_block_stride = 2 * H * block_size * d
+ * (elements); any other pool with the same per-block [H, block_size, d]
+ * layout works too.  Offsets are computed in 64-bit.
+ *
+ *   q           : packed [sum(q_lens), H, d] bf16; request r's rows start at
+ *                 sum_{s<r} q_lens[s].
+ *   block_table : int32 [num_seqs, max_blocks_per_seq] device; entries past
+ *                 ceil(ctx_lens[r] / block_size) are never read.
+ *   ctx_lens    : int32 [num_seqs] device: tokens in the cache for request r,
+ *                 INCLUDING its q_lens[r] new tokens (already written).
+ *   q_lens      : int32 [num_seqs] device: new query rows of request r.
+ *                 Row i of request r sits at position ctx - q_len + i and sees
+ *                 keys j <= ctx - q_len + i (causal, bottom-right aligned).
+ *   o           : packed [sum(q_lens), H, d] bf16 output.
+ *   lse         : packed [sum(q_lens), H] fp32 output; may be NULL.
+ *   max_q_len, max_ctx_len : host upper bounds of q_lens and ctx_lens, used
+ *                 only to size the grid (a larger bound costs only idle
+ *                 workgroups).
+ *   workspace   : device scratch of at least paged_attn_workspace_bytes(...)
+ *                 bytes (partial results of split contexts); contents on entry
+ *                 are ignored.  May be NULL when that function returns 0.
+ *
+ * Device-side contract (not checked on the device): 1 <= q_lens[r] <=
+ * ctx_lens[r] <= max_ctx_len, q_lens[r] <= max_q_len, every block-table entry
+ * needed lies in [0, num_blocks), and ceil(max_ctx_len / block_size) <=
+ * max_blocks_per_seq.  Slots of a request's last block past its context may
+ * hold anything (NaN included); they are never used.  Several requests may
+ * share (alias) physical blocks.
+ *
+ * Launches: one partial-attention kernel for the whole batch (per request,
+ * head, query tile and context split), plus one log-sum-exp combine kernel
+ * when some context is split.  Results do not depend on where the blocks sit
+ * in the pool (bit-identical under any permutation of physical blocks).
+ */
+int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                   int block_size, void* o, float* lse,
+                   int num_seqs, int H, int d, float scale, int max_blocks_per_seq,
+                   int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes paged_attn_fwd needs for these host bounds (0 if none). */
+size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size,
+                                  int max_q_len, int max_ctx_len);
+
+/*
+ * Gather through the block table ("Chunked attention ... 70x slower",
+ * section 2.1, the address function): copies K and V of every request,
+ * tokens [0, ctx_lens[r]), into packed token-major [sum(ctx_lens), H, d]
+ * outputs (request r's tokens start at sum_{s<r} ctx_lens[s]).  The copy is
+ * bit-exact and uses the same address computation as paged_attn_fwd.  It is
+ * a test and debug aid; the attention itself never gathers.
+ *   max_ctx_len : host upper bound of ctx_lens (grid sizing).
+ */
+int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                    const int32_t* ctx_lens, int block_size, int num_seqs, int H, int d,
+                    int max_blocks_per_seq, int64_t kv_block_stride, int max_ctx_len,
+                    attn_dtype_t dtype, void* k_out, void* v_out, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_strerror(int status);
+
+/* Library version, e.g. "attn_gfx950 1.0". */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_GFX950_H */

@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/attn.h declares, and rejects bad arguments with the
+documented status codes before anything is launched."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import tiled_online_softmax_attention_amd as attn
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "attn.h"
+
+OK, E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+
+
+def header_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = attn.library()
+    declared = header_functions()
+    assert set(declared) == set(attn.exported_symbols), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version():
+    assert attn.attn_strerror(0) == "ok"
+    for code in (E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV):
+        s = attn.attn_strerror(code)
+        assert s and s != "unknown attn status"
+    assert attn.attn_strerror(-1234) == "unknown attn status"
+    assert attn.attn_version().startswith("attn_gfx950")
+
+
+# fake, 256-aligned "device" addresses: never dereferenced, because every call
+# below fails validation on the host
+P = ctypes.c_void_p(1 << 20)
+P2 = ctypes.c_void_p(2 << 20)
+P3 = ctypes.c_void_p(3 << 20)
+P4 = ctypes.c_void_p(4 << 20)
+NULL = None
+
+
+def prefill(**kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=NULL, B=1, H=2, N=64, d=128, scale=0.125, causal=1, dtype=0, stream=NULL)
+    a.update(kw)
+    return attn.attn_prefill_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), E_NULL), (dict(k=NULL), E_NULL), (dict(v=NULL), E_NULL), (dict(o=NULL), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(N=0), E_SHAPE), (dict(N=-5), E_SHAPE),
+    (dict(d=96), E_HD), (dict(d=256), E_HD), (dict(d=0), E_HD),
+    (dict(dtype=7), E_DT),
+    (dict(q=ctypes.c_void_p((1 << 20) + 8)), E_AL), (dict(lse=ctypes.c_void_p((5 << 20) + 2)), E_AL),
+    (dict(scale=float("nan")), E_SCALE), (dict(scale=float("inf")), E_SCALE), (dict(scale=-0.5), E_SCALE),
+])
+def test_prefill_rejects(kw, code):
+    assert prefill(**kw) == code
+
+
+def paged(**kw):
+    a = dict(q=P, k_pool=P2, v_pool=P3, block_table=P4, ctx_lens=P, q_lens=P2, block_size=16, o=P3, lse=NULL,
+             num_seqs=4, H=8, d=128, scale=0.1, max_blocks_per_seq=64, kv_block_stride=2 * 8 * 16 * 128,
+             num_blocks=100, max_q_len=1, max_ctx_len=1024, dtype=0, workspace=NULL, workspace_bytes=0,
+             stream=NULL)
+    a.update(kw)
+    return attn.paged_attn_fwd(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), E_NULL), (dict(k_pool=NULL), E_NULL), (dict(v_pool=NULL), E_NULL),
+    (dict(block_table=NULL), E_NULL), (dict(ctx_lens=NULL), E_NULL), (dict(q_lens=NULL), E_NULL),
+    (dict(o=NULL), E_NULL),
+    (dict(num_seqs=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(max_q_len=0), E_SHAPE),
+    (dict(max_ctx_len=0), E_SHAPE), (dict(max_q_len=2000), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
+    (dict(max_blocks_per_seq=10), E_SHAPE),              # 1024 / 16 = 64 pages needed
+    (dict(kv_block_stride=100), E_SHAPE),
+    (dict(d=80), E_HD), (dict(block_size=8), E_BS), (dict(block_size=64), E_BS),
+    (dict(dtype=1), E_DT),
+    (dict(o=ctypes.c_void_p((3 << 20) + 4)), E_AL),
+    (dict(scale=-1.0), E_SCALE),
+])
+def test_paged_rejects(kw, code):
+    assert paged(**kw) == code
+
+
+def test_paged_workspace_required_when_split():
+    need = attn.paged_attn_workspace_bytes(4, 8, 128, 16, 1, 1 << 16)
+    assert need > 0
+    assert paged(max_ctx_len=1 << 16, max_blocks_per_seq=4096, workspace=NULL, workspace_bytes=0) == E_WS
+    assert paged(max_ctx_len=1 << 16, max_blocks_per_seq=4096, workspace=P, workspace_bytes=need - 1) == E_WS
+    assert paged(max_ctx_len=1 << 16, max_blocks_per_seq=4096, workspace=ctypes.c_void_p((1 << 20) + 16),
+                 workspace_bytes=need) == E_AL
+
+
+def test_workspace_plan_is_pure_and_sane():
+    # one split -> no workspace
+    assert attn.paged_attn_workspace_bytes(64, 32, 128, 16, 1, 64) == 0
+    a = attn.paged_attn_workspace_bytes(64, 32, 128, 16, 1, 16384)
+    b = attn.paged_attn_workspace_bytes(64, 32, 128, 16, 1, 16384)
+    assert a == b > 0
+    # bad geometry -> 0
+    assert attn.paged_attn_workspace_bytes(0, 32, 128, 16, 1, 100) == 0
+    assert attn.paged_attn_workspace_bytes(4, 32, 128, 8, 1, 100) == 0
+
+
+def gather(**kw):
+    a = dict(k_pool=P, v_pool=P2, block_table=P3, ctx_lens=P4, block_size=16, num_seqs=2, H=4, d=64,
+             max_blocks_per_seq=8, kv_block_stride=2 * 4 * 16 * 64, max_ctx_len=100, dtype=0, k_out=P,
+             v_out=P2, stream=NULL)
+    a.update(kw)
+    return attn.paged_kv_gather(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k_pool=NULL), E_NULL), (dict(k_out=NULL), E_NULL), (dict(num_seqs=0), E_SHAPE),
+    (dict(max_blocks_per_seq=2), E_SHAPE), (dict(d=32), E_HD), (dict(block_size=24), E_BS),
+    (dict(dtype=3), E_DT), (dict(v_out=ctypes.c_void_p((2 << 20) + 2)), E_AL),
+])
+def test_gather_rejects(kw, code):
+    assert gather(**kw) == code
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert prefill() == E_DEV

@@ -1,0 +1,219 @@
+"""GPU parity of paged_attn_fwd and paged_kv_gather (through the C ABI)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_online_softmax_attention_amd as attn
+from tiled_online_softmax_attention_amd import inputs
+from parity import check_close, log
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+class env_split:
+    """Force the context split size (tokens) for one call."""
+
+    def __init__(self, tokens):
+        self.tokens = tokens
+
+    def __enter__(self):
+        self.old = os.environ.get("ATTN_SPLIT_TOKENS")
+        if self.tokens is not None:
+            os.environ["ATTN_SPLIT_TOKENS"] = str(self.tokens)
+
+    def __exit__(self, *a):
+        if self.tokens is not None:
+            if self.old is None:
+                os.environ.pop("ATTN_SPLIT_TOKENS", None)
+            else:
+                os.environ["ATTN_SPLIT_TOKENS"] = self.old
+
+
+def make(ctx, ql, H=4, d=128, bs=16, seed=1, **kw):
+    return inputs.build_paged(torch.tensor(ctx, dtype=torch.int32), torch.tensor(ql, dtype=torch.int32), H, d, bs,
+                              seed, DEV, **kw)
+
+
+def run(pi, split=None, name="paged"):
+    log("%s: num_seqs=%d H=%d d=%d bs=%d ctx=%s q=%s split=%s" % (
+        name, pi.num_seqs, pi.H, pi.d, pi.block_size, pi.ctx_lens.tolist()[:8], pi.q_lens.tolist()[:8], split))
+    with env_split(split):
+        o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                      pi.scale)
+        torch.cuda.synchronize()
+    return o, lse
+
+
+def check_full(pi, split=None, name="paged"):
+    o, lse = run(pi, split, name)
+    o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                          pi.scale)
+    check_close(name, o, o_ref, lse, l_ref, torch.bfloat16)
+    return o, lse
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("split", [None, 64])
+def test_decode_ragged(bs, d, split):
+    ctx = [1, 15, 16, 17, 100, 513, 1030, 2047]
+    pi = make(ctx, [1] * len(ctx), H=3, d=d, bs=bs, seed=bs + d)
+    check_full(pi, split, "decode bs%d d%d" % (bs, d))
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("split", [None, 256])
+def test_small_q_decode_path(bs, split):
+    # q_len 2..4 goes through the vector decode kernel, one query row per workgroup
+    ctx = [4, 40, 333, 1000]
+    pi = make(ctx, [2, 4, 3, 4], H=2, bs=bs, seed=3)
+    check_full(pi, split, "decode q<=4 bs%d" % bs)
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("split", [None, 128, 320])
+def test_chunk_ragged(bs, d, split):
+    ctx = [5, 129, 700, 1200]
+    ql = [5, 129, 200, 77]
+    pi = make(ctx, ql, H=2, d=d, bs=bs, seed=7 + bs)
+    check_full(pi, split, "chunk bs%d d%d" % (bs, d))
+
+
+def test_chunk_mixed_with_decode_rows():
+    ctx = [900, 64, 1, 300]
+    ql = [300, 1, 1, 300]
+    pi = make(ctx, ql, H=4, bs=32, seed=21)
+    check_full(pi, None, "mixed")
+
+
+def test_permutation_bit_identity_and_aliasing():
+    """Same logical K/V in two different physical layouts (and with a second
+    request aliasing the first one's blocks): bit-identical outputs."""
+    H, d, bs = 4, 128, 16
+    ctx = torch.tensor([777, 777, 50], dtype=torch.int32)
+    ql = torch.tensor([1, 1, 1], dtype=torch.int32)
+    a = inputs.build_paged(ctx, ql, H, d, bs, seed=31, device=DEV)
+    # permuted copy: move every block to a new random slot
+    perm = torch.randperm(a.num_blocks, generator=torch.Generator().manual_seed(99)).to(DEV)
+    pool2 = torch.empty_like(a.pool)
+    pool2[perm] = a.pool
+    table2 = a.block_table.clone()
+    valid = table2 >= 0
+    table2[valid] = perm[table2[valid].long()].to(torch.int32)
+    # alias: request 1 reads request 0's blocks (its own K/V are identical then)
+    table_alias = a.block_table.clone()
+    table_alias[1] = table_alias[0]
+    q = a.q.clone()
+    q[1] = q[0]
+    for split in (None, 128):
+        with env_split(split):
+            o1, l1 = attn.paged_attention(q, a.pool, a.block_table, a.ctx_lens, a.q_lens, bs)
+            o2, l2 = attn.paged_attention(q, pool2, table2, a.ctx_lens, a.q_lens, bs)
+            o3, l3 = attn.paged_attention(q, a.pool, table_alias, a.ctx_lens, a.q_lens, bs)
+            torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        assert torch.equal(o3[0], o3[1]) and torch.equal(o3[0], o1[0]) and torch.equal(o3[2], o1[2])
+
+
+def test_repeat_determinism():
+    pi = make([3000, 10, 900], [1, 1, 1], H=8, seed=41)
+    o1, l1 = run(pi, None)
+    o2, l2 = run(pi, None)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    pc = make([3000, 300, 900], [200, 300, 5], H=4, bs=32, seed=42)
+    o1, l1 = run(pc, 512)
+    o2, l2 = run(pc, 512)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_split_count_independence():
+    pi = make([5000, 2500, 100], [1, 1, 1], H=4, seed=51)
+    base, bl = run(pi, 1 << 14)
+    for s in (64, 256, 1024):
+        o, l = run(pi, s)
+        assert (o.float() - base.float()).abs().max() <= 2e-2
+        assert (l - bl).abs().max() <= 1e-4
+
+
+def test_paged_square_matches_prefill():
+    """q_len == ctx: paged chunk attention equals causal prefill on the same data."""
+    H, d, bs, N = 2, 128, 32, 700
+    cfg = inputs.PrefillConfig("sq", 1, H, N, d, torch.bfloat16, True, 61)
+    q, k, v = inputs.prefill_inputs(cfg, DEV)
+    nb = (N + bs - 1) // bs
+    perm = torch.randperm(nb + 2, generator=torch.Generator().manual_seed(3))
+    pool = torch.full((nb + 2, 2, H, bs, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    for t0 in range(0, N, bs):
+        t1 = min(N, t0 + bs)
+        pb = int(perm[t0 // bs])
+        pool[pb, 0, :, :t1 - t0] = k[0, :, t0:t1]
+        pool[pb, 1, :, :t1 - t0] = v[0, :, t0:t1]
+    table = perm[:nb].to(torch.int32).view(1, nb).to(DEV)
+    qp = q[0].permute(1, 0, 2).contiguous()
+    lens = torch.tensor([N], dtype=torch.int32, device=DEV)
+    op, lp = attn.paged_attention(qp, pool, table, lens, lens, bs)
+    of, lf = attn.prefill(q, k, v, True)
+    torch.cuda.synchronize()
+    assert (op.float() - of[0].permute(1, 0, 2).float()).abs().max() <= 2e-2
+    assert (lp - lf[0].T).abs().max() <= 5e-3
+
+
+def test_scale_zero_bottom_right_alignment():
+    ctx = [40, 333]
+    ql = [7, 100]
+    pi = make(ctx, ql, H=2, bs=16, seed=71)
+    o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, 16, scale=0.0)
+    torch.cuda.synchronize()
+    lse = lse.double().cpu()
+    row = 0
+    for c, q in zip(ctx, ql):
+        for i in range(q):
+            want = np.log(c - q + i + 1)
+            assert abs(float(lse[row + i, 0]) - want) < 1e-4
+        row += q
+
+
+def test_gather_bit_exact():
+    ctx = [1, 16, 17, 250, 1000]
+    for bs in (16, 32):
+        pi = make(ctx, [1] * 5, H=3, d=128, bs=bs, seed=81)
+        k, v = attn.gather(pi.pool, pi.block_table, pi.ctx_lens, bs)
+        torch.cuda.synchronize()
+        ko, vo = oracle.paged_gather(pi.pool, pi.block_table, pi.ctx_lens, bs)
+        assert np.array_equal(k.cpu().view(torch.int16).numpy().view(np.uint16), ko)
+        assert np.array_equal(v.cpu().view(torch.int16).numpy().view(np.uint16), vo)
+
+
+def test_c4_full():
+    """64 requests, q_len 1, ctx U[512, 16384], 16-token pages: every row vs the oracle."""
+    c = inputs.C4
+    log("c4: building inputs")
+    pi = inputs.paged_inputs(c, DEV)
+    check_full(pi, None, "c4")
+
+
+@pytest.mark.slow
+def test_c5_sampled():
+    """8 requests x 512-token chunks on ctx U[4096, 32768] + 512, 32-token pages;
+    64 seeded (request, head, row) triples plus edge rows."""
+    c = inputs.C5
+    log("c5: building inputs")
+    pi = inputs.paged_inputs(c, DEV)
+    o, lse = run(pi, None, "c5")
+    assert bool(torch.isfinite(o).all())
+    trip = inputs.sample_triples(c.seed, 64, (c.num_seqs, c.H, c.q_len),
+                                 edge=[(0, 0, 0), (0, 0, 511), (7, 31, 0), (7, 31, 511), (3, 4, 128)])
+    r_idx = [t[0] for t in trip]
+    h_idx = [t[1] for t in trip]
+    i_idx = [t[2] for t in trip]
+    o_ref, l_ref = oracle.paged_attention_rows(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens,
+                                               pi.block_size, pi.scale, r_idx, h_idx, i_idx)
+    rows = [r * c.q_len + i for r, i in zip(r_idx, i_idx)]
+    og = torch.stack([o[rw, h] for rw, h in zip(rows, h_idx)])
+    lg = torch.stack([lse[rw, h] for rw, h in zip(rows, h_idx)])
+    check_close("c5 sampled", og, o_ref, lg, l_ref, torch.bfloat16)

@@ -1,0 +1,212 @@
+"""MI355X (gfx950) tiled online-softmax attention: thin Python binding.
+
+Every function here only marshals arguments into the C ABI of
+``libattn_gfx950.so`` (declared in ``include/attn.h``); all of the attention
+work runs in the library's HIP kernels.  PyTorch supplies device memory and
+the current stream.  If the library has not been built, the first call raises
+``RuntimeError`` -- there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+__all__ = [
+    "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
+    "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
+    "attn_strerror", "attn_version", "prefill", "paged_attention", "gather",
+]
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libattn_gfx950.so"
+
+ATTN_BF16 = 0
+ATTN_F32 = 1
+
+# every symbol include/attn.h declares
+exported_symbols = (
+    "attn_prefill_fwd",
+    "paged_attn_fwd",
+    "paged_attn_workspace_bytes",
+    "paged_kv_gather",
+    "attn_strerror",
+    "attn_version",
+)
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, attn_strerror(code), code))
+        self.code = code
+
+
+def lib_path() -> Path:
+    return LIB_PATH
+
+
+def library():
+    """Load libattn_gfx950.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not LIB_PATH.exists():
+        raise RuntimeError("libattn_gfx950.so is not built (run __graft_entry__.build() or "
+                           "python -m tiled_online_softmax_attention_amd._build)")
+    lib = ctypes.CDLL(str(LIB_PATH))
+    P, I, F, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_int64, ctypes.c_size_t
+    lib.attn_prefill_fwd.argtypes = [P, P, P, P, P, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_fwd.restype = I
+    lib.paged_attn_fwd.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, F, I, I64, I, I, I, I, P, SZ, P]
+    lib.paged_attn_fwd.restype = I
+    lib.paged_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.paged_attn_workspace_bytes.restype = SZ
+    lib.paged_kv_gather.argtypes = [P, P, P, P, I, I, I, I, I, I64, I, I, P, P, P]
+    lib.paged_kv_gather.restype = I
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_strerror(code: int) -> str:
+    return library().attn_strerror(int(code)).decode()
+
+
+def attn_version() -> str:
+    return library().attn_version().decode()
+
+
+# ---- raw entry points (same names and argument order as the C ABI) -----------
+
+def attn_prefill_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, stream):
+    return library().attn_prefill_fwd(q, k, v, o, lse, B, H, N, d, float(scale), int(causal), int(dtype),
+                                      stream)
+
+
+def paged_attn_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, d,
+                   scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len, dtype,
+                   workspace, workspace_bytes, stream):
+    return library().paged_attn_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse,
+                                    num_seqs, H, d, float(scale), max_blocks_per_seq, kv_block_stride,
+                                    num_blocks, max_q_len, max_ctx_len, int(dtype), workspace,
+                                    workspace_bytes, stream)
+
+
+def paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len) -> int:
+    return int(library().paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len))
+
+
+def paged_kv_gather(k_pool, v_pool, block_table, ctx_lens, block_size, num_seqs, H, d, max_blocks_per_seq,
+                    kv_block_stride, max_ctx_len, dtype, k_out, v_out, stream):
+    return library().paged_kv_gather(k_pool, v_pool, block_table, ctx_lens, block_size, num_seqs, H, d,
+                                     max_blocks_per_seq, kv_block_stride, max_ctx_len, int(dtype), k_out,
+                                     v_out, stream)
+
+
+# ---- torch-tensor conveniences (marshalling only) -----------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError("attention tensors must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None, want_lse=True,
+            stream=None):
+    """O (and LSE) for q, k, v of shape [B, H, N, d] on the GPU."""
+    import torch
+    B, H, N, d = q.shape
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k, v must share shape [B, H, N, d]")
+    for t in (q, k, v):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous, same dtype and device")
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    rc = attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                          1 if causal else 0, _dtype_code(q), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_prefill_fwd")
+    return out, lse
+
+
+def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float | None = None,
+                    max_q_len: int | None = None, max_ctx_len: int | None = None, out=None, lse=None,
+                    want_lse=True, workspace=None, stream=None):
+    """Paged attention over the pool [num_blocks, 2, H, block_size, d] (K at 0, V at 1).
+
+    q: packed [sum(q_lens), H, d] bf16; block_table int32 [num_seqs, max_blocks];
+    ctx_lens, q_lens int32 [num_seqs] on the device.  max_q_len / max_ctx_len are
+    host bounds (read from the tensors with a device sync when omitted)."""
+    import torch
+    num_blocks, two, H, bs, d = pool.shape
+    if two != 2 or bs != block_size:
+        raise ValueError("pool must be [num_blocks, 2, H, block_size, d]")
+    if not pool.is_contiguous() or not q.is_contiguous() or not block_table.is_contiguous():
+        raise ValueError("pool, q and block_table must be contiguous")
+    num_seqs, maxb = block_table.shape
+    if max_q_len is None:
+        max_q_len = int(q_lens.max())
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_lens.max())
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    ws_bytes = paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    kv_stride = 2 * H * block_size * d
+    k_ptr = pool.data_ptr()
+    v_ptr = k_ptr + H * block_size * d * pool.element_size()
+    rc = paged_attn_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
+                        _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, d,
+                        d ** -0.5 if scale is None else scale, maxb, kv_stride, num_blocks, max_q_len,
+                        max_ctx_len, _dtype_code(q), _ptr(workspace),
+                        workspace.numel() if workspace is not None else 0, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "paged_attn_fwd")
+    return out, lse
+
+
+def gather(pool, block_table, ctx_lens, block_size: int, total_tokens: int | None = None,
+           max_ctx_len: int | None = None, stream=None):
+    """K and V of every request through the block table, packed [sum(ctx), H, d]."""
+    import torch
+    num_blocks, two, H, bs, d = pool.shape
+    num_seqs, maxb = block_table.shape
+    if total_tokens is None:
+        total_tokens = int(ctx_lens.to(torch.int64).sum())
+    if max_ctx_len is None:
+        max_ctx_len = int(ctx_lens.max())
+    k_out = torch.empty((total_tokens, H, d), dtype=pool.dtype, device=pool.device)
+    v_out = torch.empty_like(k_out)
+    k_ptr = pool.data_ptr()
+    v_ptr = k_ptr + H * block_size * d * pool.element_size()
+    rc = paged_kv_gather(ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table), _ptr(ctx_lens),
+                         block_size, num_seqs, H, d, maxb, 2 * H * block_size * d, max_ctx_len,
+                         _dtype_code(pool), _ptr(k_out), _ptr(v_out), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "paged_kv_gather")
+    return k_out, v_out

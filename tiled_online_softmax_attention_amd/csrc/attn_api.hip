@@ -1,0 +1,180 @@
+// attn_api.hip -- the C ABI declared in include/attn.h: host-side validation,
+// launch planning and kernel launches.  Nothing here allocates device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/attn.h"
+#include "attn_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Cached "is the current device a gfx950" answer (per device ordinal).
+int check_device()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    if (dev < 0 || dev >= 64) return ATTN_ERR_DEVICE;
+    if (cached[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+        cached[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    }
+    return cached[dev] == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+int check_scale(float scale)
+{
+    if (!isfinite(scale) || scale < 0.f) return ATTN_ERR_SCALE;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int status)
+{
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_ERR_NULL: return "a required pointer is NULL";
+        case ATTN_ERR_SHAPE: return "invalid size (must be >= 1 and fit 32-bit grid indexing)";
+        case ATTN_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+        case ATTN_ERR_BLOCK_SIZE: return "block_size must be 16 or 32";
+        case ATTN_ERR_DTYPE: return "element type not supported by this entry point";
+        case ATTN_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+        case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
+        case ATTN_ERR_DEVICE: return "current device is not a gfx950 GPU";
+        default: return "unknown attn status";
+    }
+}
+
+const char* attn_version(void) { return "attn_gfx950 1.0"; }
+
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     attn_dtype_t dtype, void* stream)
+{
+    if (!q || !k || !v || !o) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
+        return ATTN_ERR_ALIGN;
+    int rc = check_scale(scale);
+    if (rc) return rc;
+    if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_SHAPE;
+    rc = check_device();
+    if (rc) return rc;
+    attn::PrefillArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.scale = scale;
+    a.causal = causal ? 1 : 0;
+    a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
+    // Pair tiles t and n-1-t when a causal launch has too few tiles to keep
+    // every CU busy with a balanced load (env ATTN_PREFILL_PAIR=0/1 forces it).
+    {
+        const int nqt = (N + attn::kChunkBM - 1) / attn::kChunkBM;
+        const int64_t tiles = (int64_t)B * H * nqt;
+        int pair = (a.causal && nqt >= 2 && tiles <= 2048) ? 1 : 0;
+        const char* env = getenv("ATTN_PREFILL_PAIR");
+        if (env && *env) pair = atoi(env) ? 1 : 0;
+        if (!a.causal || nqt < 2) pair = 0;
+        a.pair = pair;
+    }
+    rc = attn::launch_prefill(a, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
+}
+
+size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
+{
+    if (num_seqs < 1 || H < 1 || (d != 64 && d != 128) || (block_size != 16 && block_size != 32) ||
+        max_q_len < 1 || max_ctx_len < 1)
+        return 0;
+    return attn::plan_paged(num_seqs, H, d, block_size, max_q_len, max_ctx_len).ws_bytes;
+}
+
+int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                   int block_size, void* o, float* lse,
+                   int num_seqs, int H, int d, float scale, int max_blocks_per_seq,
+                   int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !q_lens || !o) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 1 ||
+        max_ctx_len < 1 || max_q_len > max_ctx_len)
+        return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if ((int64_t)(max_ctx_len + block_size - 1) / block_size > max_blocks_per_seq) return ATTN_ERR_SHAPE;
+    if (kv_block_stride < (int64_t)H * block_size * d) return ATTN_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
+        ((kv_block_stride * 2) & 15) || ((uintptr_t)block_table & 3u) || ((uintptr_t)lse & 3u))
+        return ATTN_ERR_ALIGN;
+    int rc = check_scale(scale);
+    if (rc) return rc;
+    const attn::PagedPlan plan = attn::plan_paged(num_seqs, H, d, block_size, max_q_len, max_ctx_len);
+    // grid sizes must fit 32 bits
+    const int64_t rows = (int64_t)num_seqs * max_q_len;
+    if (rows * H * plan.max_splits > (int64_t)INT32_MAX - 8) return ATTN_ERR_SHAPE;
+    if (plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes) return ATTN_ERR_WORKSPACE;
+        if ((uintptr_t)workspace & 255u) return ATTN_ERR_ALIGN;
+    }
+    rc = check_device();
+    if (rc) return rc;
+    attn::PagedArgs a{};
+    a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
+    a.block_table = block_table; a.ctx_lens = ctx_lens; a.q_lens = q_lens;
+    a.block_size = block_size; a.o = o; a.lse = lse;
+    a.num_seqs = num_seqs; a.H = H; a.d = d; a.scale = scale;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.kv_block_stride = kv_block_stride;
+    a.num_blocks = num_blocks;
+    a.max_q_len = max_q_len; a.max_ctx_len = max_ctx_len;
+    a.split_tokens = plan.split_tokens;
+    a.max_splits = plan.max_splits;
+    a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
+    a.ws_lse = plan.ws_bytes ? (float*)((char*)workspace + plan.ws_o_bytes) : nullptr;
+    rc = attn::launch_paged(a, plan, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_table,
+                    const int32_t* ctx_lens, int block_size, int num_seqs, int H, int d,
+                    int max_blocks_per_seq, int64_t kv_block_stride, int max_ctx_len,
+                    attn_dtype_t dtype, void* k_out, void* v_out, void* stream)
+{
+    if (!k_pool || !v_pool || !block_table || !ctx_lens || !k_out || !v_out) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || H < 1 || max_blocks_per_seq < 1 || max_ctx_len < 1) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if ((int64_t)(max_ctx_len + block_size - 1) / block_size > max_blocks_per_seq) return ATTN_ERR_SHAPE;
+    if (kv_block_stride < (int64_t)H * block_size * d) return ATTN_ERR_SHAPE;
+    const int eb = (dtype == ATTN_BF16) ? 2 : 4;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_out) || !aligned16(v_out) ||
+        ((kv_block_stride * eb) & 15))
+        return ATTN_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    attn::GatherArgs a{};
+    a.k_pool = k_pool; a.v_pool = v_pool; a.block_table = block_table; a.ctx_lens = ctx_lens;
+    a.block_size = block_size; a.num_seqs = num_seqs; a.H = H; a.d = d;
+    a.max_blocks_per_seq = max_blocks_per_seq; a.kv_block_stride = kv_block_stride;
+    a.max_ctx_len = max_ctx_len; a.elem_bytes = eb; a.k_out = k_out; a.v_out = v_out;
+    rc = attn::launch_gather(a, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// attn_internal.h -- argument blocks and launchers shared between the C-ABI
+// host code (attn_api.hip) and the kernel translation units.  Not installed;
+// the public interface is include/attn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int B, H, N, d;
+    float scale;
+    int causal;
+    int dtype;      // 0 bf16, 1 fp32
+    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t
+    int n_work;     // filled by the launcher
+};
+
+// Host-side plan of a paged launch: a pure function of the host bounds.
+struct PagedPlan {
+    int path;            // 0: vector decode kernel, 1: MFMA chunk kernel
+    int split_tokens;    // keys per context split (multiple of the page size)
+    int max_splits;      // ceil(max_ctx_len / split_tokens)
+    int nqt;             // query tiles per request (chunk path)
+    size_t ws_o_bytes;   // fp32 partial outputs
+    size_t ws_lse_bytes; // fp32 partial log-sum-exps
+    size_t ws_bytes;     // total (0 when max_splits == 1)
+};
+
+struct PagedArgs {
+    const void* q;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    const int32_t* q_lens;
+    int block_size;
+    void* o;
+    float* lse;
+    int num_seqs, H, d;
+    float scale;
+    int max_blocks_per_seq;
+    int64_t kv_block_stride;   // elements
+    int num_blocks;
+    int max_q_len, max_ctx_len;
+    int split_tokens, max_splits;
+    float* ws_o;     // [num_seqs*max_q_len][H][max_splits][d]
+    float* ws_lse;   // [num_seqs*max_q_len][H][max_splits]
+};
+
+struct GatherArgs {
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* block_table;
+    const int32_t* ctx_lens;
+    int block_size, num_seqs, H, d, max_blocks_per_seq;
+    int64_t kv_block_stride;
+    int max_ctx_len;
+    int elem_bytes;
+    void* k_out;
+    void* v_out;
+};
+
+constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode kernel
+constexpr int kChunkBM = 128;      // query rows per MFMA workgroup
+
+PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len);
+
+int launch_prefill(const PrefillArgs& a, hipStream_t stream);
+int launch_paged(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream);
+int launch_gather(const GatherArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,495 @@
+// paged_gfx950.hip -- attention over a paged KV cache for gfx950: decode
+// (a few query rows per request) and chunked prefill (an appended chunk of
+// query rows per request), plus the log-sum-exp combine of context splits and
+// the bit-exact gather used to check the address function.
+//
+// Address function ("Chunked attention ... 70x slower", section 2.1, and the
+// pool layout of "Flash Attention and Paged Attention", section 3): token t of
+// request r lives in physical block pb = block_table[r][t / bs] at offset
+// t % bs; the [bs, d] slab of head h in that block is contiguous, so every
+// page is read as whole 16-byte-per-lane rows, never element by element.
+// Block offsets are 64-bit (a pool may exceed 2^31 elements).
+//
+// Work decomposition: each request's context is cut into splits of a fixed
+// number of tokens (a whole number of pages).  One launch covers every
+// (request, query row or tile, head, split) of the batch; a split writes a
+// normalised fp32 partial and its log-sum-exp, and a second launch merges the
+// partials of each (row, head).  Requests whose context fits one split write
+// their final output directly.  The plan depends only on host bounds, so
+// results never depend on where blocks sit in the pool.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "attn_internal.h"
+#include "attn_mfma_kernel.h"
+
+namespace attn {
+
+// ---- small wave helpers ------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over aligned groups of 16 (or 8) lanes, result in every lane of the group.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x)
+{
+    x += dpp<0xB1>(x);      // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);      // quad_perm [2,3,0,1]
+    x += dpp<0x141>(x);     // row_half_mirror: pairs quad 0 with quad 1
+    if (LPR == 16) x += dpp<0x140>(x);   // row_mirror: pairs the two halves of a row
+    return x;
+}
+
+// sum_e a[e] * b[e] over 8 bf16 pairs, fp32 accumulation (bf16 dot2).  The
+// pairs are taken with shufflevector from whole 8-element vectors; bit-casting
+// single 32-bit elements of a loaded vector to bf16x2 is mis-lowered by the
+// compiler (every pair ends up reading the first element).
+__device__ __forceinline__ float dot8_bf16(bf16x8 a, bf16x8 b)
+{
+    float acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 0, 1), __builtin_shufflevector(b, b, 0, 1), 0.f, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 2, 3), __builtin_shufflevector(b, b, 2, 3), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 4, 5), __builtin_shufflevector(b, b, 4, 5), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(a, a, 6, 7), __builtin_shufflevector(b, b, 6, 7), acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x)
+{
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+__device__ __forceinline__ float wave_max(float x)
+{
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+    return x;
+}
+
+// sum_{s<r} lens[s], computed by one wave (every lane gets the result)
+__device__ __forceinline__ int64_t prefix_len(const int32_t* lens, int r, int lane)
+{
+    int64_t acc = 0;
+    for (int s0 = 0; s0 < r; s0 += 64) {
+        int s = s0 + lane;
+        int v = (s < r) ? lens[s] : 0;
+        acc += wave_sum_int(v);
+    }
+    return acc;
+}
+
+// ============================================================================
+// Decode kernel: one workgroup (4 waves) per (request, query row, head, split).
+// Lanes are grouped by LPR = d/8: a group of LPR lanes holds one token row of
+// a page (16 bytes = 8 channels per lane), so each 16-byte-per-lane load covers
+// 64/LPR consecutive tokens.  q.k uses bf16 dot2 on the raw pairs; the group
+// reduction is DPP; the wave takes pages w, w+4, ... of the split with the next
+// page's loads in flight while the current page is consumed; the four waves'
+// partial (m, l, o) are merged through LDS.
+// ============================================================================
+template <int D, int BS>
+__global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
+{
+    constexpr int LPR = D / 8;
+    constexpr int TPL = 64 / LPR;       // tokens per wave-load
+    constexpr int LOADS = BS / TPL;     // loads per lane per page (each of K, V)
+    __shared__ float red_o[4][D];
+    __shared__ float red_ml[4][2];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int sub = lane / LPR, oct = lane % LPR;
+    int bid = blockIdx.x;
+    const int split = bid % a.max_splits;
+    bid /= a.max_splits;
+    const int h = bid % a.H;
+    bid /= a.H;
+    const int i = bid % a.max_q_len;
+    const int r = bid / a.max_q_len;
+    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    if (i >= ql) return;
+    const int S = a.split_tokens;
+    const int nsplit = (ctx + S - 1) / S;
+    if (split >= nsplit) return;
+    const int lim = ctx - ql + i + 1;             // keys [0, lim) are visible
+    const int kbeg = split * S, kend = min(kbeg + S, lim);
+    const int64_t row = prefix_len(a.q_lens, r, lane) + i;
+    const float c2 = a.scale * kLog2e;
+
+    const bf16x8 qb = as_bf16x8(*(const u32x4*)((const char*)a.q + ((row * a.H + h) * D + oct * 8) * 2));
+    const int32_t* table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
+    const int64_t blk_bytes = a.kv_block_stride * 2;
+    const char* kbase = (const char*)a.k_pool + (int64_t)h * BS * D * 2 + oct * 16;
+    const char* vbase = (const char*)a.v_pool + (int64_t)h * BS * D * 2 + oct * 16;
+
+    float m = -INFINITY, l = 0.f;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+
+    const int pbeg = kbeg / BS;
+    const int pend = (kend > kbeg) ? (kend + BS - 1) / BS : pbeg;
+    u32x4 kr[LOADS], vr[LOADS], kn[LOADS], vn[LOADS];
+    int p = pbeg + w;
+    if (p < pend) {
+        const int64_t pb = table[p];
+        const char* kp = kbase + pb * blk_bytes;
+        const char* vp = vbase + pb * blk_bytes;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            kr[j] = *(const u32x4*)(kp + (j * TPL + sub) * D * 2);
+            vr[j] = *(const u32x4*)(vp + (j * TPL + sub) * D * 2);
+        }
+    }
+    for (; p < pend; p += 4) {
+        const int pn = p + 4;
+        if (pn < pend) {
+            const int64_t pb = table[pn];
+            const char* kp = kbase + pb * blk_bytes;
+            const char* vp = vbase + pb * blk_bytes;
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                kn[j] = *(const u32x4*)(kp + (j * TPL + sub) * D * 2);
+                vn[j] = *(const u32x4*)(vp + (j * TPL + sub) * D * 2);
+            }
+        }
+        // scores of this lane group's tokens
+        float s[LOADS];
+        const bool tail = (p + 1) * BS > kend;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            s[j] = group_sum<LPR>(dot8_bf16(qb, as_bf16x8(kr[j])));
+            if (tail) {
+                const int t = p * BS + j * TPL + sub;
+                if (t >= kend) {
+                    s[j] = -INFINITY;
+                    vr[j] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+        }
+        float mt = s[0];
+#pragma unroll
+        for (int j = 1; j < LOADS; ++j) mt = fmaxf(mt, s[j]);
+#pragma unroll
+        for (int x = LPR; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x, 64));
+        const float m_new = fmaxf(m, mt);            // finite: every page has a visible key
+        const float ms_new = m_new * c2;
+        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m * c2 - ms_new);
+        m = m_new;
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const float pj = (s[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -ms_new));
+            ps += pj;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = __builtin_fmaf(pj, bf16lo(vr[j][e]), o[2 * e]);
+                o[2 * e + 1] = __builtin_fmaf(pj, bf16hi(vr[j][e]), o[2 * e + 1]);
+            }
+        }
+        l = l * alpha + ps;
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            kr[j] = kn[j];
+            vr[j] = vn[j];
+        }
+    }
+    // merge the lane groups of this wave (same channels, different tokens)
+#pragma unroll
+    for (int x = LPR; x < 64; x <<= 1) {
+        l += __shfl_xor(l, x, 64);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], x, 64);
+    }
+    // merge the four waves
+    if (sub == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red_o[w][oct * 8 + e] = o[e];
+    }
+    if (lane == 0) {
+        red_ml[w][0] = m;
+        red_ml[w][1] = l;
+    }
+    __syncthreads();
+    if (w != 0) return;
+    float M = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) M = fmaxf(M, red_ml[x][0]);
+    const float Ms = (M == -INFINITY) ? 0.f : M * c2;
+    float sc[4], L = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        sc[x] = (red_ml[x][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_ml[x][0] * c2 - Ms);
+        L += sc[x] * red_ml[x][1];
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const float lse = L > 0.f ? (Ms + __log2f(L)) * kLn2 : -INFINITY;
+    // lane c writes channels c and c + 64 (d = 64 or 128)
+    if (nsplit == 1) {
+        __bf16* orow = (__bf16*)a.o + (row * a.H + h) * D;
+        for (int c = lane; c < D; c += 64) {
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][c];
+            orow[c] = (__bf16)(acc * inv);
+        }
+        if (a.lse && lane == 0) a.lse[row * a.H + h] = lse;
+    } else {
+        const int64_t slot = (((int64_t)r * a.max_q_len + i) * a.H + h) * a.max_splits + split;
+        float* wo = a.ws_o + slot * D;
+        for (int c = lane; c < D; c += 64) {
+            float acc = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][c];
+            wo[c] = acc * inv;
+        }
+        if (lane == 0) a.ws_lse[slot] = lse;
+    }
+}
+
+// ============================================================================
+// Chunked-prefill kernel: the bf16 MFMA tile driver with K/V rows fetched
+// through the block table.  One workgroup per (request, 128-row query tile,
+// head, split); query tiles of one (request, head, split) are adjacent in the
+// XCD-contiguous order so they share K/V pages in that XCD's L2.
+// ============================================================================
+template <int D, int BS>
+struct PagedKV {
+    const char* kbase;       // k_pool + head offset (bytes)
+    const char* vbase;
+    const int32_t* table;    // this request's block-table row
+    int64_t blk_bytes;
+    __device__ __forceinline__ const char* k_row(int key) const
+    {
+        const int64_t pb = table[key / BS];
+        return kbase + pb * blk_bytes + (key % BS) * (D * 2);
+    }
+    __device__ __forceinline__ const char* v_row(int key) const
+    {
+        const int64_t pb = table[key / BS];
+        return vbase + pb * blk_bytes + (key % BS) * (D * 2);
+    }
+};
+
+template <int D, int BS>
+__global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_work)
+{
+    using C = TileCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_K + C::LDS_V];
+    const int per = gridDim.x >> 3;
+    int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (L >= n_work) return;
+    const int nqt = (a.max_q_len + C::BM - 1) / C::BM;
+    const int qt = L % nqt;
+    L /= nqt;
+    const int split = L % a.max_splits;
+    L /= a.max_splits;
+    const int h = L % a.H;
+    const int r = L / a.H;
+    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    if (qt * C::BM >= ql) return;
+    const int S = a.split_tokens;
+    const int nsplit = (ctx + S - 1) / S;
+    if (split >= nsplit) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t row0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * C::BM;
+
+    PagedKV<D, BS> kv;
+    kv.kbase = (const char*)a.k_pool + (int64_t)h * BS * D * 2;
+    kv.vbase = (const char*)a.v_pool + (int64_t)h * BS * D * 2;
+    kv.table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
+    kv.blk_bytes = a.kv_block_stride * 2;
+
+    TileProblem P;
+    P.q = (const char*)a.q + (row0 * a.H + h) * D * 2;
+    P.q_stride = (int64_t)a.H * D * 2;
+    P.n_rows = min(C::BM, ql - qt * C::BM);
+    P.q_pos0 = ctx - ql + qt * C::BM;
+    P.causal = 1;
+    P.kv_begin = split * S;
+    P.kv_end = min(ctx, (split + 1) * S);
+    TileOut out;
+    if (nsplit == 1) {
+        out.o = (char*)a.o + (row0 * a.H + h) * D * 2;
+        out.o_stride = (int64_t)a.H * D * 2;
+        out.lse = a.lse ? a.lse + row0 * a.H + h : nullptr;
+        out.lse_stride = a.H;
+        out.fp32_out = 0;
+    } else {
+        const int64_t slot = (((int64_t)r * a.max_q_len + qt * C::BM) * a.H + h) * a.max_splits + split;
+        out.o = (char*)(a.ws_o + slot * D);
+        out.o_stride = (int64_t)a.H * a.max_splits * D * 4;
+        out.lse = a.ws_lse + slot;
+        out.lse_stride = (int64_t)a.H * a.max_splits;
+        out.fp32_out = 1;
+    }
+    run_query_tile<D>(P, kv, out, a.scale * kLog2e, lds);
+}
+
+// ============================================================================
+// Combine: one wave per (request, query row, head) whose context was split.
+// M = max_s lse_s, L = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - L) O_s.
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n_items = (int64_t)a.num_seqs * a.max_q_len * a.H;
+    if (item >= n_items) return;
+    const int h = (int)(item % a.H);
+    const int i = (int)((item / a.H) % a.max_q_len);
+    const int r = (int)(item / ((int64_t)a.H * a.max_q_len));
+    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    if (i >= ql) return;
+    const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+    if (nsplit <= 1) return;
+    const int64_t slot0 = (((int64_t)r * a.max_q_len + i) * a.H + h) * a.max_splits;
+    float M = -INFINITY;
+    for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, a.ws_lse[slot0 + s]);
+    M = wave_max(M);
+    float sum = 0.f;
+    for (int s = lane; s < nsplit; s += 64) sum += expf(a.ws_lse[slot0 + s] - M);
+    sum = wave_sum(sum);
+    const float Lse = M + logf(sum);
+    const int64_t row = prefix_len(a.q_lens, r, lane) + i;
+    __bf16* orow = (__bf16*)a.o + (row * a.H + h) * D;
+    float acc[D / 64];
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) acc[c] = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const float wgt = expf(a.ws_lse[slot0 + s] - Lse);
+        const float* os = a.ws_o + (slot0 + s) * D;
+#pragma unroll
+        for (int c = 0; c < D / 64; ++c) acc[c] = __builtin_fmaf(wgt, os[lane + 64 * c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) orow[lane + 64 * c] = (__bf16)acc[c];
+    if (a.lse && lane == 0) a.lse[row * a.H + h] = Lse;
+}
+
+// ============================================================================
+// Gather: one workgroup per (request, page, head); copies the page's [bs, d]
+// K and V slabs (bytes as stored) to packed [sum(ctx), H, d] outputs.
+// ============================================================================
+__global__ __launch_bounds__(256) void paged_gather_kernel(GatherArgs a)
+{
+    const int max_pages = (a.max_ctx_len + a.block_size - 1) / a.block_size;
+    int bid = blockIdx.x;
+    const int h = bid % a.H;
+    bid /= a.H;
+    const int pg = bid % max_pages;
+    const int r = bid / max_pages;
+    const int ctx = a.ctx_lens[r];
+    if (pg * a.block_size >= ctx) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t tok0 = prefix_len(a.ctx_lens, r, lane);
+    const int64_t pb = a.block_table[(int64_t)r * a.max_blocks_per_seq + pg];
+    const int row_bytes = a.d * a.elem_bytes;
+    const int chunks_per_row = row_bytes / 16;
+    const int64_t src_off = pb * a.kv_block_stride * a.elem_bytes + (int64_t)h * a.block_size * row_bytes;
+    for (int u = threadIdx.x; u < a.block_size * chunks_per_row; u += blockDim.x) {
+        const int tok = u / chunks_per_row, ch = u % chunks_per_row;
+        const int t = pg * a.block_size + tok;
+        if (t >= ctx) continue;
+        const int64_t dst = ((tok0 + t) * a.H + h) * (int64_t)row_bytes + ch * 16;
+        *(u32x4*)((char*)a.k_out + dst) = *(const u32x4*)((const char*)a.k_pool + src_off + (int64_t)tok * row_bytes + ch * 16);
+        *(u32x4*)((char*)a.v_out + dst) = *(const u32x4*)((const char*)a.v_pool + src_off + (int64_t)tok * row_bytes + ch * 16);
+    }
+}
+
+// ============================================================================
+// host side
+// ============================================================================
+static int env_int(const char* name, int dflt)
+{
+    const char* s = getenv(name);
+    if (!s || !*s) return dflt;
+    return atoi(s);
+}
+
+PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
+{
+    PagedPlan p{};
+    p.path = (max_q_len <= kDecodeMaxQ) ? 0 : 1;
+    const int64_t rows = (int64_t)num_seqs * max_q_len;
+    int S;
+    if (p.path == 0) {
+        // decode: 4 waves x 8 pages per split by default, halved while the
+        // batch would leave the chip short of workgroups
+        const int64_t items = rows * H;
+        S = 4 * block_size * 8;
+        while (S > 4 * block_size && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
+        p.nqt = 1;
+    } else {
+        p.nqt = (max_q_len + kChunkBM - 1) / kChunkBM;
+        const int64_t items = (int64_t)num_seqs * p.nqt * H;
+        S = 8192;
+        while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < 2048) S /= 2;
+    }
+    const int env = env_int("ATTN_SPLIT_TOKENS", 0);
+    if (env > 0) S = env;
+    // whole pages, and whole 64-key tiles on the MFMA path
+    const int unit = (p.path == 0) ? block_size : (block_size > 64 ? block_size : 64);
+    S = ((S + unit - 1) / unit) * unit;
+    p.split_tokens = S;
+    p.max_splits = (max_ctx_len + S - 1) / S;
+    if (p.max_splits < 1) p.max_splits = 1;
+    if (p.max_splits > 1) {
+        const int64_t slots = rows * H * p.max_splits;
+        p.ws_o_bytes = (size_t)(slots * d * 4);
+        p.ws_lse_bytes = (size_t)(slots * 4);
+        p.ws_o_bytes = (p.ws_o_bytes + 255) / 256 * 256;
+        p.ws_bytes = p.ws_o_bytes + p.ws_lse_bytes;
+    }
+    return p;
+}
+
+template <int D, int BS>
+static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
+{
+    if (plan.path == 0) {
+        const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H * a.max_splits;
+        hipLaunchKernelGGL((paged_decode_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    } else {
+        const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H * a.max_splits;
+        const int64_t grid = (n_work + 7) / 8 * 8;
+        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
+    }
+    if (a.max_splits > 1) {
+        const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;
+        hipLaunchKernelGGL((paged_combine_kernel<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, a);
+    }
+}
+
+int launch_paged(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
+{
+    if (a.d == 128) {
+        if (a.block_size == 16) launch_paged_t<128, 16>(a, plan, stream);
+        else launch_paged_t<128, 32>(a, plan, stream);
+    } else {
+        if (a.block_size == 16) launch_paged_t<64, 16>(a, plan, stream);
+        else launch_paged_t<64, 32>(a, plan, stream);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+int launch_gather(const GatherArgs& a, hipStream_t stream)
+{
+    const int max_pages = (a.max_ctx_len + a.block_size - 1) / a.block_size;
+    const int64_t grid = (int64_t)a.num_seqs * max_pages * a.H;
+    if (grid > (int64_t)INT32_MAX) return -2;
+    hipLaunchKernelGGL(paged_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+}  // namespace attn

@@ -1,0 +1,189 @@
+// prefill_gfx950.hip -- dense / causal prefill attention for gfx950.
+//
+//  * bf16: fused MFMA kernel (attn_mfma_kernel.h), one workgroup of 4 waves per
+//    128-row query tile (or per pair of tiles, see below), K/V streamed through
+//    LDS in 64-key tiles, causal key tiles above the diagonal never loaded.
+//  * fp32: a vector-ALU kernel with the same online softmax (fp32 storage has
+//    no dense matrix path worth using at these sizes).
+//
+// Work mapping (bf16).  Workgroups are dealt to the 8 XCDs round-robin, so the
+// linear id is remapped such that each XCD receives a contiguous range of
+// (batch*head, query tile) work: the query tiles of one head then share that
+// XCD's L2 for their K/V.  Within a head, tiles run heaviest (most keys) first.
+// For causal launches with few tiles ("pair" mode), a workgroup instead takes
+// tile t and tile n-1-t, so that every workgroup does the same number of key
+// tiles and the chip stays balanced.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_mfma_kernel.h"
+#include "attn_internal.h"
+
+namespace attn {
+
+struct ContigKV {
+    const char* k;   // head base (bytes)
+    const char* v;
+    int row_bytes;
+    __device__ __forceinline__ const char* k_row(int key) const { return k + (int64_t)key * row_bytes; }
+    __device__ __forceinline__ const char* v_row(int key) const { return v + (int64_t)key * row_bytes; }
+};
+
+// Linear work id for this workgroup after the XCD-contiguous remap; the grid
+// is padded to a multiple of 8.
+__device__ __forceinline__ int xcd_linear_id(int bid, int grid)
+{
+    const int per = grid >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
+{
+    using C = TileCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_K + C::LDS_V];
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= a.n_work) return;
+    const int nqt = (a.N + C::BM - 1) / C::BM;
+    const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
+    const int bh = L / per_bh, t = L % per_bh;
+    const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes
+    ContigKV kv{(const char*)a.k + head_off, (const char*)a.v + head_off, D * 2};
+    const float c2 = a.scale * kLog2e;
+
+    int tiles[2];
+    int ntiles = 1;
+    tiles[0] = nqt - 1 - t;                 // heavy first
+    if (a.pair) {
+        tiles[1] = t;
+        ntiles = (tiles[1] != tiles[0]) ? 2 : 1;
+    }
+#pragma unroll 1
+    for (int it = 0; it < ntiles; ++it) {
+        const int qt = tiles[it];
+        const int q0 = qt * C::BM;
+        TileProblem P;
+        P.q = (const char*)a.q + head_off + (int64_t)q0 * D * 2;
+        P.q_stride = D * 2;
+        P.n_rows = min(C::BM, a.N - q0);
+        P.q_pos0 = q0;
+        P.causal = a.causal;
+        P.kv_begin = 0;
+        P.kv_end = a.N;
+        TileOut out;
+        out.o = (char*)a.o + head_off + (int64_t)q0 * D * 2;
+        out.o_stride = D * 2;
+        out.lse = a.lse ? a.lse + (int64_t)bh * a.N + q0 : nullptr;
+        out.lse_stride = 1;
+        out.fp32_out = 0;
+        if (it) __syncthreads();   // LDS reuse across the two tiles
+        run_query_tile<D>(P, kv, out, c2, lds);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 kernel: 64 query rows per workgroup, 4 threads per row (each owns d/4
+// channels of q and of the output), 32-key K/V tiles staged in LDS as fp32.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a)
+{
+    constexpr int BM = 64, BN = 32, SUB = D / 4;
+    __shared__ float ks[BN][D + 4];
+    __shared__ float vs[BN][D + 4];
+    const int nqt = (a.N + BM - 1) / BM;
+    const int bh = blockIdx.x / nqt, qt = nqt - 1 - (int)(blockIdx.x % nqt);
+    const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
+    const int q0 = qt * BM, qi = q0 + row;
+    const int64_t head = (int64_t)bh * a.N * D;
+    const float* qp = (const float*)a.q + head;
+    const float* kp = (const float*)a.k + head;
+    const float* vp = (const float*)a.v + head;
+    const float c2 = a.scale * kLog2e;
+
+    float qv[SUB], acc[SUB];
+#pragma unroll
+    for (int c = 0; c < SUB; ++c) {
+        qv[c] = qi < a.N ? qp[(int64_t)qi * D + part * SUB + c] : 0.f;
+        acc[c] = 0.f;
+    }
+    int lim = a.N;
+    if (a.causal) lim = min(a.N, qi + 1);
+    int t_end = a.causal ? min(a.N, q0 + BM) : a.N;
+    float m = -INFINITY, l = 0.f;
+    for (int kb = 0; kb < t_end; kb += BN) {
+        __syncthreads();
+        for (int e = tid; e < BN * D; e += 256) {
+            int r = e / D, c = e % D, key = kb + r;
+            ks[r][c] = key < a.N ? kp[(int64_t)key * D + c] : 0.f;
+            vs[r][c] = key < a.N ? vp[(int64_t)key * D + c] : 0.f;
+        }
+        __syncthreads();
+        float s[BN];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            float p = 0.f;
+#pragma unroll
+            for (int c = 0; c < SUB; ++c) p = __builtin_fmaf(qv[c], ks[j][part * SUB + c], p);
+            p += __shfl_xor(p, 1, 64);
+            p += __shfl_xor(p, 2, 64);
+            s[j] = (kb + j < lim) ? p : -INFINITY;
+            mt = fmaxf(mt, s[j]);
+        }
+        float m_new = fmaxf(m, mt);
+        float ms_new = m_new == -INFINITY ? 0.f : m_new * c2;
+        float ms_old = m == -INFINITY ? 0.f : m * c2;
+        float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int c = 0; c < SUB; ++c) acc[c] *= alpha;
+#pragma unroll
+        for (int j = 0; j < BN; ++j) {
+            float p = s[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -ms_new));
+            l += p;
+#pragma unroll
+            for (int c = 0; c < SUB; ++c) acc[c] = __builtin_fmaf(p, vs[j][part * SUB + c], acc[c]);
+        }
+    }
+    if (qi < a.N) {
+        float inv = l > 0.f ? 1.f / l : 0.f;
+        float* op = (float*)a.o + head + (int64_t)qi * D + part * SUB;
+#pragma unroll
+        for (int c = 0; c < SUB; ++c) op[c] = acc[c] * inv;
+        if (a.lse && part == 0) {
+            float ms = m == -INFINITY ? 0.f : m * c2;
+            a.lse[(int64_t)bh * a.N + qi] = l > 0.f ? (ms + __log2f(l)) * kLn2 : -INFINITY;
+        }
+    }
+}
+
+int launch_prefill(const PrefillArgs& in, hipStream_t stream)
+{
+    PrefillArgs a = in;
+    if (a.dtype == 0) {
+        constexpr int BM = TileCfg<128>::BM;
+        const int nqt = (a.N + BM - 1) / BM;
+        const int64_t bh = (int64_t)a.B * a.H;
+        const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
+        const int64_t n_work = bh * per_bh;
+        if (n_work > (int64_t)INT32_MAX - 8) return -2;
+        a.n_work = (int)n_work;
+        const int grid = (int)((n_work + 7) / 8 * 8);
+        if (a.d == 128)
+            hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+    } else {
+        const int nqt = (a.N + 63) / 64;
+        const int64_t grid = (int64_t)a.B * a.H * nqt;
+        if (grid > (int64_t)INT32_MAX) return -2;
+        if (a.d == 128)
+            hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+        else
+            hipLaunchKernelGGL(prefill_f32_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+}  // namespace attn
