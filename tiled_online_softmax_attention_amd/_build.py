@@ -23,6 +23,9 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
+    # kernels never rely on NaN propagation (masked slots are selected away by
+    # index), which lets fmaxf lower to v_max3_f32 without operand quieting
+    "-Xarch_device", "-fno-honor-nans",
 ]
 
 

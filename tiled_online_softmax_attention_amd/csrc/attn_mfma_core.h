@@ -51,6 +51,17 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk, uint32_t c
     return ((L & ~15u) | ((L & 15u) ^ ((L >> 4) & 15u))) * 16u;
 }
 
+// Byte offset of 16-byte chunk `chunk` (0..7) of row d of the V^T tile (rows of
+// 8 chunks, two rows per 256-byte line).  The in-line chunk index is XORed
+// with bits of the line number and of d >> 5, so that both the MFMA reads
+// (16 consecutive d, one chunk) and the transposing writes (d spaced by 8,
+// both 8-byte halves of a chunk per 32-lane pass) hit distinct banks.
+__device__ __forceinline__ uint32_t vswz(uint32_t d, uint32_t chunk)
+{
+    const uint32_t u = ((d & 1u) << 3) | chunk;
+    return ((d >> 1) * 16u + (u ^ (((d >> 1) ^ (d >> 5)) & 15u))) * 16u;
+}
+
 // Position of key offset o (0..15) inside a 16-key MFMA step of the V^T tile:
 // bits 2 and 3 are swapped, so that lane half g finds keys {4g..4g+3} and
 // {8+4g..8+4g+3} -- exactly the keys its S^T accumulator registers hold --
@@ -107,6 +118,18 @@ struct TileCfg {
     static_assert(V_QUADS <= kThreads, "one V block per thread at most");
 };
 
+// Which 4-key quad of the V tile thread `tid` stages: consecutive groups of
+// d/8 threads take quads whose permuted slots alternate between the two
+// 8-byte halves of a 16-byte chunk (quad order 0, 2, 1, 3 inside each
+// 16-key step), so every 32-lane pass of the transposing LDS writes covers
+// both halves.
+__device__ __forceinline__ int vquad_key(int tid, int d)
+{
+    const int q = tid / (d / 8);
+    const int lo = q & 3;
+    return (q & ~3) | ((lo & 1) << 1) | (lo >> 1);
+}
+
 // Per-thread registers holding the next K/V tile while the current one is
 // being consumed (the global loads are issued one tile ahead).
 template <int D>
@@ -128,7 +151,7 @@ __device__ __forceinline__ void stage_to_lds(const KVStage<D>& st, char* lds_k, 
         *(u32x4*)(lds_k + swz(row, chunk, C::KCPR)) = st.k[i];
     }
     if (tid < C::V_QUADS) {
-        int kq = tid / (D / 8), dof = tid % (D / 8);
+        const int kq = vquad_key(tid, D), dof = tid % (D / 8);
         int key0 = kq * 4;                                   // first of 4 keys
         uint32_t kp = (key0 & ~15) | vperm16(key0 & 15);     // permuted slot (4-aligned)
         uint32_t chunk = kp >> 3, half = (kp >> 2) & 1;
@@ -143,31 +166,55 @@ __device__ __forceinline__ void stage_to_lds(const KVStage<D>& st, char* lds_k, 
             hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
             hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
             uint32_t d_lo = dof * 8 + 2 * e2, d_hi = d_lo + 1;
-            *(u32x2*)(lds_v + swz(d_lo, chunk, C::VCPR) + half * 8) = lo;
-            *(u32x2*)(lds_v + swz(d_hi, chunk, C::VCPR) + half * 8) = hi;
+            *(u32x2*)(lds_v + vswz(d_lo, chunk) + half * 8) = lo;
+            *(u32x2*)(lds_v + vswz(d_hi, chunk) + half * 8) = hi;
         }
     }
 }
 
-// State of one wave: 32 queries, O^T accumulators, running max / sum.
+// State of one wave: 32 queries, O^T accumulators, running offset / sum.
 template <int D>
 struct WaveState {
     f32x16 o[TileCfg<D>::DBLK];
-    float m;      // running max of the raw (unscaled) scores of this lane's query
+    float m;      // offset of this lane's query, raw score units (-inf: none yet)
     float l;      // running sum of this lane-half's rounded probabilities
 };
 
+__device__ __forceinline__ bf16x2 pack2(float a, float b)
+{
+    bf16x2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d)
+{
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 lo = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    bf16x4 hi = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Exponent headroom of the lazy rescale: the offset m only moves when a
+// tile's maximum exceeds it by more than kRescaleLog2 in the base-2 exponent,
+// so p = 2^(s*c2 - m*c2) stays <= 2^kRescaleLog2 (well inside fp32 and bf16
+// range) and the O/l rescale is skipped on almost every tile.  O and l always
+// share the same offset, so the final O/l and LSE = m + ln l are exact.
+constexpr float kRescaleLog2 = 8.0f;
+
 // One key tile for one wave.
-//  qf       : Q^T operand fragments (bf16x8 per 16-wide d step)
-//  c2       : scale * log2(e)
-//  key0     : absolute key index of tile row 0
-//  q_abs    : absolute position of this lane's query (for the causal test)
-//  kv_len   : keys >= kv_len are masked
-//  masked   : whether any mask test is needed for this wave on this tile
-template <int D>
+//  qf      : Q^T operand fragments (bf16x8 per 16-wide d step)
+//  c2      : scale * log2(e) (> 0);  thr = kRescaleLog2 / c2 in raw score units
+//  key0    : absolute key index of tile row 0
+//  q_lim   : this lane's query sees keys < q_lim
+//  MASKED  : whether any key of this tile may be masked for a lane of the wave
+//  (c2 > 0 always: a zero scale is passed as a tiny positive c2, which gives
+//  the same p = 1 for every allowed key and keeps exp2(-inf) = 0 for masked ones)
+template <int D, bool MASKED>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS],
-                                          const char* lds_k, const char* lds_v, int lane, float c2,
-                                          int key0, int q_lim, bool masked)
+                                          const char* lds_k, const char* lds_v, int lane, float c2, float thr,
+                                          int key0, int q_lim)
 {
     using C = TileCfg<D>;
     const int g = lane >> 5, r32 = lane & 31;
@@ -183,67 +230,61 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
         }
         s[kb] = acc;
     }
-    // ---- mask + running max ------------------------------------------------
-    // key of accumulator register i of block kb: kb*32 + (i/4)*8 + g*4 + i%4
+    // ---- mask (diagonal / tail tiles only) and tile maximum -----------------
+    // key of accumulator register i of block kb: key0 + kb*32 + (i/4)*8 + g*4 + i%4
+    const int lim_rel = q_lim - key0 - g * 4;
     float mt = -INFINITY;
-    if (masked) {
+    if (MASKED) {
 #pragma unroll
         for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                int key = key0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-                if (key >= q_lim) s[kb][i] = -INFINITY;
-                mt = fmaxf(mt, s[kb][i]);
+                const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
+                s[kb][i] = (off < lim_rel) ? s[kb][i] : -INFINITY;
             }
-    } else {
-#pragma unroll
-        for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[kb][i]);
     }
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[kb][i], s[kb][i + 1]));
     mt = fmaxf(mt, xor32(mt));
-    const float m_new = fmaxf(ws.m, mt);
-    // scaled maxima; a row that has seen no allowed key keeps max -inf and
-    // uses 0 as its offset (all its p are 0 and its O, l are still 0)
-    const float ms_new = (m_new == -INFINITY) ? 0.f : m_new * c2;
-    const float ms_old = (ws.m == -INFINITY) ? 0.f : ws.m * c2;
-    const float alpha = __builtin_amdgcn_exp2f(ms_old - ms_new);
-    ws.m = m_new;
-    // ---- p = exp2(s*c2 - m), rounded to bf16, summed -------------------------
-    uint32_t pk[C::KBLK][8];
-    float psum = 0.f;
+    // ---- lazy offset update (wave-uniform decision) --------------------------
+    const bool need = mt > ws.m + thr;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(ws.m, mt);
+        const float alpha = (ws.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ws.m - m_new) * c2);
+        ws.m = m_new;
+        ws.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) ws.o[db] *= alpha;
+    }
+    const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * c2;
+    // ---- p = exp2(s*c2 - ms), rounded to bf16; l += sum of the rounded p -----
+    bf16x2 pk[C::KBLK][8];
+    const bf16x2 ones = pack2(1.f, 1.f);
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c2, -ms_new));
-            float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c2, -ms_new));
-            if (masked) {
-                if (s[kb][i] == -INFINITY) p0 = 0.f;
-                if (s[kb][i + 1] == -INFINITY) p1 = 0.f;
-            }
-            uint32_t w = pack_bf16(p0, p1);
+            const float t0 = __builtin_fmaf(s[kb][i], c2, -ms);
+            const float t1 = __builtin_fmaf(s[kb][i + 1], c2, -ms);
+            const bf16x2 w = pack2(__builtin_amdgcn_exp2f(t0), __builtin_amdgcn_exp2f(t1));
             pk[kb][i >> 1] = w;
-            psum += bf16lo(w) + bf16hi(w);
+            if ((i >> 1) & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps1, false);
+            else ps0 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps0, false);
         }
-    ws.l = ws.l * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) ws.o[db] *= alpha;
+    ws.l += ps0 + ps1;
     // ---- O^T += V^T P^T ------------------------------------------------------
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            u32x4 pw;
-            pw[0] = pk[kb][4 * h + 0];
-            pw[1] = pk[kb][4 * h + 1];
-            pw[2] = pk[kb][4 * h + 2];
-            pw[3] = pk[kb][4 * h + 3];
-            bf16x8 b = as_bf16x8(pw);
+            const bf16x8 b = cat8(pk[kb][4 * h + 0], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]);
             const int chunk = kb * 4 + h * 2 + g;
 #pragma unroll
             for (int db = 0; db < C::DBLK; ++db) {
-                u32x4 a = *(const u32x4*)(lds_v + swz(db * 32 + r32, chunk, C::VCPR));
+                u32x4 a = *(const u32x4*)(lds_v + vswz(db * 32 + r32, chunk));
                 ws.o[db] = mfma32(as_bf16x8(a), b, ws.o[db]);
             }
         }

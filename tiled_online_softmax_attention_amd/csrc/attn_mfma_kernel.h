@@ -22,28 +22,45 @@ struct TileProblem {
     int kv_end;
 };
 
-template <int D, class KV>
-__device__ __forceinline__ void load_stage(KVStage<D>& st, const KV& kv, int key_base, int kv_end, int tid)
+// Per-thread byte offsets of the rows this thread loads inside one K/V tile
+// (identical for every tile).  K: load i covers tile rows [i*R, (i+1)*R) with
+// R = 256 / (d/8) rows; thread tid takes row i*R + tid/(d/8), chunk tid%(d/8).
+// V: the 4 keys kq*4 .. kq*4+3 of vquad_key(tid), channels dof*8 .. dof*8+7.
+template <int D>
+struct TileOffsets {
+    uint32_t k[TileCfg<D>::K_LOADS];   // row*D*2 + chunk*16
+    uint32_t v;                        // (kq*4)*D*2 + dof*16
+    int k_row[TileCfg<D>::K_LOADS];
+    int v_key;                         // kq*4
+    __device__ __forceinline__ TileOffsets(int tid)
+    {
+        using C = TileCfg<D>;
+#pragma unroll
+        for (int i = 0; i < C::K_LOADS; ++i) {
+            const int u = i * C::kThreads + tid;
+            k_row[i] = u / C::KCPR;
+            k[i] = (uint32_t)(k_row[i] * D * 2 + (u % C::KCPR) * 16);
+        }
+        v_key = vquad_key(tid, D) * 4;
+        v = (uint32_t)(v_key * D * 2 + (tid % (D / 8)) * 16);
+    }
+};
+
+// Zero the staged rows at or past kv_end (keys of the tail tile that do not
+// exist, or belong to the next context split).
+template <int D>
+__device__ __forceinline__ void zero_tail(KVStage<D>& st, const TileOffsets<D>& off, int key_base, int kv_end,
+                                          int tid)
 {
     using C = TileCfg<D>;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < C::K_LOADS; ++i) {
-        int u = i * C::kThreads + tid;
-        int row = u / C::KCPR, chunk = u % C::KCPR;
-        int key = key_base + row;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (key < kv_end) val = *(const u32x4*)(kv.k_row(key) + chunk * 16);
-        st.k[i] = val;
-    }
+    for (int i = 0; i < C::K_LOADS; ++i)
+        if (key_base + off.k_row[i] >= kv_end) st.k[i] = z;
     if (tid < C::V_QUADS) {
-        int kq = tid / (D / 8), dof = tid % (D / 8);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int key = key_base + kq * 4 + r;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (key < kv_end) val = *(const u32x4*)(kv.v_row(key) + dof * 16);
-            st.v[r] = val;
-        }
+        for (int r = 0; r < 4; ++r)
+            if (key_base + off.v_key + r >= kv_end) st.v[r] = z;
     }
 }
 
@@ -57,9 +74,12 @@ struct TileOut {
 };
 
 template <int D, class KV>
-__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2,
+__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
                                                char* lds)
 {
+    // scale * log2(e); a zero scale becomes a tiny positive factor (every
+    // allowed key still gets p = 2^0 = 1 exactly, masked keys 2^-inf = 0)
+    const float c2 = fmaxf(c2_in, 1e-30f);
     using C = TileCfg<D>;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
@@ -99,17 +119,21 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     ws.m = -INFINITY;
     ws.l = 0.f;
 
+    const float thr = kRescaleLog2 / c2;
+    const TileOffsets<D> toff(tid);
     KVStage<D> st;
     int key_base = P.kv_begin;
-    if (key_base < t_end) load_stage<D>(st, kv, key_base, P.kv_end, tid);
+    if (key_base < t_end) kv.load(st, toff, key_base, P.kv_end, tid);
     for (; key_base < t_end; key_base += C::BN) {
         __syncthreads();
         stage_to_lds<D>(st, lds_k, lds_v, tid);
         __syncthreads();
-        if (key_base + C::BN < t_end) load_stage<D>(st, kv, key_base + C::BN, P.kv_end, tid);
+        if (key_base + C::BN < t_end) kv.load(st, toff, key_base + C::BN, P.kv_end, tid);
         if (wave_active && key_base < w_lim_max) {
-            bool masked = key_base + C::BN > w_lim_min;
-            tile_step<D>(ws, qf, lds_k, lds_v, lane, c2, key_base, q_lim, masked);
+            if (key_base + C::BN > w_lim_min)
+                tile_step<D, true>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
+            else
+                tile_step<D, false>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
         }
     }
 

@@ -262,21 +262,67 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 // head, split); query tiles of one (request, head, split) are adjacent in the
 // XCD-contiguous order so they share K/V pages in that XCD's L2.
 // ============================================================================
+// K/V tiles through the block table.  For d = 128 every K load of a tile
+// covers 16 consecutive keys and every wave's V quads cover 16 consecutive
+// keys, so each of those 16-key groups lies in one page: the page number and
+// its base are wave-uniform (scalar table read) and threads add a 32-bit
+// in-page offset.  Pages past the last one of the context are never looked
+// up (the page index is clamped), and rows past kv_end are zeroed.
 template <int D, int BS>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
     const char* vbase;
     const int32_t* table;    // this request's block-table row
     int64_t blk_bytes;
-    __device__ __forceinline__ const char* k_row(int key) const
+    __device__ __forceinline__ const char* page(const char* base, int key, int last_page) const
     {
-        const int64_t pb = table[key / BS];
-        return kbase + pb * blk_bytes + (key % BS) * (D * 2);
+        const int pg = min(key / BS, last_page);
+        return base + (int64_t)table[pg] * blk_bytes;
     }
-    __device__ __forceinline__ const char* v_row(int key) const
+    __device__ __forceinline__ void load(KVStage<D>& st, const TileOffsets<D>& off, int key_base, int kv_end,
+                                         int tid) const
     {
-        const int64_t pb = table[key / BS];
-        return vbase + pb * blk_bytes + (key % BS) * (D * 2);
+        using C = TileCfg<D>;
+        const int last_page = (kv_end - 1) / BS;
+        const int last = kv_end - 1 - key_base;
+        if constexpr (D == 128) {
+            static_assert(256 / (D / 8) == 16 && BS % 16 == 0, "16-key groups must sit in one page");
+#pragma unroll
+            for (int i = 0; i < C::K_LOADS; ++i) {
+                const int key = key_base + 16 * i;                    // group base, uniform
+                const char* pgb = page(kbase, key, last_page);
+                const int row = min(off.k_row[i], max(last, 16 * i)); // stays inside the group's page
+                const int in_page = (key % BS) + (row - 16 * i);
+                st.k[i] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.k[i] % (D * 2)));
+            }
+            if (tid < C::V_QUADS) {
+                const int key = key_base + (off.v_key & ~15);          // wave-uniform 16-key group
+                const char* pgb = page(vbase, key, last_page);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = min(off.v_key + r, max(last, off.v_key & ~15));
+                    const int in_page = (key % BS) + (row - (off.v_key & ~15));
+                    st.v[r] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.v % (D * 2)));
+                }
+            }
+        } else {
+            // generic path: one table read per row
+#pragma unroll
+            for (int i = 0; i < C::K_LOADS; ++i) {
+                const int key = key_base + min(off.k_row[i], max(last, 0));
+                st.k[i] = *(const u32x4*)(page(kbase, key, last_page) + (uint32_t)((key % BS) * (D * 2)) +
+                                          (off.k[i] % (D * 2)));
+            }
+            if (tid < C::V_QUADS) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = key_base + min(off.v_key + r, max(last, 0));
+                    st.v[r] = *(const u32x4*)(page(vbase, key, last_page) + (uint32_t)((key % BS) * (D * 2)) +
+                                              (off.v % (D * 2)));
+                }
+            }
+        }
+        if (key_base + C::BN > kv_end) zero_tail<D>(st, off, key_base, kv_end, tid);
     }
 };
 
@@ -424,10 +470,11 @@ PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, 
     const int64_t rows = (int64_t)num_seqs * max_q_len;
     int S;
     if (p.path == 0) {
-        // decode: 4 waves x 8 pages per split by default, halved while the
-        // batch would leave the chip short of workgroups
+        // decode: 4 waves x 4 pages per split by default (measured best on the
+        // 64-request, 16-token-page decode batch), halved while the batch
+        // would leave the chip short of workgroups
         const int64_t items = rows * H;
-        S = 4 * block_size * 8;
+        S = 4 * block_size * 4;
         while (S > 4 * block_size && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         p.nqt = 1;
     } else {

@@ -21,12 +21,44 @@
 
 namespace attn {
 
+// K/V tiles of one head of a contiguous [B, H, N, d] tensor.  A head slab is
+// N * d * 2 bytes (< 4 GiB for any N the ABI accepts), so the tile base is a
+// wave-uniform pointer and every thread adds a fixed 32-bit offset; the tail
+// tile clamps rows to N - 1 and zeroes them after the load.
+template <int D>
 struct ContigKV {
     const char* k;   // head base (bytes)
     const char* v;
-    int row_bytes;
-    __device__ __forceinline__ const char* k_row(int key) const { return k + (int64_t)key * row_bytes; }
-    __device__ __forceinline__ const char* v_row(int key) const { return v + (int64_t)key * row_bytes; }
+    __device__ __forceinline__ void load(KVStage<D>& st, const TileOffsets<D>& off, int key_base, int kv_end,
+                                         int tid) const
+    {
+        using C = TileCfg<D>;
+        const char* kt = k + (uint32_t)key_base * (uint32_t)(D * 2);
+        const char* vt = v + (uint32_t)key_base * (uint32_t)(D * 2);
+        if (key_base + C::BN <= kv_end) {
+#pragma unroll
+            for (int i = 0; i < C::K_LOADS; ++i) st.k[i] = *(const u32x4*)(kt + off.k[i]);
+            if (tid < C::V_QUADS) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) st.v[r] = *(const u32x4*)(vt + off.v + r * (D * 2));
+            }
+        } else {
+            const int last = kv_end - 1 - key_base;     // last valid row of the tile
+#pragma unroll
+            for (int i = 0; i < C::K_LOADS; ++i) {
+                const int row = min(off.k_row[i], last);
+                st.k[i] = *(const u32x4*)(kt + off.k[i] - (off.k_row[i] - row) * (D * 2));
+            }
+            if (tid < C::V_QUADS) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = min(off.v_key + r, last);
+                    st.v[r] = *(const u32x4*)(vt + off.v + row * (D * 2) - off.v_key * (D * 2));
+                }
+            }
+            zero_tail<D>(st, off, key_base, kv_end, tid);
+        }
+    }
 };
 
 // Linear work id for this workgroup after the XCD-contiguous remap; the grid
@@ -37,7 +69,7 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
     return (bid & 7) * per + (bid >> 3);
 }
 
-template <int D>
+template <int D, bool PAIR>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using C = TileCfg<D>;
@@ -45,16 +77,16 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
     const int nqt = (a.N + C::BM - 1) / C::BM;
-    const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
+    const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
     const int bh = L / per_bh, t = L % per_bh;
     const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes
-    ContigKV kv{(const char*)a.k + head_off, (const char*)a.v + head_off, D * 2};
+    ContigKV<D> kv{(const char*)a.k + head_off, (const char*)a.v + head_off};
     const float c2 = a.scale * kLog2e;
 
     int tiles[2];
     int ntiles = 1;
     tiles[0] = nqt - 1 - t;                 // heavy first
-    if (a.pair) {
+    if (PAIR) {
         tiles[1] = t;
         ntiles = (tiles[1] != tiles[0]) ? 2 : 1;
     }
@@ -170,10 +202,13 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
         const int grid = (int)((n_work + 7) / 8 * 8);
-        if (a.d == 128)
-            hipLaunchKernelGGL(prefill_bf16_kernel<128>, dim3(grid), dim3(256), 0, stream, a);
-        else
-            hipLaunchKernelGGL(prefill_bf16_kernel<64>, dim3(grid), dim3(256), 0, stream, a);
+        if (a.d == 128) {
+            if (a.pair) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, stream, a);
+        } else {
+            if (a.pair) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, stream, a);
+        }
     } else {
         const int nqt = (a.N + 63) / 64;
         const int64_t grid = (int64_t)a.B * a.H * nqt;
