@@ -79,12 +79,12 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
-    // Pair tiles t and n-1-t when a causal launch has too few tiles to keep
-    // every CU busy with a balanced load (env ATTN_PREFILL_PAIR=0/1 forces it).
+    // Pairing tiles t and n-1-t (one workgroup, equal work per workgroup) is
+    // available for causal launches with env ATTN_PREFILL_PAIR=1; it is off by
+    // default because the paired kernel needs more registers than one tile.
     {
         const int nqt = (N + attn::kChunkBM - 1) / attn::kChunkBM;
-        const int64_t tiles = (int64_t)B * H * nqt;
-        int pair = (a.causal && nqt >= 2 && tiles <= 2048) ? 1 : 0;
+        int pair = 0;
         const char* env = getenv("ATTN_PREFILL_PAIR");
         if (env && *env) pair = atoi(env) ? 1 : 0;
         if (!a.causal || nqt < 2) pair = 0;

@@ -17,11 +17,13 @@
 //    accumulators (8 consecutive registers = 8 keys per lane); the key order
 //    inside each 16-key MFMA step is permuted consistently on the V side, which
 //    leaves the contraction unchanged.
-//  * K tiles sit in LDS row-major; V tiles are written to LDS transposed
+//  * K tiles sit in LDS row-major with rows padded by 16 bytes, so 16
+//    consecutive rows start in 16 distinct bank groups and every read address
+//    is one base plus an immediate.  V tiles are written to LDS transposed
 //    (d-major, keys contiguous, in the permuted order) so that each lane reads
-//    its 8 keys of one d-column with a single 16-byte LDS read.  Both tiles use
-//    an XOR swizzle of 16-byte chunks so that 16 consecutive lanes hit 16
-//    distinct chunks of a 256-byte LDS line (no bank conflicts on the reads).
+//    its 8 keys of one d-column with a single 16-byte LDS read; the V^T rows
+//    use an XOR swizzle of 16-byte chunks within each 256-byte line.  Reads
+//    and the transposing writes are both free of bank conflicts.
 //  * Softmax runs in base 2: scores are scaled by scale*log2(e) inside one FMA
 //    and exponentiated with the hardware exp2.  P is rounded to bf16 (round to
 //    nearest even) for the MFMA and the running sum adds those rounded values.
@@ -51,17 +53,6 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk, uint32_t c
     return ((L & ~15u) | ((L & 15u) ^ ((L >> 4) & 15u))) * 16u;
 }
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of row d of the V^T tile (rows of
-// 8 chunks, two rows per 256-byte line).  The in-line chunk index is XORed
-// with bits of the line number and of d >> 5, so that both the MFMA reads
-// (16 consecutive d, one chunk) and the transposing writes (d spaced by 8,
-// both 8-byte halves of a chunk per 32-lane pass) hit distinct banks.
-__device__ __forceinline__ uint32_t vswz(uint32_t d, uint32_t chunk)
-{
-    const uint32_t u = ((d & 1u) << 3) | chunk;
-    return ((d >> 1) * 16u + (u ^ (((d >> 1) ^ (d >> 5)) & 15u))) * 16u;
-}
-
 // Position of key offset o (0..15) inside a 16-key MFMA step of the V^T tile:
 // bits 2 and 3 are swapped, so that lane half g finds keys {4g..4g+3} and
 // {8+4g..8+4g+3} -- exactly the keys its S^T accumulator registers hold --
@@ -71,9 +62,19 @@ __device__ __forceinline__ uint32_t vperm16(uint32_t o)
     return (o & 3u) | ((o & 4u) << 1) | ((o & 8u) >> 1);
 }
 
-__device__ __forceinline__ float xor32(float x)
+// max / sum of x over lanes l and l ^ 32 (the two halves holding one
+// query's keys), through the gfx950 lane-half swap instead of an LDS permute
+__device__ __forceinline__ float half_max(float x)
 {
-    return __shfl_xor(x, 32, 64);
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c)
@@ -112,23 +113,20 @@ struct TileCfg {
     static constexpr int KBLK = BN / 32;            // 32-key blocks of S^T
     static constexpr int K_LOADS = BN * KCPR / kThreads;    // 16 B K loads per thread
     static constexpr int V_QUADS = (BN / 4) * (D / 8);      // 4-key x 8-d V blocks
-    static constexpr int LDS_K = BN * D * 2;
+    static constexpr int KSTRIDE = D * 2 + 16;      // padded K row in LDS (bytes)
+    static constexpr int LDS_K = BN * KSTRIDE;
     static constexpr int LDS_V = BN * D * 2;
+    static constexpr int LDS_TOTAL = 2 * (LDS_K + LDS_V);   // double-buffered
     static_assert(BN * KCPR % kThreads == 0, "K tile must split evenly");
     static_assert(V_QUADS <= kThreads, "one V block per thread at most");
 };
 
-// Which 4-key quad of the V tile thread `tid` stages: consecutive groups of
-// d/8 threads take quads whose permuted slots alternate between the two
-// 8-byte halves of a 16-byte chunk (quad order 0, 2, 1, 3 inside each
-// 16-key step), so every 32-lane pass of the transposing LDS writes covers
-// both halves.
-__device__ __forceinline__ int vquad_key(int tid, int d)
-{
-    const int q = tid / (d / 8);
-    const int lo = q & 3;
-    return (q & ~3) | ((lo & 1) << 1) | (lo >> 1);
-}
+// The 4-key x 8-channel block of the V tile that thread `tid` stages: wave w
+// takes channel octets 4w .. 4w+3 for all 16 key quads (lane % 4 picks the
+// octet, lane / 4 the quad).  With this order every 32-lane pass of the
+// transposing LDS writes hits 32 distinct bank pairs.
+__device__ __forceinline__ int vblock_quad(int tid) { return (tid & 63) >> 2; }
+__device__ __forceinline__ int vblock_oct(int tid) { return ((tid >> 6) << 2) | (tid & 3); }
 
 // Per-thread registers holding the next K/V tile while the current one is
 // being consumed (the global loads are issued one tile ahead).
@@ -148,10 +146,10 @@ __device__ __forceinline__ void stage_to_lds(const KVStage<D>& st, char* lds_k, 
     for (int i = 0; i < C::K_LOADS; ++i) {
         int u = i * C::kThreads + tid;
         int row = u / C::KCPR, chunk = u % C::KCPR;
-        *(u32x4*)(lds_k + swz(row, chunk, C::KCPR)) = st.k[i];
+        *(u32x4*)(lds_k + row * C::KSTRIDE + chunk * 16) = st.k[i];
     }
     if (tid < C::V_QUADS) {
-        const int kq = vquad_key(tid, D), dof = tid % (D / 8);
+        const int kq = vblock_quad(tid), dof = vblock_oct(tid);
         int key0 = kq * 4;                                   // first of 4 keys
         uint32_t kp = (key0 & ~15) | vperm16(key0 & 15);     // permuted slot (4-aligned)
         uint32_t chunk = kp >> 3, half = (kp >> 2) & 1;
@@ -166,8 +164,8 @@ __device__ __forceinline__ void stage_to_lds(const KVStage<D>& st, char* lds_k, 
             hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
             hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
             uint32_t d_lo = dof * 8 + 2 * e2, d_hi = d_lo + 1;
-            *(u32x2*)(lds_v + vswz(d_lo, chunk) + half * 8) = lo;
-            *(u32x2*)(lds_v + vswz(d_hi, chunk) + half * 8) = hi;
+            *(u32x2*)(lds_v + swz(d_lo, chunk, C::VCPR) + half * 8) = lo;
+            *(u32x2*)(lds_v + swz(d_hi, chunk, C::VCPR) + half * 8) = hi;
         }
     }
 }
@@ -225,7 +223,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
         f32x16 acc = {};
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            u32x4 a = *(const u32x4*)(lds_k + swz(kb * 32 + r32, ks * 2 + g, C::KCPR));
+            u32x4 a = *(const u32x4*)(lds_k + (kb * 32 + r32) * C::KSTRIDE + (ks * 2 + g) * 16);
             acc = mfma32(as_bf16x8(a), qf[ks], acc);
         }
         s[kb] = acc;
@@ -247,7 +245,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s[kb][i], s[kb][i + 1]));
-    mt = fmaxf(mt, xor32(mt));
+    mt = half_max(mt);
     // ---- lazy offset update (wave-uniform decision) --------------------------
     const bool need = mt > ws.m + thr;
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -284,7 +282,7 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
             const int chunk = kb * 4 + h * 2 + g;
 #pragma unroll
             for (int db = 0; db < C::DBLK; ++db) {
-                u32x4 a = *(const u32x4*)(lds_v + vswz(db * 32 + r32, chunk));
+                u32x4 a = *(const u32x4*)(lds_v + swz(db * 32 + r32, chunk, C::VCPR));
                 ws.o[db] = mfma32(as_bf16x8(a), b, ws.o[db]);
             }
         }

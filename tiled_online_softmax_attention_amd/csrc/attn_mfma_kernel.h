@@ -24,26 +24,25 @@ struct TileProblem {
 
 // Per-thread byte offsets of the rows this thread loads inside one K/V tile
 // (identical for every tile).  K: load i covers tile rows [i*R, (i+1)*R) with
-// R = 256 / (d/8) rows; thread tid takes row i*R + tid/(d/8), chunk tid%(d/8).
-// V: the 4 keys kq*4 .. kq*4+3 of vquad_key(tid), channels dof*8 .. dof*8+7.
+// R = 256 / (d/8) rows; thread tid takes row i*R + tid/(d/8), chunk tid%(d/8),
+// so its offset is tid*16 + i*R*d*2.  V: keys vblock_quad(tid)*4 + 0..3,
+// channels vblock_oct(tid)*8 .. +7.
 template <int D>
 struct TileOffsets {
-    uint32_t k[TileCfg<D>::K_LOADS];   // row*D*2 + chunk*16
-    uint32_t v;                        // (kq*4)*D*2 + dof*16
-    int k_row[TileCfg<D>::K_LOADS];
-    int v_key;                         // kq*4
+    static constexpr int R = TileCfg<D>::kThreads / TileCfg<D>::KCPR;   // K rows per load
+    uint32_t k0;      // tid * 16 (offset of load 0)
+    int k_row0;       // tid / (d/8)
+    int v_key;        // first key of this thread's V quad
+    uint32_t v;       // v_key*D*2 + octet*16
     __device__ __forceinline__ TileOffsets(int tid)
     {
-        using C = TileCfg<D>;
-#pragma unroll
-        for (int i = 0; i < C::K_LOADS; ++i) {
-            const int u = i * C::kThreads + tid;
-            k_row[i] = u / C::KCPR;
-            k[i] = (uint32_t)(k_row[i] * D * 2 + (u % C::KCPR) * 16);
-        }
-        v_key = vquad_key(tid, D) * 4;
-        v = (uint32_t)(v_key * D * 2 + (tid % (D / 8)) * 16);
+        k0 = (uint32_t)tid * 16u;
+        k_row0 = tid / TileCfg<D>::KCPR;
+        v_key = vblock_quad(tid) * 4;
+        v = (uint32_t)(v_key * D * 2 + vblock_oct(tid) * 16);
     }
+    __device__ __forceinline__ uint32_t k(int i) const { return k0 + (uint32_t)(i * R * D * 2); }
+    __device__ __forceinline__ int k_row(int i) const { return k_row0 + i * R; }
 };
 
 // Zero the staged rows at or past kv_end (keys of the tail tile that do not
@@ -56,7 +55,7 @@ __device__ __forceinline__ void zero_tail(KVStage<D>& st, const TileOffsets<D>& 
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < C::K_LOADS; ++i)
-        if (key_base + off.k_row[i] >= kv_end) st.k[i] = z;
+        if (key_base + off.k_row(i) >= kv_end) st.k[i] = z;
     if (tid < C::V_QUADS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -83,8 +82,6 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     using C = TileCfg<D>;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6, g = lane >> 5, r32 = lane & 31;
-    char* lds_k = lds;
-    char* lds_v = lds + C::LDS_K;
 
     // ---- Q^T fragments for this lane's query --------------------------------
     const int qrow = w * 32 + r32;
@@ -122,23 +119,36 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     const float thr = kRescaleLog2 / c2;
     const TileOffsets<D> toff(tid);
     KVStage<D> st;
-    int key_base = P.kv_begin;
-    if (key_base < t_end) kv.load(st, toff, key_base, P.kv_end, tid);
-    for (; key_base < t_end; key_base += C::BN) {
+    // Two LDS buffers: while tile j is consumed from one, tile j+1 is written
+    // into the other (its global loads were issued one tile earlier), so each
+    // tile costs one barrier.
+    const int ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
+    if (ntile > 0) {
+        kv.load(st, toff, P.kv_begin, P.kv_end, tid);
+        stage_to_lds<D>(st, lds, lds + C::LDS_K, tid);
+        if (ntile > 1) kv.load(st, toff, P.kv_begin + C::BN, P.kv_end, tid);
         __syncthreads();
-        stage_to_lds<D>(st, lds_k, lds_v, tid);
-        __syncthreads();
-        if (key_base + C::BN < t_end) kv.load(st, toff, key_base + C::BN, P.kv_end, tid);
+    }
+    for (int j = 0; j < ntile; ++j) {
+        const int key_base = P.kv_begin + j * C::BN;
+        const char* lds_k = lds + (j & 1) * (C::LDS_K + C::LDS_V);
+        const char* lds_v = lds_k + C::LDS_K;
         if (wave_active && key_base < w_lim_max) {
             if (key_base + C::BN > w_lim_min)
                 tile_step<D, true>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
             else
                 tile_step<D, false>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
         }
+        if (j + 1 < ntile) {
+            char* nk = lds + ((j + 1) & 1) * (C::LDS_K + C::LDS_V);
+            stage_to_lds<D>(st, nk, nk + C::LDS_K, tid);
+            if (j + 2 < ntile) kv.load(st, toff, key_base + 2 * C::BN, P.kv_end, tid);
+        }
+        __syncthreads();
     }
 
     // ---- epilogue -------------------------------------------------------------
-    const float l_tot = ws.l + xor32(ws.l);
+    const float l_tot = half_sum(ws.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < P.n_rows) {
         if (out.fp32_out) {

@@ -263,11 +263,11 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 // XCD-contiguous order so they share K/V pages in that XCD's L2.
 // ============================================================================
 // K/V tiles through the block table.  For d = 128 every K load of a tile
-// covers 16 consecutive keys and every wave's V quads cover 16 consecutive
-// keys, so each of those 16-key groups lies in one page: the page number and
-// its base are wave-uniform (scalar table read) and threads add a 32-bit
-// in-page offset.  Pages past the last one of the context are never looked
-// up (the page index is clamped), and rows past kv_end are zeroed.
+// covers 16 consecutive keys, which lie in one page: the page number and its
+// base are wave-uniform (scalar table read) and threads add a 32-bit in-page
+// offset.  A thread's V quad (4 consecutive keys) also lies in one page, read
+// through a per-lane table entry.  Pages past the last one of the context are
+// never looked up (the page index is clamped), and rows past kv_end are zeroed.
 template <int D, int BS>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
@@ -286,40 +286,30 @@ struct PagedKV {
         const int last_page = (kv_end - 1) / BS;
         const int last = kv_end - 1 - key_base;
         if constexpr (D == 128) {
-            static_assert(256 / (D / 8) == 16 && BS % 16 == 0, "16-key groups must sit in one page");
+            static_assert(TileOffsets<D>::R == 16 && BS % 16 == 0, "16-key groups must sit in one page");
 #pragma unroll
             for (int i = 0; i < C::K_LOADS; ++i) {
                 const int key = key_base + 16 * i;                    // group base, uniform
                 const char* pgb = page(kbase, key, last_page);
-                const int row = min(off.k_row[i], max(last, 16 * i)); // stays inside the group's page
+                const int row = min(off.k_row(i), max(last, 16 * i)); // stays inside the group's page
                 const int in_page = (key % BS) + (row - 16 * i);
-                st.k[i] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.k[i] % (D * 2)));
-            }
-            if (tid < C::V_QUADS) {
-                const int key = key_base + (off.v_key & ~15);          // wave-uniform 16-key group
-                const char* pgb = page(vbase, key, last_page);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = min(off.v_key + r, max(last, off.v_key & ~15));
-                    const int in_page = (key % BS) + (row - (off.v_key & ~15));
-                    st.v[r] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.v % (D * 2)));
-                }
+                st.k[i] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.k0 % (D * 2)));
             }
         } else {
-            // generic path: one table read per row
 #pragma unroll
             for (int i = 0; i < C::K_LOADS; ++i) {
-                const int key = key_base + min(off.k_row[i], max(last, 0));
+                const int key = key_base + min(off.k_row(i), max(last, 0));
                 st.k[i] = *(const u32x4*)(page(kbase, key, last_page) + (uint32_t)((key % BS) * (D * 2)) +
-                                          (off.k[i] % (D * 2)));
+                                          (off.k(i) % (D * 2)));
             }
-            if (tid < C::V_QUADS) {
+        }
+        if (tid < C::V_QUADS) {
+            const int key4 = key_base + min(off.v_key, max(last & ~3, 0));   // quad base, one page
+            const char* pgb = page(vbase, key4, last_page);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = key_base + min(off.v_key + r, max(last, 0));
-                    st.v[r] = *(const u32x4*)(page(vbase, key, last_page) + (uint32_t)((key % BS) * (D * 2)) +
-                                              (off.v % (D * 2)));
-                }
+            for (int r = 0; r < 4; ++r) {
+                const int key = min(key_base + off.v_key + r, max(kv_end - 1, key4));
+                st.v[r] = *(const u32x4*)(pgb + (uint32_t)((key % BS) * (D * 2)) + (off.v % (D * 2)));
             }
         }
         if (key_base + C::BN > kv_end) zero_tail<D>(st, off, key_base, kv_end, tid);
@@ -330,7 +320,7 @@ template <int D, int BS>
 __global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_work)
 {
     using C = TileCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_K + C::LDS_V];
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_TOTAL];
     const int per = gridDim.x >> 3;
     int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (L >= n_work) return;

@@ -37,7 +37,7 @@ struct ContigKV {
         const char* vt = v + (uint32_t)key_base * (uint32_t)(D * 2);
         if (key_base + C::BN <= kv_end) {
 #pragma unroll
-            for (int i = 0; i < C::K_LOADS; ++i) st.k[i] = *(const u32x4*)(kt + off.k[i]);
+            for (int i = 0; i < C::K_LOADS; ++i) st.k[i] = *(const u32x4*)(kt + off.k(i));
             if (tid < C::V_QUADS) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) st.v[r] = *(const u32x4*)(vt + off.v + r * (D * 2));
@@ -46,8 +46,8 @@ struct ContigKV {
             const int last = kv_end - 1 - key_base;     // last valid row of the tile
 #pragma unroll
             for (int i = 0; i < C::K_LOADS; ++i) {
-                const int row = min(off.k_row[i], last);
-                st.k[i] = *(const u32x4*)(kt + off.k[i] - (off.k_row[i] - row) * (D * 2));
+                const int row = min(off.k_row(i), last);
+                st.k[i] = *(const u32x4*)(kt + off.k(i) - (off.k_row(i) - row) * (D * 2));
             }
             if (tid < C::V_QUADS) {
 #pragma unroll
@@ -73,7 +73,7 @@ template <int D, bool PAIR>
 __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using C = TileCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_K + C::LDS_V];
+    __shared__ __attribute__((aligned(16))) char lds[C::LDS_TOTAL];
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
     const int nqt = (a.N + C::BM - 1) / C::BM;
