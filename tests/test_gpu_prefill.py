@@ -15,22 +15,33 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_case(B, H, N, d, dtype, causal, seed, pair=None):
+class env_set:
+    """Set environment knobs of the library for one call."""
+
+    def __init__(self, **kw):
+        self.kw = {k: v for k, v in kw.items() if v is not None}
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kw}
+        for k, v in self.kw.items():
+            os.environ[k] = str(v)
+
+    def __exit__(self, *a):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def run_case(B, H, N, d, dtype, causal, seed, pair=None, qb=None):
     cfg = inputs.PrefillConfig("case", B, H, N, d, dtype, causal, seed)
-    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s" % (B, H, N, d, dtype, causal, seed, pair))
+    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s qb=%s" % (B, H, N, d, dtype, causal, seed,
+                                                                                   pair, qb))
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    old = os.environ.get("ATTN_PREFILL_PAIR")
-    if pair is not None:
-        os.environ["ATTN_PREFILL_PAIR"] = "1" if pair else "0"
-    try:
+    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair), ATTN_PREFILL_QB=qb):
         o, lse = attn.prefill(q, k, v, causal, cfg.scale)
         torch.cuda.synchronize()
-    finally:
-        if pair is not None:
-            if old is None:
-                os.environ.pop("ATTN_PREFILL_PAIR", None)
-            else:
-                os.environ["ATTN_PREFILL_PAIR"] = old
     o_ref, lse_ref = oracle.attention(q, k, v, cfg.scale, causal)
     return check_close("B%dH%dN%dd%d" % (B, H, N, d), o, o_ref, lse, lse_ref, dtype), (q, k, v, o, lse)
 
@@ -66,6 +77,11 @@ def test_fp32_shapes(N, d, causal):
 @pytest.mark.parametrize("pair", [False, True])
 def test_pair_mode_matches_oracle(pair):
     run_case(2, 4, 1000, 128, torch.bfloat16, True, 7, pair=pair)
+
+
+@pytest.mark.parametrize("N,d,causal", [(1, 128, True), (300, 128, True), (700, 128, False), (513, 64, True)])
+def test_two_query_blocks_per_wave(N, d, causal):
+    run_case(1, 3, N, d, torch.bfloat16, causal, 400 + N, qb=2)
 
 
 def test_deterministic_and_pair_independent():

@@ -6,7 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_internal.h"
 
 namespace {
@@ -71,6 +71,7 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     int rc = check_scale(scale);
     if (rc) return rc;
     if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_SHAPE;
+    if ((int64_t)N * d * (dtype == ATTN_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;  // 32-bit row offsets
     rc = check_device();
     if (rc) return rc;
     attn::PrefillArgs a{};
@@ -79,15 +80,21 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
-    // Pairing tiles t and n-1-t (one workgroup, equal work per workgroup) is
-    // available for causal launches with env ATTN_PREFILL_PAIR=1; it is off by
-    // default because the paired kernel needs more registers than one tile.
+    // bf16 query tiles: 128 rows (one 32-query block per wave, two workgroups
+    // per CU).  256-row tiles (two blocks per wave sharing every LDS fragment,
+    // one workgroup per CU) are opt-in with ATTN_PREFILL_QB=2: they halve LDS
+    // reads per MFMA but need the whole register file and measured slower.
+    // Pairing tiles t and n-1-t (equal work per workgroup) is opt-in for
+    // causal 128-row launches with ATTN_PREFILL_PAIR=1.
     {
-        const int nqt = (N + attn::kChunkBM - 1) / attn::kChunkBM;
+        int qb = 1;
+        const char* env_qb = getenv("ATTN_PREFILL_QB");
+        if (env_qb && *env_qb) qb = (atoi(env_qb) == 2) ? 2 : 1;
         int pair = 0;
         const char* env = getenv("ATTN_PREFILL_PAIR");
         if (env && *env) pair = atoi(env) ? 1 : 0;
-        if (!a.causal || nqt < 2) pair = 0;
+        if (!a.causal || qb != 1 || N <= 128) pair = 0;
+        a.qb = qb;
         a.pair = pair;
     }
     rc = attn::launch_prefill(a, (hipStream_t)stream);

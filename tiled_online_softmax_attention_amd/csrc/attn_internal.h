@@ -19,7 +19,8 @@ struct PrefillArgs {
     float scale;
     int causal;
     int dtype;      // 0 bf16, 1 fp32
-    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t
+    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t (qb == 1 only)
+    int qb;         // bf16: 32-query blocks per wave (1: 128-row tiles, 2: 256-row tiles)
     int n_work;     // filled by the launcher
 };
 
@@ -29,6 +30,7 @@ struct PagedPlan {
     int split_tokens;    // keys per context split (multiple of the page size)
     int max_splits;      // ceil(max_ctx_len / split_tokens)
     int nqt;             // query tiles per request (chunk path)
+    int qb;              // chunk path: 32-query blocks per wave (tile = 128 * qb rows)
     size_t ws_o_bytes;   // fp32 partial outputs
     size_t ws_lse_bytes; // fp32 partial log-sum-exps
     size_t ws_bytes;     // total (0 when max_splits == 1)
@@ -69,7 +71,6 @@ struct GatherArgs {
 };
 
 constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode kernel
-constexpr int kChunkBM = 128;      // query rows per MFMA workgroup
 
 PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len);
 

@@ -262,69 +262,39 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 // head, split); query tiles of one (request, head, split) are adjacent in the
 // XCD-contiguous order so they share K/V pages in that XCD's L2.
 // ============================================================================
-// K/V tiles through the block table.  For d = 128 every K load of a tile
-// covers 16 consecutive keys, which lie in one page: the page number and its
-// base are wave-uniform (scalar table read) and threads add a 32-bit in-page
-// offset.  A thread's V quad (4 consecutive keys) also lies in one page, read
-// through a per-lane table entry.  Pages past the last one of the context are
-// never looked up (the page index is clamped), and rows past kv_end are zeroed.
+// K/V rows through the block table.  A 16-row group of keys (16-aligned)
+// lies inside one page of 16 or 32 tokens, so the group base is one scalar
+// table read; keys are clamped to the last key of the context first, so no
+// page past the context is ever looked up.
 template <int D, int BS>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
     const char* vbase;
     const int32_t* table;    // this request's block-table row
     int64_t blk_bytes;
-    __device__ __forceinline__ const char* page(const char* base, int key, int last_page) const
+    __device__ __forceinline__ const char* k_group(int key, int kv_end) const
     {
-        const int pg = min(key / BS, last_page);
-        return base + (int64_t)table[pg] * blk_bytes;
+        return kbase + (int64_t)table[min(key, kv_end - 1) / BS] * blk_bytes;
     }
-    __device__ __forceinline__ void load(KVStage<D>& st, const TileOffsets<D>& off, int key_base, int kv_end,
-                                         int tid) const
+    __device__ __forceinline__ const char* v_group(int key, int kv_end) const
     {
-        using C = TileCfg<D>;
-        const int last_page = (kv_end - 1) / BS;
-        const int last = kv_end - 1 - key_base;
-        if constexpr (D == 128) {
-            static_assert(TileOffsets<D>::R == 16 && BS % 16 == 0, "16-key groups must sit in one page");
-#pragma unroll
-            for (int i = 0; i < C::K_LOADS; ++i) {
-                const int key = key_base + 16 * i;                    // group base, uniform
-                const char* pgb = page(kbase, key, last_page);
-                const int row = min(off.k_row(i), max(last, 16 * i)); // stays inside the group's page
-                const int in_page = (key % BS) + (row - 16 * i);
-                st.k[i] = *(const u32x4*)(pgb + (uint32_t)(in_page * (D * 2)) + (off.k0 % (D * 2)));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < C::K_LOADS; ++i) {
-                const int key = key_base + min(off.k_row(i), max(last, 0));
-                st.k[i] = *(const u32x4*)(page(kbase, key, last_page) + (uint32_t)((key % BS) * (D * 2)) +
-                                          (off.k(i) % (D * 2)));
-            }
-        }
-        if (tid < C::V_QUADS) {
-            const int key4 = key_base + min(off.v_key, max(last & ~3, 0));   // quad base, one page
-            const char* pgb = page(vbase, key4, last_page);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = min(key_base + off.v_key + r, max(kv_end - 1, key4));
-                st.v[r] = *(const u32x4*)(pgb + (uint32_t)((key % BS) * (D * 2)) + (off.v % (D * 2)));
-            }
-        }
-        if (key_base + C::BN > kv_end) zero_tail<D>(st, off, key_base, kv_end, tid);
+        return vbase + (int64_t)table[min(key, kv_end - 1) / BS] * blk_bytes;
     }
+    __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1) % BS; }
+    __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
 };
 
-template <int D, int BS>
-__global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_work)
+template <int D, int BS, int QB>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void paged_chunk_kernel(PagedArgs a, int n_work)
 {
     using C = TileCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_TOTAL];
+    constexpr int BM = QueryTile<QB>::BM;
+    __shared__ __attribute__((aligned(16))) char lds0[C::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[C::BUF_BYTES];
     const int per = gridDim.x >> 3;
     int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (L >= n_work) return;
-    const int nqt = (a.max_q_len + C::BM - 1) / C::BM;
+    const int nqt = (a.max_q_len + BM - 1) / BM;
     const int qt = L % nqt;
     L /= nqt;
     const int split = L % a.max_splits;
@@ -332,12 +302,12 @@ __global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_
     const int h = L % a.H;
     const int r = L / a.H;
     const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
-    if (qt * C::BM >= ql) return;
+    if (qt * BM >= ql) return;
     const int S = a.split_tokens;
     const int nsplit = (ctx + S - 1) / S;
     if (split >= nsplit) return;
     const int lane = threadIdx.x & 63;
-    const int64_t row0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * C::BM;
+    const int64_t row0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * BM;
 
     PagedKV<D, BS> kv;
     kv.kbase = (const char*)a.k_pool + (int64_t)h * BS * D * 2;
@@ -348,8 +318,8 @@ __global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_
     TileProblem P;
     P.q = (const char*)a.q + (row0 * a.H + h) * D * 2;
     P.q_stride = (int64_t)a.H * D * 2;
-    P.n_rows = min(C::BM, ql - qt * C::BM);
-    P.q_pos0 = ctx - ql + qt * C::BM;
+    P.n_rows = min(BM, ql - qt * BM);
+    P.q_pos0 = ctx - ql + qt * BM;
     P.causal = 1;
     P.kv_begin = split * S;
     P.kv_end = min(ctx, (split + 1) * S);
@@ -361,14 +331,14 @@ __global__ __launch_bounds__(256, 2) void paged_chunk_kernel(PagedArgs a, int n_
         out.lse_stride = a.H;
         out.fp32_out = 0;
     } else {
-        const int64_t slot = (((int64_t)r * a.max_q_len + qt * C::BM) * a.H + h) * a.max_splits + split;
+        const int64_t slot = (((int64_t)r * a.max_q_len + qt * BM) * a.H + h) * a.max_splits + split;
         out.o = (char*)(a.ws_o + slot * D);
         out.o_stride = (int64_t)a.H * a.max_splits * D * 4;
         out.lse = a.ws_lse + slot;
         out.lse_stride = (int64_t)a.H * a.max_splits;
         out.fp32_out = 1;
     }
-    run_query_tile<D>(P, kv, out, a.scale * kLog2e, lds);
+    run_query_tile<D, QB>(P, kv, out, a.scale * kLog2e, lds0, lds1);
 }
 
 // ============================================================================
@@ -468,7 +438,12 @@ PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, 
         while (S > 4 * block_size && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         p.nqt = 1;
     } else {
-        p.nqt = (max_q_len + kChunkBM - 1) / kChunkBM;
+        // 128-row query tiles; 256-row tiles (two 32-query blocks per wave) are
+        // opt-in with ATTN_CHUNK_QB=2 (they measured slower: register spills)
+        p.qb = 1;
+        const int envqb = env_int("ATTN_CHUNK_QB", 0);
+        if (envqb == 1 || envqb == 2) p.qb = envqb;
+        p.nqt = (max_q_len + 128 * p.qb - 1) / (128 * p.qb);
         const int64_t items = (int64_t)num_seqs * p.nqt * H;
         S = 8192;
         while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < 2048) S /= 2;
@@ -500,7 +475,10 @@ static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_
     } else {
         const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H * a.max_splits;
         const int64_t grid = (n_work + 7) / 8 * 8;
-        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
+        if (plan.qb == 2)
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
+        else
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
     }
     if (a.max_splits > 1) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;

@@ -21,44 +21,18 @@
 
 namespace attn {
 
-// K/V tiles of one head of a contiguous [B, H, N, d] tensor.  A head slab is
-// N * d * 2 bytes (< 4 GiB for any N the ABI accepts), so the tile base is a
-// wave-uniform pointer and every thread adds a fixed 32-bit offset; the tail
-// tile clamps rows to N - 1 and zeroes them after the load.
+// K/V rows of one head of a contiguous [B, H, N, d] tensor.  The head slab is
+// one group: row offsets are absolute (N * d * 2 < 4 GiB is checked on the
+// host), clamped to the last row of the context.
 template <int D>
 struct ContigKV {
     const char* k;   // head base (bytes)
     const char* v;
-    __device__ __forceinline__ void load(KVStage<D>& st, const TileOffsets<D>& off, int key_base, int kv_end,
-                                         int tid) const
-    {
-        using C = TileCfg<D>;
-        const char* kt = k + (uint32_t)key_base * (uint32_t)(D * 2);
-        const char* vt = v + (uint32_t)key_base * (uint32_t)(D * 2);
-        if (key_base + C::BN <= kv_end) {
-#pragma unroll
-            for (int i = 0; i < C::K_LOADS; ++i) st.k[i] = *(const u32x4*)(kt + off.k(i));
-            if (tid < C::V_QUADS) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) st.v[r] = *(const u32x4*)(vt + off.v + r * (D * 2));
-            }
-        } else {
-            const int last = kv_end - 1 - key_base;     // last valid row of the tile
-#pragma unroll
-            for (int i = 0; i < C::K_LOADS; ++i) {
-                const int row = min(off.k_row(i), last);
-                st.k[i] = *(const u32x4*)(kt + off.k(i) - (off.k_row(i) - row) * (D * 2));
-            }
-            if (tid < C::V_QUADS) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = min(off.v_key + r, last);
-                    st.v[r] = *(const u32x4*)(vt + off.v + row * (D * 2) - off.v_key * (D * 2));
-                }
-            }
-            zero_tail<D>(st, off, key_base, kv_end, tid);
-        }
-    }
+    uint32_t head_bytes;
+    __device__ __forceinline__ uint32_t group_bytes() const { return head_bytes; }
+    __device__ __forceinline__ const char* k_group(int, int) const { return k; }
+    __device__ __forceinline__ const char* v_group(int, int) const { return v; }
+    __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1); }
 };
 
 // Linear work id for this workgroup after the XCD-contiguous remap; the grid
@@ -69,18 +43,20 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
     return (bid & 7) * per + (bid >> 3);
 }
 
-template <int D, bool PAIR>
-__global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
+template <int D, int QB, bool PAIR>
+__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void prefill_bf16_kernel(PrefillArgs a)
 {
     using C = TileCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds[C::LDS_TOTAL];
+    constexpr int BM = QueryTile<QB>::BM;
+    __shared__ __attribute__((aligned(16))) char lds0[C::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[C::BUF_BYTES];
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
-    const int nqt = (a.N + C::BM - 1) / C::BM;
+    const int nqt = (a.N + BM - 1) / BM;
     const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
     const int bh = L / per_bh, t = L % per_bh;
     const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes
-    ContigKV<D> kv{(const char*)a.k + head_off, (const char*)a.v + head_off};
+    ContigKV<D> kv{(const char*)a.k + head_off, (const char*)a.v + head_off, (uint32_t)a.N * (uint32_t)(D * 2)};
     const float c2 = a.scale * kLog2e;
 
     int tiles[2];
@@ -93,11 +69,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
 #pragma unroll 1
     for (int it = 0; it < ntiles; ++it) {
         const int qt = tiles[it];
-        const int q0 = qt * C::BM;
+        const int q0 = qt * BM;
         TileProblem P;
         P.q = (const char*)a.q + head_off + (int64_t)q0 * D * 2;
         P.q_stride = D * 2;
-        P.n_rows = min(C::BM, a.N - q0);
+        P.n_rows = min(BM, a.N - q0);
         P.q_pos0 = q0;
         P.causal = a.causal;
         P.kv_begin = 0;
@@ -109,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16_kernel(PrefillArgs a)
         out.lse_stride = 1;
         out.fp32_out = 0;
         if (it) __syncthreads();   // LDS reuse across the two tiles
-        run_query_tile<D>(P, kv, out, c2, lds);
+        run_query_tile<D, QB>(P, kv, out, c2, lds0, lds1);
     }
 }
 
@@ -194,7 +170,7 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
     if (a.dtype == 0) {
-        constexpr int BM = TileCfg<128>::BM;
+        const int BM = 128 * a.qb;
         const int nqt = (a.N + BM - 1) / BM;
         const int64_t bh = (int64_t)a.B * a.H;
         const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
@@ -202,13 +178,18 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
         const int grid = (int)((n_work + 7) / 8 * 8);
+#define ATTN_LAUNCH_PREFILL(DD, QQ, PP) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DD, QQ, PP>), dim3(grid), dim3(256), 0, stream, a)
         if (a.d == 128) {
-            if (a.pair) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), dim3(grid), dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), dim3(grid), dim3(256), 0, stream, a);
+            if (a.qb == 2) ATTN_LAUNCH_PREFILL(128, 2, false);
+            else if (a.pair) ATTN_LAUNCH_PREFILL(128, 1, true);
+            else ATTN_LAUNCH_PREFILL(128, 1, false);
         } else {
-            if (a.pair) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), dim3(grid), dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), dim3(grid), dim3(256), 0, stream, a);
+            if (a.qb == 2) ATTN_LAUNCH_PREFILL(64, 2, false);
+            else if (a.pair) ATTN_LAUNCH_PREFILL(64, 1, true);
+            else ATTN_LAUNCH_PREFILL(64, 1, false);
         }
+#undef ATTN_LAUNCH_PREFILL
     } else {
         const int nqt = (a.N + 63) / 64;
         const int64_t grid = (int64_t)a.B * a.H * nqt;
