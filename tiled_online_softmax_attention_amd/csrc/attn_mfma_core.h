@@ -20,11 +20,12 @@
 //    (ds_read_b64_tr_b16): in each 16-lane group, lane i receives element j
 //    from the 8-byte row segment addressed by lane 4j + i/4, at position i%4.
 //  * K and V tiles are copied from global memory straight into LDS
-//    (global_load_lds_dwordx4: lane l of a wave lands at base + 16*l), so no
-//    registers stage them; the source chunk each lane fetches is chosen so
-//    that the tile ends up XOR-swizzled in LDS.  The K swizzle makes the MFMA
-//    K reads (16 consecutive rows, one 16-byte chunk) conflict-free, the V
-//    swizzle makes the transposing reads (4 consecutive rows x 64 bytes per
+//    (buffer_load_dwordx4 ... lds: lane l of a wave lands at base + 16*l),
+//    so no registers stage them; the source each lane fetches is chosen so
+//    that the tile lands in the layout its readers want.  K is stored in
+//    16-row groups, chunk-major, so the MFMA K reads (16 consecutive rows,
+//    one 16-byte chunk) are contiguous; V is row-major with an XOR swizzle
+//    that makes the transposing reads (4 consecutive rows x 64 bytes per
 //    32-lane pass) conflict-free.
 //  * Softmax runs in base 2: scores are scaled by scale*log2(e) inside one FMA
 //    and exponentiated with the hardware exp2.  P is rounded to bf16 (round to
@@ -49,20 +50,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// Linear 16-byte-chunk index after the XOR swizzle used for K tiles: chunks
-// are grouped in 256-byte lines of 16 and the in-line index is XORed with the
-// line number (mod 16).  The map is its own inverse.
-__device__ __forceinline__ uint32_t swz_index(uint32_t L)
-{
-    return (L & ~15u) | ((L & 15u) ^ ((L >> 4) & 15u));
-}
-
-// Byte offset of chunk `chunk` of K row `row` (rows of `cpr` chunks).
-__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk, uint32_t cpr)
-{
-    return swz_index(row * cpr + chunk) * 16u;
-}
 
 // max / sum of x over lanes l and l ^ 32 (the two halves holding one
 // query's keys), through the gfx950 lane-half swap instead of an LDS permute
@@ -149,27 +136,38 @@ __device__ __forceinline__ uint32_t v_ofs(uint32_t row, uint32_t chunk)
     return row * (uint32_t)TileCfg<D>::ROW_BYTES + ((chunk ^ v_row_xor<D>(row)) << 4);
 }
 
-// Source of this lane's part of copy i of wave w's 16-row group (identical
-// for every tile).  Copy i fills LDS rows r0 = 16w + i*ROWS_PER_DMA onwards;
-// lane l lands at byte r0*ROW_BYTES + 16*l, i.e. at physical chunk position
-// r0*KCPR + l, and must fetch the logical (row, chunk) stored there.  Rows
-// are returned relative to the group (0..15), chunks as byte offsets.
+// K tile layout in LDS: 16-row groups, each stored chunk-major (for every
+// 16-byte chunk of the row, the 16 rows' copies of it are contiguous).  The
+// MFMA K reads (16 consecutive rows, one chunk per 16-lane quarter) then
+// touch 256 contiguous bytes: conflict-free without a swizzle, and every
+// read of a tile is one per-lane base plus an immediate.
 template <int D>
-__device__ __forceinline__ void k_dma_src(int w, int i, int lane, int& row, uint32_t& col)
+__device__ __forceinline__ uint32_t k_ofs(uint32_t row, uint32_t chunk)
 {
-    using C = TileCfg<D>;
-    // the swizzle permutes chunks inside 256-byte lines only, which never
-    // straddle a 16-row group, so the row stays inside the group
-    const uint32_t L = swz_index((uint32_t)((16 * w + i * C::ROWS_PER_DMA) * C::KCPR + lane));
-    row = (int)(L / C::KCPR) - 16 * w;
-    col = (L % C::KCPR) * 16u;
+    return (row >> 4) * (16u * TileCfg<D>::ROW_BYTES) + chunk * 256u + (row & 15u) * 16u;
 }
+
+// Sources of the wave-wide LDS copies (lane l of a copy lands at the copy's
+// LDS base + 16*l).  Offsets are bytes from the first row of the wave's
+// 16-row group; copy i adds a wave-uniform step.
+//  K: copy i fills chunks 4i..4i+3 of the group's 16 rows; lane l lands at
+//     row l % 16 of chunk 4i + l / 16.  Step: 4 chunks = 64 source bytes.
+//  V: copy i fills rows i*ROWS_PER_DMA onwards (row-major); lane l lands at
+//     row i*ROWS_PER_DMA + l / KCPR, physical chunk l % KCPR, which holds
+//     logical chunk (l % KCPR) ^ v_row_xor(row).  The XOR only looks at row
+//     bits below ROWS_PER_DMA, so it does not depend on i.  Step: 1 KiB.
+constexpr uint32_t kKDmaStep = 64;
+constexpr uint32_t kVDmaStep = 1024;
 template <int D>
-__device__ __forceinline__ void v_dma_src(int i, int lane, int& row, uint32_t& col)
+__device__ __forceinline__ int k_dma_row(int lane) { return lane & 15; }
+template <int D>
+__device__ __forceinline__ uint32_t k_dma_col(int lane) { return (uint32_t)(lane >> 4) * 16u; }
+template <int D>
+__device__ __forceinline__ int v_dma_row(int lane) { return lane / TileCfg<D>::KCPR; }
+template <int D>
+__device__ __forceinline__ uint32_t v_dma_col(int lane)
 {
-    using C = TileCfg<D>;
-    row = i * C::ROWS_PER_DMA + lane / C::KCPR;
-    col = (((uint32_t)(lane % C::KCPR)) ^ v_row_xor<D>((uint32_t)row)) * 16u;
+    return (((uint32_t)(lane % TileCfg<D>::KCPR)) ^ v_row_xor<D>((uint32_t)(lane / TileCfg<D>::KCPR))) * 16u;
 }
 
 // State of one wave: QB blocks of 32 queries, O^T accumulators, running
@@ -202,6 +200,20 @@ __device__ __forceinline__ bf16x8 v_operand(const char* lds_v, int row, uint32_t
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+// acc *= alpha, register by register in the accumulator's own registers.
+// (Written as a plain vector multiply, the rarely taken rescale branch puts
+// the product in fresh registers, and the common path then pays a copy of the
+// whole accumulator every tile to merge the two.)
+__device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha)
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float x = acc[i];
+        asm("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(alpha));
+        acc[i] = x;
+    }
+}
+
 // One key tile for one wave holding QB blocks of 32 queries.  Every K
 // fragment read from LDS feeds the S^T MFMAs of all QB blocks, and every V^T
 // fragment feeds their O^T MFMAs.
@@ -225,13 +237,12 @@ __device__ __forceinline__ void tile_step(WaveState<D, QB>& ws, const bf16x8 (&q
     for (int kb = 0; kb < C::KBLK; ++kb) {
         // keep each block's K fragment reads next to their MFMAs (hoisting all
         // of them costs registers the loop cannot spare)
-        __builtin_amdgcn_sched_barrier(0);
         f32x16 acc[QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            const bf16x8 a = as_bf16x8(*(const u32x4*)(lds_k + swz(kb * 32 + r32, ks * 2 + g, C::KCPR)));
+            const bf16x8 a = as_bf16x8(*(const u32x4*)(lds_k + k_ofs<D>(kb * 32 + r32, ks * 2 + g)));
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma32(a, qf[qb][ks], acc[qb]);
         }
@@ -274,7 +285,7 @@ __device__ __forceinline__ void tile_step(WaveState<D, QB>& ws, const bf16x8 (&q
             ws.m[qb] = m_new;
             ws.l[qb] *= alpha;
 #pragma unroll
-            for (int db = 0; db < C::DBLK; ++db) ws.o[qb][db] *= alpha;
+            for (int db = 0; db < C::DBLK; ++db) scale_in_place(ws.o[qb][db], alpha);
         }
     }
     // ---- p = exp2(s*c2 - ms), rounded to bf16; l += sum of the rounded p -----
@@ -309,7 +320,6 @@ __device__ __forceinline__ void tile_step(WaveState<D, QB>& ws, const bf16x8 (&q
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            __builtin_amdgcn_sched_barrier(0);
             bf16x8 b[QB];
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb)

@@ -61,48 +61,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const char* base, uin
 
 // Issue this wave's direct copies of one K/V tile (16 rows of each) into an
 // LDS buffer.  Rows at or past kv_end are fetched from row kv_end - 1 (valid
-// data, masked out of S), so no copy reads outside the context.
+// data, masked out of S), so no copy reads outside the context.  For a full
+// group the per-lane source offsets are loop-invariant (k_voff, v_voff) and
+// the group's position goes in the scalar offset.
 template <int D, class KV>
 __device__ __forceinline__ void issue_tile_dma(const KV& kv, char* lds_k, char* lds_v, int key_base, int kv_end,
-                                               int w, int lane)
+                                               int w, int lane, uint32_t k_voff, uint32_t v_voff)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = TileCfg<D>;
     const int gkey = key_base + 16 * w;                 // this wave's first key (uniform)
     const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kv.k_group(gkey, kv_end), kv.group_bytes());
     const __amdgpu_buffer_rsrc_t vr = raw_rsrc(kv.v_group(gkey, kv_end), kv.group_bytes());
-    const int grow = kv.group_row(gkey, kv_end);
-    const bool full = gkey + 16 <= kv_end;
+    char* kdst = lds_k + w * 16 * C::ROW_BYTES;
+    char* vdst = lds_v + w * 16 * C::ROW_BYTES;
+    if (__builtin_expect(gkey + 16 <= kv_end, 1)) {
+        const uint32_t soff = (uint32_t)kv.group_row(gkey, kv_end) * C::ROW_BYTES;
 #pragma unroll
-    for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-        const int r0 = 16 * w + i * C::ROWS_PER_DMA;
-        int krow, vrow;
-        uint32_t kcol, vcol;
-        k_dma_src<D>(w, i, lane, krow, kcol);
-        v_dma_src<D>(i, lane, vrow, vcol);
-        const int kgr = full ? grow + krow : kv.group_row(gkey + krow, kv_end);
-        const int vgr = full ? grow + vrow : kv.group_row(gkey + vrow, kv_end);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, ATTN_LDS(lds_k + r0 * C::ROW_BYTES), 16,
-                                                 (uint32_t)kgr * C::ROW_BYTES + kcol, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, ATTN_LDS(lds_v + r0 * C::ROW_BYTES), 16,
-                                                 (uint32_t)vgr * C::ROW_BYTES + vcol, 0, 0, 0);
+        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, ATTN_LDS(kdst + i * 1024), 16, k_voff + i * kKDmaStep,
+                                                     soff, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, ATTN_LDS(vdst + i * 1024), 16, v_voff + i * kVDmaStep,
+                                                     soff, 0, 0);
+        }
+    } else {
+        const uint32_t koff = (uint32_t)kv.group_row(gkey + k_dma_row<D>(lane), kv_end) * C::ROW_BYTES +
+                              k_dma_col<D>(lane);
+        const uint32_t vcol = v_dma_col<D>(lane);
+#pragma unroll
+        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
+            const int vrow = kv.group_row(gkey + i * C::ROWS_PER_DMA + v_dma_row<D>(lane), kv_end);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, ATTN_LDS(kdst + i * 1024), 16, koff + i * kKDmaStep, 0,
+                                                     0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, ATTN_LDS(vdst + i * 1024), 16,
+                                                     (uint32_t)vrow * C::ROW_BYTES + vcol, 0, 0, 0);
+        }
     }
 #endif
-}
-
-template <int D, int QB>
-__device__ __forceinline__ void run_tile_step(WaveState<D, QB>& ws, const bf16x8 (&qf)[QB][TileCfg<D>::KSTEPS],
-                                              const char* lds_k, const char* lds_v, int lane, float c2, float thr,
-                                              int key_base, const int (&q_lim)[QB], bool active, int w_lim_min,
-                                              int w_lim_max)
-{
-    using C = TileCfg<D>;
-    if (active && key_base < w_lim_max) {
-        if (key_base + C::BN > w_lim_min)
-            tile_step<D, QB, true>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
-        else
-            tile_step<D, QB, false>(ws, qf, lds_k, lds_v, lane, c2, thr, key_base, q_lim);
-    }
 }
 
 // lds0 / lds1: the two LDS buffers (K tile then V tile in each); they must be
@@ -124,14 +119,6 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     // ---- Q^T fragments, per-query key limits ----------------------------------
     bf16x8 qf[QB][C::KSTEPS];
     int q_lim[QB];
-    // bounds over the wave (rows past n_rows are never stored; they use the
-    // last valid row's limit so they never widen the wave's key range)
-    const int last_row = max(P.n_rows - 1, 0);
-    int w_lim_min = P.kv_end, w_lim_max = P.kv_end;
-    if (P.causal) {
-        w_lim_min = min(P.kv_end, P.q_pos0 + min(wrow0, last_row) + 1);
-        w_lim_max = min(P.kv_end, P.q_pos0 + min(wrow0 + 32 * QB - 1, last_row) + 1);
-    }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
         const int qrow = wrow0 + qb * 32 + r32;
@@ -141,11 +128,9 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
             if (qrow < P.n_rows) val = *(const u32x4*)(P.q + qrow * P.q_stride + (ks * 2 + g) * 16);
             qf[qb][ks] = as_bf16x8(val);
         }
-        q_lim[qb] = P.kv_end;
-        if (P.causal) q_lim[qb] = min(q_lim[qb], P.q_pos0 + qrow + 1);
-        if (qrow >= P.n_rows) q_lim[qb] = w_lim_max;
+        // rows past n_rows run on zero queries and are never stored
+        q_lim[qb] = P.causal ? min(P.kv_end, P.q_pos0 + qrow + 1) : P.kv_end;
     }
-    const bool active = wrow0 < P.n_rows;   // waves past the last row only help copy
     // keys the whole tile needs
     int t_end = P.kv_end;
     if (P.causal) t_end = min(P.kv_end, P.q_pos0 + P.n_rows);
@@ -160,6 +145,8 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     }
 
     const float thr = kRescaleLog2 / c2;
+    const uint32_t k_voff = (uint32_t)k_dma_row<D>(lane) * C::ROW_BYTES + k_dma_col<D>(lane);
+    const uint32_t v_voff = (uint32_t)v_dma_row<D>(lane) * C::ROW_BYTES + v_dma_col<D>(lane);
     char* k0 = lds0;
     char* v0 = lds0 + C::TILE_BYTES;
     char* k1 = lds1;
@@ -168,19 +155,47 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     // being consumed; "wait for my copies, then barrier" publishes it.
     const int ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
     if (ntile > 0) {
-        issue_tile_dma<D>(kv, k0, v0, P.kv_begin, P.kv_end, w, lane);
+        issue_tile_dma<D>(kv, k0, v0, P.kv_begin, P.kv_end, w, lane, k_voff, v_voff);
         __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
         __syncthreads();
     }
-    for (int j = 0; j < ntile; j += 2) {
+    // Phase 1: tiles that every row of the tile sees in full (below the
+    // diagonal of query row 0 and before kv_end): no masking and no per-wave
+    // skipping, so the loop body is straight-line apart from the rescale.
+    // Waves past the last valid row compute on zero queries here and never
+    // store.  This keeps O in one register set across the loop (branches
+    // around the tile step make the allocator move O between register sets).
+    int n_full = 0;
+    {
+        const int lim = P.causal ? min(P.kv_end, P.q_pos0 + 1) : P.kv_end;
+        if (lim > P.kv_begin) n_full = min(ntile, (lim - P.kv_begin) / C::BN);
+    }
+    int j = 0;
+    for (; j + 2 <= n_full; j += 2) {
         const int kb0 = P.kv_begin + j * C::BN;
-        if (j + 1 < ntile) issue_tile_dma<D>(kv, k1, v1, kb0 + C::BN, P.kv_end, w, lane);
-        run_tile_step<D, QB>(ws, qf, k0, v0, lane, c2, thr, kb0, q_lim, active, w_lim_min, w_lim_max);
+        issue_tile_dma<D>(kv, k1, v1, kb0 + C::BN, P.kv_end, w, lane, k_voff, v_voff);
+        tile_step<D, QB, false>(ws, qf, k0, v0, lane, c2, thr, kb0, q_lim);
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        __syncthreads();
+        if (j + 2 < ntile) issue_tile_dma<D>(kv, k0, v0, kb0 + 2 * C::BN, P.kv_end, w, lane, k_voff, v_voff);
+        tile_step<D, QB, false>(ws, qf, k1, v1, lane, c2, thr, kb0 + C::BN, q_lim);
+        __builtin_amdgcn_s_waitcnt(0x3f70);
+        __syncthreads();
+    }
+    // Phase 2: the rest (diagonal and tail tiles), always through the masked
+    // step: a tile that is fully masked for a lane adds exactly nothing
+    // (p = 0, and the running offset only moves on a finite score), so waves
+    // whose rows see none of it need no separate skip path.  j is even here,
+    // so tile j is in buffer 0.
+    for (; j < ntile; j += 2) {
+        const int kb0 = P.kv_begin + j * C::BN;
+        if (j + 1 < ntile) issue_tile_dma<D>(kv, k1, v1, kb0 + C::BN, P.kv_end, w, lane, k_voff, v_voff);
+        tile_step<D, QB, true>(ws, qf, k0, v0, lane, c2, thr, kb0, q_lim);
         __builtin_amdgcn_s_waitcnt(0x3f70);
         __syncthreads();
         if (j + 1 < ntile) {
-            if (j + 2 < ntile) issue_tile_dma<D>(kv, k0, v0, kb0 + 2 * C::BN, P.kv_end, w, lane);
-            run_tile_step<D, QB>(ws, qf, k1, v1, lane, c2, thr, kb0 + C::BN, q_lim, active, w_lim_min, w_lim_max);
+            if (j + 2 < ntile) issue_tile_dma<D>(kv, k0, v0, kb0 + 2 * C::BN, P.kv_end, w, lane, k_voff, v_voff);
+            tile_step<D, QB, true>(ws, qf, k1, v1, lane, c2, thr, kb0 + C::BN, q_lim);
             __builtin_amdgcn_s_waitcnt(0x3f70);
             __syncthreads();
         }
