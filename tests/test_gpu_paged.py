@@ -84,20 +84,14 @@ def test_chunk_ragged(bs, d, split):
     check_full(pi, split, "chunk bs%d d%d" % (bs, d))
 
 
-@pytest.mark.parametrize("split", [None, 256])
-def test_chunk_two_query_blocks_per_wave(split):
-    ctx = [300, 1200, 40]
-    ql = [300, 260, 7]
+@pytest.mark.parametrize("split", [64, 128, 192])
+def test_chunk_split_tile_counts(split):
+    """Splits of one, two and three 64-key tiles, with ragged tails: every
+    length of the software-pipelined key loop (one tile, odd and even counts)."""
+    ctx = [300, 1200, 40, 130]
+    ql = [300, 260, 7, 129]
     pi = make(ctx, ql, H=2, bs=32, seed=17)
-    old = os.environ.get("ATTN_CHUNK_QB")
-    os.environ["ATTN_CHUNK_QB"] = "2"
-    try:
-        check_full(pi, split, "chunk qb2")
-    finally:
-        if old is None:
-            os.environ.pop("ATTN_CHUNK_QB", None)
-        else:
-            os.environ["ATTN_CHUNK_QB"] = old
+    check_full(pi, split, "chunk split%d" % split)
 
 
 def test_chunk_mixed_with_decode_rows():

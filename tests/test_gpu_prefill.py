@@ -34,12 +34,11 @@ class env_set:
                 os.environ[k] = v
 
 
-def run_case(B, H, N, d, dtype, causal, seed, pair=None, qb=None):
+def run_case(B, H, N, d, dtype, causal, seed, pair=None):
     cfg = inputs.PrefillConfig("case", B, H, N, d, dtype, causal, seed)
-    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s qb=%s" % (B, H, N, d, dtype, causal, seed,
-                                                                                   pair, qb))
+    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s" % (B, H, N, d, dtype, causal, seed, pair))
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair), ATTN_PREFILL_QB=qb):
+    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair)):
         o, lse = attn.prefill(q, k, v, causal, cfg.scale)
         torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, cfg.scale, causal)
@@ -79,9 +78,13 @@ def test_pair_mode_matches_oracle(pair):
     run_case(2, 4, 1000, 128, torch.bfloat16, True, 7, pair=pair)
 
 
-@pytest.mark.parametrize("N,d,causal", [(1, 128, True), (300, 128, True), (700, 128, False), (513, 64, True)])
-def test_two_query_blocks_per_wave(N, d, causal):
-    run_case(1, 3, N, d, torch.bfloat16, causal, 400 + N, qb=2)
+@pytest.mark.parametrize("N", [64, 65, 128, 192, 256, 320, 384])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_tile_counts(N, d, causal):
+    """One to six 64-key tiles per query tile: odd and even tile counts and
+    the boundary between unmasked and masked tiles of the pipelined loop."""
+    run_case(1, 2, N, d, torch.bfloat16, causal, 400 + N + d)
 
 
 def test_deterministic_and_pair_independent():

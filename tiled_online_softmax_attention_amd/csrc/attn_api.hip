@@ -80,21 +80,14 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
-    // bf16 query tiles: 128 rows (one 32-query block per wave, two workgroups
-    // per CU).  256-row tiles (two blocks per wave sharing every LDS fragment,
-    // one workgroup per CU) are opt-in with ATTN_PREFILL_QB=2: they halve LDS
-    // reads per MFMA but need the whole register file and measured slower.
+    // bf16 query tiles: 128 rows (32 queries per wave, two workgroups per CU).
     // Pairing tiles t and n-1-t (equal work per workgroup) is opt-in for
-    // causal 128-row launches with ATTN_PREFILL_PAIR=1.
+    // causal launches with ATTN_PREFILL_PAIR=1.
     {
-        int qb = 1;
-        const char* env_qb = getenv("ATTN_PREFILL_QB");
-        if (env_qb && *env_qb) qb = (atoi(env_qb) == 2) ? 2 : 1;
         int pair = 0;
         const char* env = getenv("ATTN_PREFILL_PAIR");
         if (env && *env) pair = atoi(env) ? 1 : 0;
-        if (!a.causal || qb != 1 || N <= 128) pair = 0;
-        a.qb = qb;
+        if (!a.causal || N <= 128) pair = 0;
         a.pair = pair;
     }
     rc = attn::launch_prefill(a, (hipStream_t)stream);

@@ -20,7 +20,6 @@ struct PrefillArgs {
     int causal;
     int dtype;      // 0 bf16, 1 fp32
     int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t (qb == 1 only)
-    int qb;         // bf16: 32-query blocks per wave (1: 128-row tiles, 2: 256-row tiles)
     int n_work;     // filled by the launcher
 };
 
@@ -30,7 +29,6 @@ struct PagedPlan {
     int split_tokens;    // keys per context split (multiple of the page size)
     int max_splits;      // ceil(max_ctx_len / split_tokens)
     int nqt;             // query tiles per request (chunk path)
-    int qb;              // chunk path: 32-query blocks per wave (tile = 128 * qb rows)
     size_t ws_o_bytes;   // fp32 partial outputs
     size_t ws_lse_bytes; // fp32 partial log-sum-exps
     size_t ws_bytes;     // total (0 when max_splits == 1)

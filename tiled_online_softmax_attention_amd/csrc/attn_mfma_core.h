@@ -8,7 +8,7 @@
 // l = exp(m - m_new) l + sum p, O = exp(m - m_new) O + p V, and O / l once at
 // the end.  Here it is laid out for 64-wide wavefronts and 32x32x16 bf16 MFMA:
 //
-//  * Each wave owns QB blocks of 32 query rows.  It computes S^T = K Q^T, so
+//  * Each wave owns 32 query rows.  It computes S^T = K Q^T, so
 //    the MFMA accumulator puts one query per lane (lane % 32) and that query's
 //    keys down the 16 accumulator registers: the running offset, sum and the
 //    rescale factor are per-lane scalars, and the two lane halves (lane / 32)
@@ -103,23 +103,26 @@ __device__ __forceinline__ bf16x8 cat8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d)
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Tile geometry: 4 waves, 64-key tiles; each wave copies 16 rows of K and of
-// V per tile.
+// Tile geometry: 4 waves, 32-key tiles of two 16-row groups.  Per tile, waves
+// 0 and 1 copy the two K groups and waves 2 and 3 the two V groups.  Short
+// tiles keep the per-wave registers low enough for three workgroups per CU
+// (12 waves), which hides more of the latency of each wave's dependent chain
+// (S MFMAs -> max -> exp -> PV MFMAs) than longer tiles at two per CU.
 template <int D>
 struct TileCfg {
     static constexpr int kWaves = 4;
     static constexpr int kThreads = 64 * kWaves;
-    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int BN = 32;                   // keys per tile
     static constexpr int KCPR = D / 8;              // 16-byte chunks per row
     static constexpr int KSTEPS = D / 16;           // MFMA k-steps for Q K^T
     static constexpr int DBLK = D / 32;             // 32-wide d blocks of O^T
     static constexpr int KBLK = BN / 32;            // 32-key blocks of S^T
     static constexpr int ROW_BYTES = D * 2;
     static constexpr int TILE_BYTES = BN * ROW_BYTES;          // one of K or V
+    static constexpr int GROUPS = BN / 16;                     // 16-row groups per tile
     static constexpr int ROWS_PER_DMA = 1024 / ROW_BYTES;      // rows per wave-wide 16 B/lane copy
-    static constexpr int DMA_PER_WAVE = 16 / ROWS_PER_DMA;     // copies per wave per tile (each of K, V)
-    static constexpr int BUF_BYTES = 2 * TILE_BYTES;           // K + V of one tile
-    static_assert(BN == 16 * kWaves, "each wave copies 16 rows");
+    static constexpr int COPIES_PER_GROUP = 16 / ROWS_PER_DMA;
+    static_assert(kWaves == 2 * GROUPS, "one wave per 16-row group of K or V");
 };
 
 // XOR applied to the 16-byte chunk index of V row `row`: 4 consecutive rows
@@ -170,13 +173,20 @@ __device__ __forceinline__ uint32_t v_dma_col(int lane)
     return (((uint32_t)(lane % TileCfg<D>::KCPR)) ^ v_row_xor<D>((uint32_t)(lane / TileCfg<D>::KCPR))) * 16u;
 }
 
-// State of one wave: QB blocks of 32 queries, O^T accumulators, running
-// offsets and sums (one per lane and query block).
-template <int D, int QB>
+// State of one wave: 32 queries (one per lane % 32), O^T accumulators, the
+// running offset and the running sum.
+template <int D>
 struct WaveState {
-    f32x16 o[QB][TileCfg<D>::DBLK];
-    float m[QB];  // offset of this lane's query, raw score units (-inf: none yet)
-    float l[QB];  // running sum of this lane-half's rounded probabilities
+    f32x16 o[TileCfg<D>::DBLK];
+    float m;  // offset of this lane's query, raw score units (-inf: none yet)
+    float l;  // running sum of this lane-half's rounded probabilities
+};
+
+// Scores of one key tile: S^T blocks of 32 keys (accumulator register i of
+// block kb holds key kb*32 + (i/4)*8 + (lane/32)*4 + i%4 of the tile).
+template <int D>
+struct TileScores {
+    f32x16 s[TileCfg<D>::KBLK];
 };
 
 // Exponent headroom of the lazy rescale: the offset m only moves when a
@@ -214,122 +224,124 @@ __device__ __forceinline__ void scale_in_place(f32x16& acc, float alpha)
     }
 }
 
-// One key tile for one wave holding QB blocks of 32 queries.  Every K
-// fragment read from LDS feeds the S^T MFMAs of all QB blocks, and every V^T
-// fragment feeds their O^T MFMAs.
-//  qf      : Q^T operand fragments per block (bf16x8 per 16-wide d step)
-//  c2      : scale * log2(e) (> 0);  thr = kRescaleLog2 / c2 in raw score units
-//  key0    : absolute key index of tile row 0
-//  q_lim   : per block, this lane's query sees keys < q_lim
-//  MASKED  : whether any key of this tile may be masked for a lane of the wave
-//  (c2 > 0 always: a zero scale is passed as a tiny positive c2, which gives
-//  the same p = 1 for every allowed key and keeps exp2(-inf) = 0 for masked ones)
-template <int D, int QB, bool MASKED>
-__device__ __forceinline__ void tile_step(WaveState<D, QB>& ws, const bf16x8 (&qf)[QB][TileCfg<D>::KSTEPS],
-                                          const char* lds_k, const char* lds_v, int lane, float c2, float thr,
-                                          int key0, const int (&q_lim)[QB])
+// The tile step of the block-wise forward, in stages: S MFMAs, mask and
+// maximum, lazy offset update, exponentials, PV MFMAs.
+
+// S^T = K Q^T for one key tile.  All K fragments of a 32-key block are read
+// first, so the LDS latency is paid once per block rather than per MFMA.
+template <int D>
+__device__ __forceinline__ void qk_tile(TileScores<D>& S, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const char* lds_k,
+                                        int lane)
 {
     using C = TileCfg<D>;
     const int g = lane >> 5, r32 = lane & 31;
-    // ---- S^T = K Q^T --------------------------------------------------------
-    f32x16 s[QB][C::KBLK];
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb) {
-        // keep each block's K fragment reads next to their MFMAs (hoisting all
-        // of them costs registers the loop cannot spare)
-        f32x16 acc[QB];
+        bf16x8 kf[C::KSTEPS];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) acc[qb] = f32x16{};
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
+            kf[ks] = as_bf16x8(*(const u32x4*)(lds_k + k_ofs<D>(kb * 32 + r32, ks * 2 + g)));
+        f32x16 acc = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            const bf16x8 a = as_bf16x8(*(const u32x4*)(lds_k + k_ofs<D>(kb * 32 + r32, ks * 2 + g)));
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) acc[qb] = mfma32(a, qf[qb][ks], acc[qb]);
-        }
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = acc[qb];
+        for (int ks = 0; ks < C::KSTEPS; ++ks) acc = mfma32(kf[ks], qf[ks], acc);
+        S.s[kb] = acc;
     }
-    // ---- mask (diagonal / tail tiles only) and tile maximum -----------------
-    // key of accumulator register i of block kb: key0 + kb*32 + (i/4)*8 + g*4 + i%4
+}
+
+// Mask (MASKED: keys >= q_lim become -inf) and the tile maximum of this
+// lane's query over both lane halves.
+//  key0  : absolute key index of tile row 0
+//  q_lim : this lane's query sees keys < q_lim
+template <int D, bool MASKED>
+__device__ __forceinline__ float tile_max(TileScores<D>& S, int lane, int key0, int q_lim)
+{
+    using C = TileCfg<D>;
+    const int g = lane >> 5;
     if (MASKED) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const int lim_rel = q_lim[qb] - key0 - g * 4;
-#pragma unroll
-            for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
-                    s[qb][kb][i] = (off < lim_rel) ? s[qb][kb][i] : -INFINITY;
-                }
-        }
-    }
-    float mt[QB];
-    bool need = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        float x = -INFINITY;
+        const int lim_rel = q_lim - key0 - g * 4;
 #pragma unroll
         for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) x = fmaxf(x, fmaxf(s[qb][kb][i], s[qb][kb][i + 1]));
-        mt[qb] = half_max(x);
-        need = need || (mt[qb] > ws.m[qb] + thr);
-    }
-    // ---- lazy offset update (wave-uniform decision) --------------------------
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            const float m_new = fmaxf(ws.m[qb], mt[qb]);
-            const float alpha = (ws.m[qb] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ws.m[qb] - m_new) * c2);
-            ws.m[qb] = m_new;
-            ws.l[qb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::DBLK; ++db) scale_in_place(ws.o[qb][db], alpha);
-        }
-    }
-    // ---- p = exp2(s*c2 - ms), rounded to bf16; l += sum of the rounded p -----
-    bf16x2 pk[QB][C::KBLK][8];
-    const bf16x2 ones = pack2(1.f, 1.f);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float ms = (ws.m[qb] == -INFINITY) ? 0.f : ws.m[qb] * c2;
-        float ps0 = 0.f, ps1 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < C::KBLK; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const float t0 = __builtin_fmaf(s[qb][kb][i], c2, -ms);
-                const float t1 = __builtin_fmaf(s[qb][kb][i + 1], c2, -ms);
-                const bf16x2 w = pack2(__builtin_amdgcn_exp2f(t0), __builtin_amdgcn_exp2f(t1));
-                pk[qb][kb][i >> 1] = w;
-                if ((i >> 1) & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps1, false);
-                else ps0 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps0, false);
+            for (int i = 0; i < 16; ++i) {
+                const int off = kb * 32 + (i >> 2) * 8 + (i & 3);
+                S.s[kb][i] = (off < lim_rel) ? S.s[kb][i] : -INFINITY;
             }
-        ws.l[qb] += ps0 + ps1;
     }
-    // ---- O^T += V^T P^T ------------------------------------------------------
-    // Lane (16-lane group G = lane/16, i = lane%16) addresses V row
-    // k0 + i/4 and the 4 channels d0 + 4*(i%4), d0 = db*32 + (G%2)*16, with
-    // k0 = kb*32 + 16h + 4g (+8 for the second read); the transposing read
-    // hands it keys k0..k0+3 of channel d0 + i -- the keys its P^T registers
-    // 8h..8h+7 hold.
+    float x = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) x = fmaxf(x, fmaxf(S.s[kb][i], S.s[kb][i + 1]));
+    return half_max(x);
+}
+
+// Lazy offset update (wave-uniform decision): when some query's tile maximum
+// mt exceeds its offset by more than the headroom, move the offsets and
+// rescale O and l by exp2((m_old - m_new) * c2).
+//  c2  : scale * log2(e) (> 0);  thr = kRescaleLog2 / c2 in raw score units
+template <int D>
+__device__ __forceinline__ void update_offset(WaveState<D>& ws, float mt, float c2, float thr)
+{
+    using C = TileCfg<D>;
+    if (__builtin_amdgcn_ballot_w64(mt > ws.m + thr) != 0) {
+        const float m_new = fmaxf(ws.m, mt);
+        const float alpha = (ws.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ws.m - m_new) * c2);
+        ws.m = m_new;
+        ws.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) scale_in_place(ws.o[db], alpha);
+    }
+}
+
+// p = exp2(s*c2 - m*c2) rounded to bf16 (packed in pairs, the P^T operand
+// layout); l += the sum of the rounded p.  (c2 > 0 always: a zero scale is
+// passed as a tiny positive c2, which gives the same p = 1 for every allowed
+// key and keeps exp2(-inf) = 0 for masked ones.)
+template <int D>
+__device__ __forceinline__ void exp_tile(bf16x2 (&pk)[TileCfg<D>::KBLK][8], const TileScores<D>& S, WaveState<D>& ws,
+                                         float c2)
+{
+    using C = TileCfg<D>;
+    const bf16x2 ones = pack2(1.f, 1.f);
+    const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * c2;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < C::KBLK; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            const float t0 = __builtin_fmaf(S.s[kb][i], c2, -ms);
+            const float t1 = __builtin_fmaf(S.s[kb][i + 1], c2, -ms);
+            const bf16x2 w = pack2(__builtin_amdgcn_exp2f(t0), __builtin_amdgcn_exp2f(t1));
+            pk[kb][i >> 1] = w;
+            if ((i >> 1) & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps1, false);
+            else ps0 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps0, false);
+        }
+    ws.l += ps0 + ps1;
+}
+
+// O^T += V^T P^T for one key tile.
+// Lane (16-lane group G = lane/16, i = lane%16) addresses V row k0 + i/4 and
+// the 4 channels d0 + 4*(i%4), d0 = db*32 + (G%2)*16, with
+// k0 = kb*32 + 16h + 4g (+8 for the second read); the transposing read hands
+// it keys k0..k0+3 of channel d0 + i -- the keys its P^T registers
+// 8h..8h+7 hold.
+template <int D>
+__device__ __forceinline__ void pv_tile(WaveState<D>& ws, const bf16x2 (&pk)[TileCfg<D>::KBLK][8], const char* lds_v,
+                                        int lane)
+{
+    using C = TileCfg<D>;
+    const int g = lane >> 5;
     const int tr_row = g * 4 + ((lane & 15) >> 2);
     const uint32_t tr_col = (uint32_t)((((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2);
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            bf16x8 b[QB];
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-                b[qb] = cat8(pk[qb][kb][4 * h + 0], pk[qb][kb][4 * h + 1], pk[qb][kb][4 * h + 2],
-                             pk[qb][kb][4 * h + 3]);
+            const bf16x8 b = cat8(pk[kb][4 * h + 0], pk[kb][4 * h + 1], pk[kb][4 * h + 2], pk[kb][4 * h + 3]);
 #pragma unroll
             for (int db = 0; db < C::DBLK; ++db) {
                 const bf16x8 a = v_operand<D>(lds_v, kb * 32 + 16 * h + tr_row, tr_col + db * 64);
-#pragma unroll
-                for (int qb = 0; qb < QB; ++qb) ws.o[qb][db] = mfma32(a, b[qb], ws.o[qb][db]);
+                ws.o[db] = mfma32(a, b, ws.o[db]);
             }
         }
 }

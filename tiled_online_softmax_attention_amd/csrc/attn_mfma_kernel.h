@@ -1,5 +1,5 @@
 // attn_mfma_kernel.h -- the per-workgroup driver of the bf16 MFMA attention
-// forward: loads the query tile into registers, streams 64-key K/V tiles into
+// forward: loads the query tile into registers, streams 32-key K/V tiles into
 // LDS with direct global->LDS copies issued one tile ahead (two LDS buffers,
 // one barrier per tile), runs the online-softmax tile step of
 // attn_mfma_core.h, and writes O (bf16, or fp32 partials) and the
@@ -43,10 +43,15 @@ struct TileOut {
     int fp32_out;        // 1: write fp32 normalised O (partials), 0: bf16
 };
 
-// Query rows per workgroup: 4 waves x QB blocks of 32 queries.
-template <int QB>
-struct QueryTile {
-    static constexpr int BM = 4 * 32 * QB;
+// Query rows per workgroup: 4 waves x 32 queries.
+constexpr int kTileRows = 128;
+
+// LDS of one workgroup: two buffers, each holding one K tile then one V tile.
+// They are distinct __shared__ objects, so reads of one are not ordered
+// behind copies in flight into the other.
+struct TileBuffers {
+    char* b0;
+    char* b1;
 };
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -59,184 +64,193 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const char* base, uin
 }
 #endif
 
-// Issue this wave's direct copies of one K/V tile (16 rows of each) into an
-// LDS buffer.  Rows at or past kv_end are fetched from row kv_end - 1 (valid
+// Wave-level constants of one query tile.
+struct WaveCtx {
+    int lane, w;
+    float c2, thr;
+    int q_lim;           // this lane's query sees keys < q_lim
+    int kv_begin, kv_end, ntile;
+    uint32_t voff;       // this lane's copy source offset within a full group
+};
+
+// Issue this wave's copies of one tile into buffer `buf` (K tile at byte 0, V
+// tile at TILE_BYTES): wave w < GROUPS copies K group w, the others V group
+// w - GROUPS.  Rows at or past kv_end are fetched from row kv_end - 1 (valid
 // data, masked out of S), so no copy reads outside the context.  For a full
-// group the per-lane source offsets are loop-invariant (k_voff, v_voff) and
-// the group's position goes in the scalar offset.
+// group the per-lane source offset is loop-invariant (cx.voff) and the
+// group's position goes in the scalar offset.
 template <int D, class KV>
-__device__ __forceinline__ void issue_tile_dma(const KV& kv, char* lds_k, char* lds_v, int key_base, int kv_end,
-                                               int w, int lane, uint32_t k_voff, uint32_t v_voff)
+__device__ __forceinline__ void issue_tile_copies(const KV& kv, const WaveCtx& cx, char* buf, int key_base)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
     using C = TileCfg<D>;
-    const int gkey = key_base + 16 * w;                 // this wave's first key (uniform)
-    const __amdgpu_buffer_rsrc_t kr = raw_rsrc(kv.k_group(gkey, kv_end), kv.group_bytes());
-    const __amdgpu_buffer_rsrc_t vr = raw_rsrc(kv.v_group(gkey, kv_end), kv.group_bytes());
-    char* kdst = lds_k + w * 16 * C::ROW_BYTES;
-    char* vdst = lds_v + w * 16 * C::ROW_BYTES;
+    const bool is_v = cx.w >= C::GROUPS;                      // uniform
+    const int grp = is_v ? cx.w - C::GROUPS : cx.w;
+    const int kv_end = cx.kv_end;
+    const int gkey = key_base + 16 * grp;                     // first key of the group (uniform)
+    const __amdgpu_buffer_rsrc_t r =
+        raw_rsrc(is_v ? kv.v_group(gkey, kv_end) : kv.k_group(gkey, kv_end), kv.group_bytes());
+    char* dst = buf + (is_v ? C::TILE_BYTES : 0) + grp * 16 * C::ROW_BYTES;
     if (__builtin_expect(gkey + 16 <= kv_end, 1)) {
         const uint32_t soff = (uint32_t)kv.group_row(gkey, kv_end) * C::ROW_BYTES;
+        const uint32_t step = is_v ? kVDmaStep : kKDmaStep;
 #pragma unroll
-        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, ATTN_LDS(kdst + i * 1024), 16, k_voff + i * kKDmaStep,
-                                                     soff, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, ATTN_LDS(vdst + i * 1024), 16, v_voff + i * kVDmaStep,
-                                                     soff, 0, 0);
-        }
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16, cx.voff + i * step, soff, 0,
+                                                     0);
+    } else if (!is_v) {
+        const uint32_t koff = (uint32_t)kv.group_row(gkey + k_dma_row<D>(cx.lane), kv_end) * C::ROW_BYTES +
+                              k_dma_col<D>(cx.lane);
+#pragma unroll
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16, koff + i * kKDmaStep, 0, 0, 0);
     } else {
-        const uint32_t koff = (uint32_t)kv.group_row(gkey + k_dma_row<D>(lane), kv_end) * C::ROW_BYTES +
-                              k_dma_col<D>(lane);
-        const uint32_t vcol = v_dma_col<D>(lane);
+        const uint32_t vcol = v_dma_col<D>(cx.lane);
 #pragma unroll
-        for (int i = 0; i < C::DMA_PER_WAVE; ++i) {
-            const int vrow = kv.group_row(gkey + i * C::ROWS_PER_DMA + v_dma_row<D>(lane), kv_end);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, ATTN_LDS(kdst + i * 1024), 16, koff + i * kKDmaStep, 0,
-                                                     0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, ATTN_LDS(vdst + i * 1024), 16,
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i) {
+            const int vrow = kv.group_row(gkey + i * C::ROWS_PER_DMA + v_dma_row<D>(cx.lane), kv_end);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16,
                                                      (uint32_t)vrow * C::ROW_BYTES + vcol, 0, 0, 0);
         }
     }
 #endif
 }
 
-// lds0 / lds1: the two LDS buffers (K tile then V tile in each); they must be
-// distinct __shared__ objects so that reads of one are not ordered behind
-// copies still in flight into the other.
-template <int D, int QB, class KV>
-__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
-                                               char* lds0, char* lds1)
+__device__ __forceinline__ void publish_copies()
 {
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
+    __syncthreads();
+}
+
+// One key tile (K at buf, V at buf + TILE_BYTES) for this wave's 32 queries.
+template <int D, bool MASKED>
+__device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
+                                          const char* buf, int key0)
+{
+    using C = TileCfg<D>;
+    TileScores<D> S;
+    qk_tile(S, qf, buf, cx.lane);
+    const float mt = tile_max<D, MASKED>(S, cx.lane, key0, cx.q_lim);
+    update_offset(ws, mt, cx.c2, cx.thr);
+    bf16x2 pk[C::KBLK][8];
+    exp_tile(pk, S, ws, cx.c2);
+    pv_tile(ws, pk, buf + C::TILE_BYTES, cx.lane);
+}
+
+template <int D, class KV>
+__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
+                                               const TileBuffers& buf)
+{
+    using C = TileCfg<D>;
+    WaveCtx cx;
     // scale * log2(e); a zero scale becomes a tiny positive factor (every
     // allowed key still gets p = 2^0 = 1 exactly, masked keys 2^-inf = 0)
-    const float c2 = fmaxf(c2_in, 1e-30f);
-    using C = TileCfg<D>;
+    cx.c2 = fmaxf(c2_in, 1e-30f);
+    cx.thr = kRescaleLog2 / cx.c2;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, g = lane >> 5, r32 = lane & 31;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wrow0 = w * 32 * QB;            // first query row of this wave
+    cx.lane = tid & 63;
+    const int g = cx.lane >> 5, r32 = cx.lane & 31;
+    cx.w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qrow = cx.w * 32 + r32;        // this lane's query row in the tile
 
-    // ---- Q^T fragments, per-query key limits ----------------------------------
-    bf16x8 qf[QB][C::KSTEPS];
-    int q_lim[QB];
+    // ---- Q^T fragments, key limit ---------------------------------------------
+    bf16x8 qf[C::KSTEPS];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wrow0 + qb * 32 + r32;
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (qrow < P.n_rows) val = *(const u32x4*)(P.q + qrow * P.q_stride + (ks * 2 + g) * 16);
-            qf[qb][ks] = as_bf16x8(val);
-        }
-        // rows past n_rows run on zero queries and are never stored
-        q_lim[qb] = P.causal ? min(P.kv_end, P.q_pos0 + qrow + 1) : P.kv_end;
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (qrow < P.n_rows) val = *(const u32x4*)(P.q + qrow * P.q_stride + (ks * 2 + g) * 16);
+        qf[ks] = as_bf16x8(val);
     }
+    // rows past n_rows run on zero queries and are never stored
+    cx.q_lim = P.causal ? min(P.kv_end, P.q_pos0 + qrow + 1) : P.kv_end;
     // keys the whole tile needs
-    int t_end = P.kv_end;
-    if (P.causal) t_end = min(P.kv_end, P.q_pos0 + P.n_rows);
+    const int t_end = P.causal ? min(P.kv_end, P.q_pos0 + P.n_rows) : P.kv_end;
+    cx.kv_begin = P.kv_begin;
+    cx.kv_end = P.kv_end;
+    cx.ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
+    cx.voff = (cx.w >= C::GROUPS)
+                  ? (uint32_t)v_dma_row<D>(cx.lane) * C::ROW_BYTES + v_dma_col<D>(cx.lane)
+                  : (uint32_t)k_dma_row<D>(cx.lane) * C::ROW_BYTES + k_dma_col<D>(cx.lane);
 
-    WaveState<D, QB> ws;
+    WaveState<D> ws;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) ws.o[qb][db] = f32x16{};
-        ws.m[qb] = -INFINITY;
-        ws.l[qb] = 0.f;
-    }
+    for (int db = 0; db < C::DBLK; ++db) ws.o[db] = f32x16{};
+    ws.m = -INFINITY;
+    ws.l = 0.f;
 
-    const float thr = kRescaleLog2 / c2;
-    const uint32_t k_voff = (uint32_t)k_dma_row<D>(lane) * C::ROW_BYTES + k_dma_col<D>(lane);
-    const uint32_t v_voff = (uint32_t)v_dma_row<D>(lane) * C::ROW_BYTES + v_dma_col<D>(lane);
-    char* k0 = lds0;
-    char* v0 = lds0 + C::TILE_BYTES;
-    char* k1 = lds1;
-    char* v1 = lds1 + C::TILE_BYTES;
-    // Tile j lives in buffer j % 2.  Its copies are issued while tile j - 1 is
-    // being consumed; "wait for my copies, then barrier" publishes it.
-    const int ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
-    if (ntile > 0) {
-        issue_tile_dma<D>(kv, k0, v0, P.kv_begin, P.kv_end, w, lane, k_voff, v_voff);
-        __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
-        __syncthreads();
-    }
-    // Phase 1: tiles that every row of the tile sees in full (below the
-    // diagonal of query row 0 and before kv_end): no masking and no per-wave
-    // skipping, so the loop body is straight-line apart from the rescale.
-    // Waves past the last valid row compute on zero queries here and never
-    // store.  This keeps O in one register set across the loop (branches
-    // around the tile step make the allocator move O between register sets).
+    // Tiles [0, n_full) are seen in full by every row of the tile (below the
+    // diagonal of query row 0 and before kv_end): no masking.  The rest
+    // (diagonal and tail) go through the masked step, for every wave: a tile
+    // fully masked for a lane adds exactly nothing (p = 0, and the offset
+    // only moves on a finite score), and waves past the last valid row run on
+    // zero queries and never store.  Keeping the per-tile code free of
+    // per-wave branches also keeps O in one register set across the loop.
     int n_full = 0;
     {
         const int lim = P.causal ? min(P.kv_end, P.q_pos0 + 1) : P.kv_end;
-        if (lim > P.kv_begin) n_full = min(ntile, (lim - P.kv_begin) / C::BN);
+        if (lim > P.kv_begin) n_full = min(cx.ntile, (lim - P.kv_begin) / C::BN);
+    }
+    // Tile j lives in buffer j % 2.  Its copies are issued while tile j - 1 is
+    // being consumed; "wait for my copies, then barrier" publishes it.
+    if (cx.ntile > 0) {
+        issue_tile_copies<D>(kv, cx, buf.b0, cx.kv_begin);
+        publish_copies();
     }
     int j = 0;
     for (; j + 2 <= n_full; j += 2) {
-        const int kb0 = P.kv_begin + j * C::BN;
-        issue_tile_dma<D>(kv, k1, v1, kb0 + C::BN, P.kv_end, w, lane, k_voff, v_voff);
-        tile_step<D, QB, false>(ws, qf, k0, v0, lane, c2, thr, kb0, q_lim);
-        __builtin_amdgcn_s_waitcnt(0x3f70);
-        __syncthreads();
-        if (j + 2 < ntile) issue_tile_dma<D>(kv, k0, v0, kb0 + 2 * C::BN, P.kv_end, w, lane, k_voff, v_voff);
-        tile_step<D, QB, false>(ws, qf, k1, v1, lane, c2, thr, kb0 + C::BN, q_lim);
-        __builtin_amdgcn_s_waitcnt(0x3f70);
-        __syncthreads();
+        const int kb0 = cx.kv_begin + j * C::BN;
+        issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        tile_step<D, false>(ws, qf, cx, buf.b0, kb0);
+        publish_copies();
+        if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+        tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN);
+        publish_copies();
     }
-    // Phase 2: the rest (diagonal and tail tiles), always through the masked
-    // step: a tile that is fully masked for a lane adds exactly nothing
-    // (p = 0, and the running offset only moves on a finite score), so waves
-    // whose rows see none of it need no separate skip path.  j is even here,
-    // so tile j is in buffer 0.
-    for (; j < ntile; j += 2) {
-        const int kb0 = P.kv_begin + j * C::BN;
-        if (j + 1 < ntile) issue_tile_dma<D>(kv, k1, v1, kb0 + C::BN, P.kv_end, w, lane, k_voff, v_voff);
-        tile_step<D, QB, true>(ws, qf, k0, v0, lane, c2, thr, kb0, q_lim);
-        __builtin_amdgcn_s_waitcnt(0x3f70);
-        __syncthreads();
-        if (j + 1 < ntile) {
-            if (j + 2 < ntile) issue_tile_dma<D>(kv, k0, v0, kb0 + 2 * C::BN, P.kv_end, w, lane, k_voff, v_voff);
-            tile_step<D, QB, true>(ws, qf, k1, v1, lane, c2, thr, kb0 + C::BN, q_lim);
-            __builtin_amdgcn_s_waitcnt(0x3f70);
-            __syncthreads();
+    // j is even here, so tile j is in buffer 0
+    for (; j < cx.ntile; j += 2) {
+        const int kb0 = cx.kv_begin + j * C::BN;
+        if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        tile_step<D, true>(ws, qf, cx, buf.b0, kb0);
+        publish_copies();
+        if (j + 1 < cx.ntile) {
+            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+            tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN);
+            publish_copies();
         }
     }
 
     // ---- epilogue -------------------------------------------------------------
+    const float l_tot = half_sum(ws.l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < P.n_rows) {
+        if (out.fp32_out) {
+            float* orow = (float*)(out.o + qrow * out.o_stride);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = wrow0 + qb * 32 + r32;
-        const float l_tot = half_sum(ws.l[qb]);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (qrow < P.n_rows) {
-            if (out.fp32_out) {
-                float* orow = (float*)(out.o + qrow * out.o_stride);
+            for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
-                for (int db = 0; db < C::DBLK; ++db)
+                for (int a = 0; a < 4; ++a) {
+                    f32x4 v4;
+                    v4[0] = ws.o[db][a * 4 + 0] * inv;
+                    v4[1] = ws.o[db][a * 4 + 1] * inv;
+                    v4[2] = ws.o[db][a * 4 + 2] * inv;
+                    v4[3] = ws.o[db][a * 4 + 3] * inv;
+                    *(f32x4*)(orow + db * 32 + a * 8 + g * 4) = v4;
+                }
+        } else {
+            char* orow = out.o + qrow * out.o_stride;
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        f32x4 v4;
-                        v4[0] = ws.o[qb][db][a * 4 + 0] * inv;
-                        v4[1] = ws.o[qb][db][a * 4 + 1] * inv;
-                        v4[2] = ws.o[qb][db][a * 4 + 2] * inv;
-                        v4[3] = ws.o[qb][db][a * 4 + 3] * inv;
-                        *(f32x4*)(orow + db * 32 + a * 8 + g * 4) = v4;
-                    }
-            } else {
-                char* orow = out.o + qrow * out.o_stride;
+            for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
-                for (int db = 0; db < C::DBLK; ++db)
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        u32x2 w2;
-                        w2[0] = pack_bf16(ws.o[qb][db][a * 4 + 0] * inv, ws.o[qb][db][a * 4 + 1] * inv);
-                        w2[1] = pack_bf16(ws.o[qb][db][a * 4 + 2] * inv, ws.o[qb][db][a * 4 + 3] * inv);
-                        *(u32x2*)(orow + (db * 32 + a * 8 + g * 4) * 2) = w2;
-                    }
-            }
-            if (out.lse && g == 0) {
-                const float ms = (ws.m[qb] == -INFINITY) ? 0.f : ws.m[qb] * c2;
-                out.lse[qrow * out.lse_stride] = (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
-            }
+                for (int a = 0; a < 4; ++a) {
+                    u32x2 w2;
+                    w2[0] = pack_bf16(ws.o[db][a * 4 + 0] * inv, ws.o[db][a * 4 + 1] * inv);
+                    w2[1] = pack_bf16(ws.o[db][a * 4 + 2] * inv, ws.o[db][a * 4 + 3] * inv);
+                    *(u32x2*)(orow + (db * 32 + a * 8 + g * 4) * 2) = w2;
+                }
+        }
+        if (out.lse && g == 0) {
+            const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * cx.c2;
+            out.lse[qrow * out.lse_stride] = (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }

@@ -284,13 +284,14 @@ struct PagedKV {
     __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
 };
 
-template <int D, int BS, int QB>
-__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void paged_chunk_kernel(PagedArgs a, int n_work)
+template <int D, int BS>
+__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work)
 {
     using C = TileCfg<D>;
-    constexpr int BM = QueryTile<QB>::BM;
-    __shared__ __attribute__((aligned(16))) char lds0[C::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[C::BUF_BYTES];
+    constexpr int BM = kTileRows;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    const TileBuffers buf{lds0, lds1};
     const int per = gridDim.x >> 3;
     int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (L >= n_work) return;
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void paged_chunk_kernel(Paged
         out.lse_stride = (int64_t)a.H * a.max_splits;
         out.fp32_out = 1;
     }
-    run_query_tile<D, QB>(P, kv, out, a.scale * kLog2e, lds0, lds1);
+    run_query_tile<D>(P, kv, out, a.scale * kLog2e, buf);
 }
 
 // ============================================================================
@@ -438,12 +439,7 @@ PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, 
         while (S > 4 * block_size && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         p.nqt = 1;
     } else {
-        // 128-row query tiles; 256-row tiles (two 32-query blocks per wave) are
-        // opt-in with ATTN_CHUNK_QB=2 (they measured slower: register spills)
-        p.qb = 1;
-        const int envqb = env_int("ATTN_CHUNK_QB", 0);
-        if (envqb == 1 || envqb == 2) p.qb = envqb;
-        p.nqt = (max_q_len + 128 * p.qb - 1) / (128 * p.qb);
+        p.nqt = (max_q_len + kTileRows - 1) / kTileRows;
         const int64_t items = (int64_t)num_seqs * p.nqt * H;
         S = 8192;
         while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < 2048) S /= 2;
@@ -475,10 +471,7 @@ static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_
     } else {
         const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H * a.max_splits;
         const int64_t grid = (n_work + 7) / 8 * 8;
-        if (plan.qb == 2)
-            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 2>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
-        else
-            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a, (int)n_work);
+        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a, (int)n_work);
     }
     if (a.max_splits > 1) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;

@@ -43,13 +43,14 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
     return (bid & 7) * per + (bid >> 3);
 }
 
-template <int D, int QB, bool PAIR>
-__global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void prefill_bf16_kernel(PrefillArgs a)
+template <int D, bool PAIR>
+__global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
 {
     using C = TileCfg<D>;
-    constexpr int BM = QueryTile<QB>::BM;
-    __shared__ __attribute__((aligned(16))) char lds0[C::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[C::BUF_BYTES];
+    constexpr int BM = kTileRows;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    const TileBuffers buf{lds0, lds1};
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work) return;
     const int nqt = (a.N + BM - 1) / BM;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256, QB == 1 ? 2 : 1) void prefill_bf16_kernel(Pref
         out.lse_stride = 1;
         out.fp32_out = 0;
         if (it) __syncthreads();   // LDS reuse across the two tiles
-        run_query_tile<D, QB>(P, kv, out, c2, lds0, lds1);
+        run_query_tile<D>(P, kv, out, c2, buf);
     }
 }
 
@@ -170,7 +171,7 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
     if (a.dtype == 0) {
-        const int BM = 128 * a.qb;
+        const int BM = kTileRows;
         const int nqt = (a.N + BM - 1) / BM;
         const int64_t bh = (int64_t)a.B * a.H;
         const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
@@ -178,16 +179,14 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
         const int grid = (int)((n_work + 7) / 8 * 8);
-#define ATTN_LAUNCH_PREFILL(DD, QQ, PP) \
-    hipLaunchKernelGGL((prefill_bf16_kernel<DD, QQ, PP>), dim3(grid), dim3(256), 0, stream, a)
+#define ATTN_LAUNCH_PREFILL(DD, PP) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
         if (a.d == 128) {
-            if (a.qb == 2) ATTN_LAUNCH_PREFILL(128, 2, false);
-            else if (a.pair) ATTN_LAUNCH_PREFILL(128, 1, true);
-            else ATTN_LAUNCH_PREFILL(128, 1, false);
+            if (a.pair) ATTN_LAUNCH_PREFILL(128, true);
+            else ATTN_LAUNCH_PREFILL(128, false);
         } else {
-            if (a.qb == 2) ATTN_LAUNCH_PREFILL(64, 2, false);
-            else if (a.pair) ATTN_LAUNCH_PREFILL(64, 1, true);
-            else ATTN_LAUNCH_PREFILL(64, 1, false);
+            if (a.pair) ATTN_LAUNCH_PREFILL(64, true);
+            else ATTN_LAUNCH_PREFILL(64, false);
         }
 #undef ATTN_LAUNCH_PREFILL
     } else {
