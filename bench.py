@@ -32,13 +32,17 @@ sys.path.insert(0, str(ROOT))
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
 METRIC = "causal prefill TFLOP/s + paged-decode KV GB/s (and % roofline), 1 MI355X"
-KERNEL_SOURCES = ["attn_mfma_core.h", "attn_mfma_kernel.h", "prefill_gfx950.hip", "paged_gfx950.hip",
-                  "attn_api.hip", "attn_internal.h"]
+# Sources each measured kernel is built from (csrc/): a PMC summary in
+# profiles/ is used only while these files are unchanged.
+KERNEL_SOURCES = {
+    "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "prefill_gfx950.hip", "attn_internal.h"],
+    "decode_c4": ["paged_gfx950.hip", "attn_internal.h"],
+}
 
 
-def kernel_source_hash():
+def kernel_source_hash(kernel_key):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in KERNEL_SOURCES[kernel_key]:
         h.update((ROOT / "tiled_online_softmax_attention_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
@@ -54,7 +58,7 @@ def read_traffic(kernel_key):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != kernel_source_hash():
+    if kv.get("source_sha") != kernel_source_hash(kernel_key):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
