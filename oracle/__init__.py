@@ -23,6 +23,9 @@ passage of the source pages it follows, is stated in the C file's comments:
 * ``tiled_online``         -- the ipipp.com page's block-wise online-softmax
                               forward, in fp64, for the online == two-pass pin.
 * ``lse_merge``            -- merge of partial (O_s, lse_s) over a key partition.
+
+The KV-append oracle (block allocator and per-token page writes) is plain
+Python in ``oracle/kv_cache.py``.
 """
 from __future__ import annotations
 
