@@ -157,6 +157,74 @@ def cpu_baseline_decode(pi, budget_s, oracle):
             "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
 
 
+def append_bytes(new_lens, H, d, elem=2):
+    """Algorithmic bytes of one KV append: the new K and V rows read once and
+    written once, plus each request's lengths and new table entries."""
+    t = sum(new_lens)
+    return 2 * t * H * d * elem * 2 + len(new_lens) * 12
+
+
+def bench_append(args):
+    """KV append (paged_kv_append: allocation launch + copy launch) on the
+    chunked-prefill shape (8 requests x 512 tokens onto U[4096, 32768], 32-token
+    pages) and on one decode step (64 requests x 1 token onto U[512, 16384],
+    16-token pages).  Each timed call starts from the same cache state (table
+    and free count restored, untimed), so it allocates and writes the same
+    blocks every time."""
+    import torch
+    import tiled_online_softmax_attention_amd as attn
+    from tiled_online_softmax_attention_amd import inputs
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.library()
+    dev = torch.device("cuda:0")
+    res = {"metric": "paged KV append GB/s", "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16", "data": "synthetic"}
+    for name, cfg in (("chunk_c5", inputs.C5), ("decode_c4", inputs.C4)):
+        ctx, ql, _ = inputs.draw_lengths(cfg)
+        ctx, ql = [int(c) for c in ctx], [int(q) for q in ql]
+        ctx_old = [c - q for c, q in zip(ctx, ql)]
+        ai = inputs.append_inputs(ctx_old, ql, cfg.H, cfg.d, cfg.block_size, cfg.seed, device=dev)
+        table0 = ai.block_table.clone()
+        free = torch.tensor(ai.free_list + [0] * (ai.pool.shape[0] - len(ai.free_list)), dtype=torch.int32,
+                            device=dev)
+        count = torch.empty(1, dtype=torch.int32, device=dev)
+        ctx_d = torch.tensor(ctx_old, dtype=torch.int32, device=dev)
+        new_d = torch.tensor(ql, dtype=torch.int32, device=dev)
+        nctx = torch.empty_like(ctx_d)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+        timer = EventTimer(torch)
+        for i in range(args.warmup + args.steps):
+            ai.block_table.copy_(table0)
+            count.fill_(len(ai.free_list))
+            e = timer.start() if i >= args.warmup else None
+            attn.kv_append(ai.k_new, ai.v_new, ctx_d, new_d, ai.pool, ai.block_table, free, count,
+                           cfg.block_size, max_new_len=max(ql), new_ctx_lens=nctx, status=status, check=False)
+            if e is not None:
+                timer.stop(e)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        ms = timer.mean_ms()
+        nb = append_bytes(ql, cfg.H, cfg.d)
+        res[name] = {"launch_ms": round(ms, 4), "bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "new_tokens": sum(ql), "requests": len(ql),
+                     "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
+        del ai, table0, free
+        torch.cuda.empty_cache()
+    res["value"] = res["chunk_c5"]["GB/s"]
+    res["config"] = {"workload": "KV append: 8 x 512 tokens (32-token pages) and 64 x 1 token (16-token pages), "
+                                 "H=32, d=128"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,8 +234,11 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append"], default="all")
     args = ap.parse_args()
+
+    if args.only == "append":
+        return bench_append(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -145,6 +145,77 @@ int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block
                     int max_blocks_per_seq, int64_t kv_block_stride, int max_ctx_len,
                     attn_dtype_t dtype, void* k_out, void* v_out, void* stream);
 
+/*
+ * KV append with a device-side block allocator ("Flash Attention and Paged
+ * Attention", section 3: fixed-size blocks, a free list, per-request page
+ * tables that grow by whole blocks; "Sequence length doubles, inference time
+ * quadruples", decode stage: every new token's K and V are added to the cache
+ * after the tokens already there).  Appends new_lens[r] tokens to every
+ * request r of a batch, in one allocation launch and one copy launch.
+ *
+ *   k_new, v_new : packed [sum(new_lens), H, d] (element type `dtype`); request
+ *                  r's rows start at sum_{s<r} new_lens[s].  May be NULL when
+ *                  max_new_len == 0.
+ *   ctx_lens     : int32 [num_seqs] device: tokens already cached per request.
+ *   new_lens     : int32 [num_seqs] device: tokens to append (>= 0).
+ *   k_pool, v_pool, kv_block_stride, block_size : the pool and its addressing,
+ *                  exactly as for paged_attn_fwd; token ctx_lens[r] + i lands
+ *                  in logical block (ctx_lens[r] + i) / block_size, slot
+ *                  (ctx_lens[r] + i) % block_size.
+ *   block_table  : int32 [num_seqs, max_blocks_per_seq] device, in/out.  On
+ *                  entry entries [0, ceil(ctx / block_size)) are the request's
+ *                  blocks (ids in [0, num_blocks)); on success entries
+ *                  [ceil(ctx / bs), ceil((ctx + new) / bs)) receive the newly
+ *                  allocated blocks.  Other entries are untouched.
+ *   free_blocks  : int32 [num_blocks] device, the free list as a stack: ids
+ *                  free_blocks[0 .. *free_count) are free, the top is at
+ *                  *free_count - 1.
+ *   free_count   : int32 device scalar, in/out.
+ *   new_ctx_lens : int32 [num_seqs] device output ctx + new, or NULL; must not
+ *                  be ctx_lens itself.
+ *   status       : int32 device scalar output, ATTN_APPEND_*.
+ *   max_new_len  : host upper bound of new_lens (grid sizing only).
+ *
+ * Allocation follows the pages' allocator: a request that needs k more blocks
+ * takes k ids off the top of the stack, one pop per block, and requests are
+ * served in order -- request r's i-th new block is
+ * free_blocks[*free_count - 1 - (sum_{s<r} need_s + i)], and *free_count drops
+ * by the batch total.  The append is all-or-nothing: if a request would need
+ * more than max_blocks_per_seq table entries (ATTN_APPEND_TABLE_FULL), the
+ * batch needs more blocks than are free (ATTN_APPEND_EXHAUSTED), or a length
+ * or *free_count is out of range (ATTN_APPEND_INVALID), *status says so and
+ * no table entry, pool slot, free_count or new_ctx_lens value changes.
+ * Results reach *status asynchronously (read it after the stream reaches the
+ * call); the allocator runs on the device so a step needs no host round trip.
+ * If an existing table entry a new token lands in is outside [0, num_blocks)
+ * that token is skipped and *status becomes ATTN_APPEND_INVALID after the
+ * blocks were allocated.  Calls that overlap on the same pool or free list
+ * race.
+ */
+enum {
+    ATTN_APPEND_OK = 0,
+    ATTN_APPEND_EXHAUSTED = 1,   /* not enough free blocks for the batch */
+    ATTN_APPEND_TABLE_FULL = 2,  /* a request would need more than max_blocks_per_seq blocks */
+    ATTN_APPEND_INVALID = 3      /* negative length, *free_count out of range, or bad block id */
+};
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* ctx_lens, const int32_t* new_lens,
+                    void* k_pool, void* v_pool, int32_t* block_table, int32_t* free_blocks, int32_t* free_count,
+                    int32_t* new_ctx_lens, int32_t* status, int block_size, int num_seqs, int H, int d,
+                    int max_blocks_per_seq, int64_t kv_block_stride, int num_blocks, int max_new_len,
+                    attn_dtype_t dtype, void* stream);
+
+/*
+ * Return blocks to the free list (the pages' release): blocks[0 .. n) (int32
+ * device) are pushed in order, so blocks[n-1] becomes the top of the stack
+ * and is the next one allocated.  All-or-nothing: if *free_count + n would
+ * exceed num_blocks (ATTN_APPEND_EXHAUSTED) or an id is outside [0,
+ * num_blocks) or *free_count is out of range (ATTN_APPEND_INVALID), *status
+ * says so and nothing changes.  Pushing an id that is already free is not
+ * detected.
+ */
+int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t* free_count, int32_t* status,
+                     int num_blocks, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_strerror(int status);
 

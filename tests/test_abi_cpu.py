@@ -134,3 +134,40 @@ def test_valid_call_without_gpu_reports_device_error():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert prefill() == E_DEV
+
+
+def append(**kw):
+    a = dict(k_new=P, v_new=P2, ctx_lens=P3, new_lens=P4, k_pool=P, v_pool=P2, block_table=P3, free_blocks=P4,
+             free_count=P, new_ctx_lens=P2, status=P3, block_size=16, num_seqs=4, H=8, d=128,
+             max_blocks_per_seq=64, kv_block_stride=2 * 8 * 16 * 128, num_blocks=100, max_new_len=16, dtype=0,
+             stream=NULL)
+    a.update(kw)
+    return attn.paged_kv_append(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ctx_lens=NULL), E_NULL), (dict(new_lens=NULL), E_NULL), (dict(k_pool=NULL), E_NULL),
+    (dict(v_pool=NULL), E_NULL), (dict(block_table=NULL), E_NULL), (dict(free_blocks=NULL), E_NULL),
+    (dict(free_count=NULL), E_NULL), (dict(status=NULL), E_NULL), (dict(k_new=NULL), E_NULL),
+    (dict(v_new=NULL), E_NULL),
+    (dict(num_seqs=0), E_SHAPE), (dict(H=0), E_SHAPE), (dict(max_blocks_per_seq=0), E_SHAPE),
+    (dict(num_blocks=0), E_SHAPE), (dict(max_new_len=-1), E_SHAPE), (dict(kv_block_stride=100), E_SHAPE),
+    (dict(new_ctx_lens=P3), E_SHAPE),                    # aliases ctx_lens
+    (dict(d=96), E_HD), (dict(block_size=8), E_BS), (dict(dtype=5), E_DT),
+    (dict(k_pool=ctypes.c_void_p((1 << 20) + 8)), E_AL), (dict(v_new=ctypes.c_void_p((2 << 20) + 4)), E_AL),
+    (dict(), E_DEV),                                    # valid arguments: only the device check is left
+    (dict(k_new=NULL, v_new=NULL, max_new_len=0), E_DEV),
+])
+def test_append_rejects(kw, code):
+    assert append(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(blocks=NULL), E_NULL), (dict(free_blocks=NULL), E_NULL), (dict(free_count=NULL), E_NULL),
+    (dict(status=NULL), E_NULL), (dict(n=-1), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
+    (dict(blocks=NULL, n=0), E_DEV), (dict(), E_DEV),
+])
+def test_release_rejects(kw, code):
+    a = dict(blocks=P, n=4, free_blocks=P2, free_count=P3, status=P4, num_blocks=100, stream=NULL)
+    a.update(kw)
+    assert attn.paged_kv_release(**a) == code

@@ -14,7 +14,9 @@ from pathlib import Path
 __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
-    "attn_strerror", "attn_version", "prefill", "paged_attention", "gather",
+    "paged_kv_append", "paged_kv_release", "attn_strerror", "attn_version", "prefill", "paged_attention",
+    "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
+    "APPEND_INVALID",
 ]
 
 PKG = Path(__file__).resolve().parent
@@ -23,12 +25,17 @@ LIB_PATH = PKG / "libattn_gfx950.so"
 ATTN_BF16 = 0
 ATTN_F32 = 1
 
+# device status words of paged_kv_append / paged_kv_release
+APPEND_OK, APPEND_EXHAUSTED, APPEND_TABLE_FULL, APPEND_INVALID = 0, 1, 2, 3
+
 # every symbol include/attn.h declares
 exported_symbols = (
     "attn_prefill_fwd",
     "paged_attn_fwd",
     "paged_attn_workspace_bytes",
     "paged_kv_gather",
+    "paged_kv_append",
+    "paged_kv_release",
     "attn_strerror",
     "attn_version",
 )
@@ -64,6 +71,10 @@ def library():
     lib.paged_attn_workspace_bytes.restype = SZ
     lib.paged_kv_gather.argtypes = [P, P, P, P, I, I, I, I, I, I64, I, I, P, P, P]
     lib.paged_kv_gather.restype = I
+    lib.paged_kv_append.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I, P]
+    lib.paged_kv_append.restype = I
+    lib.paged_kv_release.argtypes = [P, I, P, P, P, I, P]
+    lib.paged_kv_release.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -105,6 +116,19 @@ def paged_kv_gather(k_pool, v_pool, block_table, ctx_lens, block_size, num_seqs,
     return library().paged_kv_gather(k_pool, v_pool, block_table, ctx_lens, block_size, num_seqs, H, d,
                                      max_blocks_per_seq, kv_block_stride, max_ctx_len, int(dtype), k_out,
                                      v_out, stream)
+
+
+def paged_kv_append(k_new, v_new, ctx_lens, new_lens, k_pool, v_pool, block_table, free_blocks, free_count,
+                    new_ctx_lens, status, block_size, num_seqs, H, d, max_blocks_per_seq, kv_block_stride,
+                    num_blocks, max_new_len, dtype, stream):
+    return library().paged_kv_append(k_new, v_new, ctx_lens, new_lens, k_pool, v_pool, block_table, free_blocks,
+                                     free_count, new_ctx_lens, status, block_size, num_seqs, H, d,
+                                     max_blocks_per_seq, kv_block_stride, num_blocks, max_new_len, int(dtype),
+                                     stream)
+
+
+def paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream):
+    return library().paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream)
 
 
 # ---- torch-tensor conveniences (marshalling only) -----------------------------
@@ -210,3 +234,57 @@ def gather(pool, block_table, ctx_lens, block_size: int, total_tokens: int | Non
     if rc != 0:
         raise AttnError(rc, "paged_kv_gather")
     return k_out, v_out
+
+
+def _status_error(code: int, what: str) -> RuntimeError:
+    names = {APPEND_EXHAUSTED: "KV cache exhausted (not enough free blocks)",
+             APPEND_TABLE_FULL: "a request would outgrow its block table",
+             APPEND_INVALID: "invalid length, free count or block id"}
+    return RuntimeError("%s: %s" % (what, names.get(code, "status %d" % code)))
+
+
+def kv_append(k_new, v_new, ctx_lens, new_lens, pool, block_table, free_blocks, free_count, block_size: int,
+              max_new_len: int | None = None, new_ctx_lens=None, status=None, check: bool = True, stream=None):
+    """Append new K/V rows to the paged pool [num_blocks, 2, H, bs, d], allocating
+    blocks on the device (paged_kv_append).  With check=True the call waits for
+    the stream and raises RuntimeError when the device reports a failure (the
+    append then changed nothing); with check=False it returns the device status
+    tensor without waiting.  Returns (new_ctx_lens, status)."""
+    import torch
+    num_blocks, two, H, bs, d = pool.shape
+    num_seqs, maxb = block_table.shape
+    if max_new_len is None:
+        max_new_len = int(new_lens.max()) if new_lens.numel() else 0
+    if new_ctx_lens is None:
+        new_ctx_lens = torch.empty_like(ctx_lens)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=pool.device)
+    k_ptr = pool.data_ptr()
+    v_ptr = k_ptr + H * block_size * d * pool.element_size()
+    rc = paged_kv_append(_ptr(k_new), _ptr(v_new), _ptr(ctx_lens), _ptr(new_lens), ctypes.c_void_p(k_ptr),
+                         ctypes.c_void_p(v_ptr), _ptr(block_table), _ptr(free_blocks), _ptr(free_count),
+                         _ptr(new_ctx_lens), _ptr(status), block_size, num_seqs, H, d, maxb,
+                         2 * H * block_size * d, num_blocks, max_new_len, _dtype_code(pool), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "paged_kv_append")
+    if check:
+        code = int(status.item())
+        if code != APPEND_OK:
+            raise _status_error(code, "paged_kv_append")
+    return new_ctx_lens, status
+
+
+def kv_release(blocks, free_blocks, free_count, num_blocks: int, status=None, check: bool = True, stream=None):
+    """Push block ids back on the device free list (paged_kv_release)."""
+    import torch
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=free_blocks.device)
+    rc = paged_kv_release(_ptr(blocks), int(blocks.numel()), _ptr(free_blocks), _ptr(free_count), _ptr(status),
+                          num_blocks, _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "paged_kv_release")
+    if check:
+        code = int(status.item())
+        if code != APPEND_OK:
+            raise _status_error(code, "paged_kv_release")
+    return status

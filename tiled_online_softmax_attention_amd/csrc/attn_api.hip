@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include "attn.h"
+#include "append_internal.h"
 #include "attn_internal.h"
 
 namespace {
@@ -175,6 +176,52 @@ int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block
     a.max_ctx_len = max_ctx_len; a.elem_bytes = eb; a.k_out = k_out; a.v_out = v_out;
     rc = attn::launch_gather(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
+}
+
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* ctx_lens, const int32_t* new_lens,
+                    void* k_pool, void* v_pool, int32_t* block_table, int32_t* free_blocks, int32_t* free_count,
+                    int32_t* new_ctx_lens, int32_t* status, int block_size, int num_seqs, int H, int d,
+                    int max_blocks_per_seq, int64_t kv_block_stride, int num_blocks, int max_new_len,
+                    attn_dtype_t dtype, void* stream)
+{
+    if (!ctx_lens || !new_lens || !k_pool || !v_pool || !block_table || !free_blocks || !free_count || !status)
+        return ATTN_ERR_NULL;
+    if (max_new_len > 0 && (!k_new || !v_new)) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_new_len < 0) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
+    if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
+    if (kv_block_stride < (int64_t)H * block_size * d) return ATTN_ERR_SHAPE;
+    if ((int64_t)num_seqs * ((max_new_len + 3) / 4) > INT32_MAX) return ATTN_ERR_SHAPE;
+    const int eb = (dtype == ATTN_BF16) ? 2 : 4;
+    if (!aligned16(k_pool) || !aligned16(v_pool) || (k_new && !aligned16(k_new)) || (v_new && !aligned16(v_new)) ||
+        ((kv_block_stride * eb) & 15))
+        return ATTN_ERR_ALIGN;
+    if (new_ctx_lens && new_ctx_lens == ctx_lens) return ATTN_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    attn::AppendArgs a{};
+    a.k_new = k_new; a.v_new = v_new; a.ctx_lens = ctx_lens; a.new_lens = new_lens;
+    a.k_pool = k_pool; a.v_pool = v_pool; a.block_table = block_table; a.free_blocks = free_blocks;
+    a.free_count = free_count; a.new_ctx_lens = new_ctx_lens; a.status = status;
+    a.block_size = block_size; a.num_seqs = num_seqs; a.H = H; a.d = d; a.max_blocks_per_seq = max_blocks_per_seq;
+    a.kv_block_stride = kv_block_stride; a.num_blocks = num_blocks; a.max_new_len = max_new_len; a.elem_bytes = eb;
+    rc = attn::launch_append(a, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
+}
+
+int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t* free_count, int32_t* status,
+                     int num_blocks, void* stream)
+{
+    if (!free_blocks || !free_count || !status || (n > 0 && !blocks)) return ATTN_ERR_NULL;
+    if (n < 0 || num_blocks < 1) return ATTN_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    attn::ReleaseArgs a{};
+    a.blocks = blocks; a.n = n; a.free_blocks = free_blocks; a.free_count = free_count; a.status = status;
+    a.num_blocks = num_blocks;
+    rc = attn::launch_release(a, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -159,8 +159,9 @@ def draw_lengths(cfg: PagedConfig, num_seqs=None, ctx_lo=None, ctx_hi=None):
 
 
 def build_paged(ctx_lens, q_lens, H, d, block_size, seed, device="cpu", dtype=torch.bfloat16,
-                cpu_gen=None, spare_frac=0.01, poison=True, max_blocks_per_seq=None):
-    """Lay out a scattered paged KV pool for the given lengths."""
+                cpu_gen=None, spare_frac=0.01, poison=True, max_blocks_per_seq=None, extra_blocks=0):
+    """Lay out a scattered paged KV pool for the given lengths (plus
+    extra_blocks unused blocks on top of the ~spare_frac spares)."""
     ctx_lens = torch.as_tensor(ctx_lens, dtype=torch.int32).cpu()
     q_lens = torch.as_tensor(q_lens, dtype=torch.int32).cpu()
     if cpu_gen is None:
@@ -168,7 +169,7 @@ def build_paged(ctx_lens, q_lens, H, d, block_size, seed, device="cpu", dtype=to
         cpu_gen.manual_seed(seed)
     nblk = [(int(c) + block_size - 1) // block_size for c in ctx_lens]
     used = sum(nblk)
-    spare = max(1, math.ceil(spare_frac * used))
+    spare = max(1, math.ceil(spare_frac * used)) + int(extra_blocks)
     num_blocks = used + spare
     perm = torch.randperm(num_blocks, generator=cpu_gen).to(torch.int32)
     maxb = max(nblk) if max_blocks_per_seq is None else max_blocks_per_seq
@@ -200,6 +201,39 @@ def paged_inputs(cfg: PagedConfig, device="cpu", num_seqs=None, ctx_lo=None, ctx
     ctx, ql, g = draw_lengths(cfg, num_seqs, ctx_lo, ctx_hi)
     return build_paged(ctx, ql, cfg.H if H is None else H, cfg.d, cfg.block_size, cfg.seed, device,
                        cfg.dtype, cpu_gen=g)
+
+
+@dataclass
+class AppendInputs:
+    pool: torch.Tensor         # [num_blocks, 2, H, block_size, d]; spare blocks NaN
+    block_table: torch.Tensor  # int32 [num_seqs, max_blocks]; entries past ceil(ctx_old/bs) are -1
+    ctx_old: torch.Tensor      # int32 [num_seqs]: tokens cached before the append
+    new_lens: torch.Tensor     # int32 [num_seqs]: tokens to append
+    k_new: torch.Tensor        # packed [sum(new_lens), H, d]
+    v_new: torch.Tensor
+    free_list: list            # free block ids, bottom of the stack first
+    block_size: int
+
+
+def append_inputs(ctx_old, new_lens, H, d, block_size, seed, device="cpu", dtype=torch.bfloat16, slack_blocks=4,
+                  table_slack=1):
+    """A paged cache holding ctx_old tokens per request, a free list with
+    enough blocks for appending new_lens tokens (plus slack_blocks), and the
+    new K/V rows.  Free ids are the pool's spare blocks in seeded order."""
+    ctx_old = [int(c) for c in ctx_old]
+    new_lens = [int(n) for n in new_lens]
+    bs = block_size
+    need = sum(-(-(c + n) // bs) - (-(-c // bs)) for c, n in zip(ctx_old, new_lens))
+    maxb = max(1, max(-(-(c + n) // bs) for c, n in zip(ctx_old, new_lens))) + table_slack
+    pi = build_paged(ctx_old, [0] * len(ctx_old), H, d, bs, seed, device, dtype, spare_frac=0.0,
+                     max_blocks_per_seq=maxb, extra_blocks=need + slack_blocks - 1)
+    g = device_generator(seed + 7919, device)
+    tot = sum(new_lens)
+    k_new = _randn((tot, H, d), g, device, dtype)
+    v_new = _randn((tot, H, d), g, device, dtype)
+    return AppendInputs(pool=pi.pool, block_table=pi.block_table, ctx_old=pi.ctx_lens,
+                        new_lens=torch.tensor(new_lens, dtype=torch.int32, device=device), k_new=k_new, v_new=v_new,
+                        free_list=list(pi.spare_blocks), block_size=bs)
 
 
 def sample_triples(seed: int, n: int, dims, edge=()):
