@@ -63,10 +63,10 @@ def _declare(lib):
     P = ctypes.c_void_p
     I = ctypes.c_int
     D = ctypes.c_double
-    lib.oracle_attention.argtypes = [P, P, P, I, I, I, I, I, I, D, I, P, P]
-    lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, I, I, I, D, I, I, P, P, P, P, P]
-    lib.oracle_paged_attention.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, I, D, P, P]
-    lib.oracle_paged_attention_rows.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, I, D, I, P, P, P, P, P]
+    lib.oracle_attention.argtypes = [P, P, P, I, I, I, I, I, I, I, D, I, P, P]
+    lib.oracle_attention_rows.argtypes = [P, P, P, I, I, I, I, I, I, I, D, I, I, P, P, P, P, P]
+    lib.oracle_paged_attention.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, I, I, D, P, P]
+    lib.oracle_paged_attention_rows.argtypes = [P, I, P, I, P, P, P, I, I, I, I, I, I, I, D, I, P, P, P, P, P]
     lib.oracle_paged_gather.argtypes = [P, I, P, P, I, I, I, I, I, I, P, P]
     lib.oracle_tiled_online.argtypes = [P, P, P, I, I, I, I, D, I, I, P, P]
     lib.oracle_lse_merge.argtypes = [I, I, P, P, P, P]
@@ -143,17 +143,19 @@ def num_threads() -> int:
 
 
 def attention(q, k, v, scale: float, causal: bool = False):
-    """q: [B,H,Nq,d], k/v: [B,H,Nk,d] (bf16/fp32/fp64).  Returns (o fp64, lse fp64)."""
+    """q: [B,H,Nq,d], k/v: [B,Hkv,Nk,d] with H a multiple of Hkv (groups of
+    H/Hkv consecutive query heads share a K/V head; Hkv == H is plain
+    multi-head attention).  bf16/fp32/fp64.  Returns (o fp64, lse fp64)."""
     qa, dt = _host_array(q)
     ka, dk = _host_array(k)
     va, dv = _host_array(v)
     assert dt == dk == dv is not None
     B, H, Nq, d = qa.shape
-    Nk = ka.shape[2]
-    assert ka.shape == (B, H, Nk, d) and va.shape == ka.shape
+    Hkv, Nk = ka.shape[1], ka.shape[2]
+    assert ka.shape == (B, Hkv, Nk, d) and va.shape == ka.shape
     o = np.empty((B, H, Nq, d), np.float64)
     lse = np.empty((B, H, Nq), np.float64)
-    _check(load().oracle_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, B, H, Nq, Nk, d, float(scale),
+    _check(load().oracle_attention(_ptr(qa), _ptr(ka), _ptr(va), dt, B, H, Hkv, Nq, Nk, d, float(scale),
                                    1 if causal else 0, _ptr(o), _ptr(lse)), "attention")
     return o, lse
 
@@ -164,33 +166,35 @@ def attention_rows(q, k, v, scale: float, causal: bool, bidx, hidx, rows):
     ka, _ = _host_array(k)
     va, _ = _host_array(v)
     B, H, Nq, d = qa.shape
-    Nk = ka.shape[2]
+    Hkv, Nk = ka.shape[1], ka.shape[2]
     bi, hi, ri = _i32(bidx), _i32(hidx), _i32(rows)
     n = len(bi)
     o = np.empty((n, d), np.float64)
     lse = np.empty((n,), np.float64)
-    _check(load().oracle_attention_rows(_ptr(qa), _ptr(ka), _ptr(va), dt, B, H, Nq, Nk, d, float(scale),
+    _check(load().oracle_attention_rows(_ptr(qa), _ptr(ka), _ptr(va), dt, B, H, Hkv, Nq, Nk, d, float(scale),
                                         1 if causal else 0, n, _ptr(bi), _ptr(hi), _ptr(ri), _ptr(o),
                                         _ptr(lse)), "attention_rows")
     return o, lse
 
 
 def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float):
-    """q: packed [sum(q_lens), H, d]; pool: [num_blocks, 2, H, bs, d].
+    """q: packed [sum(q_lens), H, d]; pool: [num_blocks, 2, Hkv, bs, d] with H a
+    multiple of Hkv (query head h reads K/V head h // (H // Hkv)).
     Returns (o fp64 [sum(q_lens), H, d], lse fp64 [sum(q_lens), H])."""
     qa, dq = _host_array(q)
     pa, dp = _host_array(pool)
     bt = _i32(block_table)
     cl, ql = _i32(ctx_lens), _i32(q_lens)
-    num_blocks, two, H, bs, d = pa.shape
+    num_blocks, two, Hkv, bs, d = pa.shape
     assert two == 2 and bs == block_size
     num_seqs, maxb = bt.shape
     total_q = int(ql.sum())
+    H = qa.shape[1]
     assert qa.shape == (total_q, H, d)
     o = np.empty((total_q, H, d), np.float64)
     lse = np.empty((total_q, H), np.float64)
     _check(load().oracle_paged_attention(_ptr(qa), dq, _ptr(pa), dp, _ptr(bt), _ptr(cl), _ptr(ql), num_seqs,
-                                         H, d, bs, maxb, num_blocks, float(scale), _ptr(o), _ptr(lse)),
+                                         H, Hkv, d, bs, maxb, num_blocks, float(scale), _ptr(o), _ptr(lse)),
            "paged_attention")
     return o, lse
 
@@ -202,14 +206,15 @@ def paged_attention_rows(q, pool, block_table, ctx_lens, q_lens, block_size: int
     pa, dp = _host_array(pool)
     bt = _i32(block_table)
     cl, ql = _i32(ctx_lens), _i32(q_lens)
-    num_blocks, two, H, bs, d = pa.shape
+    num_blocks, two, Hkv, bs, d = pa.shape
+    H = qa.shape[1]
     num_seqs, maxb = bt.shape
     ri, hi, ii = _i32(ridx), _i32(hidx), _i32(iidx)
     n = len(ri)
     o = np.empty((n, d), np.float64)
     lse = np.empty((n,), np.float64)
     _check(load().oracle_paged_attention_rows(_ptr(qa), dq, _ptr(pa), dp, _ptr(bt), _ptr(cl), _ptr(ql),
-                                              num_seqs, H, d, bs, maxb, num_blocks, float(scale), n,
+                                              num_seqs, H, Hkv, d, bs, maxb, num_blocks, float(scale), n,
                                               _ptr(ri), _ptr(hi), _ptr(ii), _ptr(o), _ptr(lse)),
            "paged_attention_rows")
     return o, lse

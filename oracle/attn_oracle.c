@@ -136,15 +136,22 @@ static void load_head(const void* x, int dtype, int64_t bh, int64_t rows, int d,
     for (int64_t r = 0; r < rows * d; ++r) out[r] = elem(x, dtype, base + r);
 }
 
+/* K/V head of query head h when Hkv K/V heads serve H query heads: groups of
+ * H / Hkv consecutive query heads share one K/V head ("Sequence length
+ * doubles, inference time quadruples", further optimisations: grouped-query
+ * attention; Hkv == H is ordinary multi-head attention, Hkv == 1 is MQA). */
+static int kv_head(int h, int H, int Hkv) { return h / (H / Hkv); }
+
 /*
- * Contiguous attention over [B,H,Nq,d] queries and [B,H,Nk,d] keys/values.
- * o: fp64 [B,H,Nq,d]; lse: fp64 [B,H,Nq] (may be NULL).
+ * Contiguous attention over [B,H,Nq,d] queries and [B,Hkv,Nk,d] keys/values
+ * (H a multiple of Hkv).  o: fp64 [B,H,Nq,d]; lse: fp64 [B,H,Nq] (may be NULL).
  */
 int oracle_attention(const void* q, const void* k, const void* v, int dtype,
-                     int B, int H, int Nq, int Nk, int d, double scale, int mask_mode,
+                     int B, int H, int Hkv, int Nq, int Nk, int d, double scale, int mask_mode,
                      double* o, double* lse)
 {
     if (!q || !k || !v || !o || B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1) return ORACLE_ERR_ARG;
+    if (Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
     if (dtype < ORACLE_BF16 || dtype > ORACLE_F64 || mask_mode < 0 || mask_mode > 1) return ORACLE_ERR_ARG;
     int err = ORACLE_OK;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -159,9 +166,10 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
 #pragma omp atomic write
             err = ORACLE_ERR_ALLOC;
         } else {
+            int64_t bkv = (bh / H) * Hkv + kv_head((int)(bh % H), H, Hkv);
             load_head(q, dtype, bh, Nq, d, Q);
-            load_head(k, dtype, bh, Nk, d, K);
-            load_head(v, dtype, bh, Nk, d, V);
+            load_head(k, dtype, bkv, Nk, d, K);
+            load_head(v, dtype, bkv, Nk, d, V);
             for (int64_t i = 0; i < Nq; ++i) lim[i] = allowed_keys(mask_mode, i, Nq, Nk);
             attention_dense(Q, K, V, Nq, Nk, d, scale, lim, S, P, o + bh * Nq * d,
                             lse ? lse + bh * Nq : NULL);
@@ -177,11 +185,12 @@ int oracle_attention(const void* q, const void* k, const void* v, int dtype,
  * Each sample materialises its full masked score row against all Nk keys.
  */
 int oracle_attention_rows(const void* q, const void* k, const void* v, int dtype,
-                          int B, int H, int Nq, int Nk, int d, double scale, int mask_mode,
+                          int B, int H, int Hkv, int Nq, int Nk, int d, double scale, int mask_mode,
                           int n, const int* bidx, const int* hidx, const int* rows,
                           double* o, double* lse)
 {
     if (!q || !k || !v || !o || !bidx || !hidx || !rows || n < 0) return ORACLE_ERR_ARG;
+    if (Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
     for (int s = 0; s < n; ++s)
         if (bidx[s] < 0 || bidx[s] >= B || hidx[s] < 0 || hidx[s] >= H || rows[s] < 0 || rows[s] >= Nq)
             return ORACLE_ERR_ARG;
@@ -198,9 +207,10 @@ int oracle_attention_rows(const void* q, const void* k, const void* v, int dtype
 #pragma omp atomic write
             err = ORACLE_ERR_ALLOC;
         } else {
+            int64_t bkv = (int64_t)bidx[s] * Hkv + kv_head(hidx[s], H, Hkv);
             for (int c = 0; c < d; ++c) Q[c] = elem(q, dtype, (bh * Nq + rows[s]) * d + c);
-            load_head(k, dtype, bh, Nk, d, K);
-            load_head(v, dtype, bh, Nk, d, V);
+            load_head(k, dtype, bkv, Nk, d, K);
+            load_head(v, dtype, bkv, Nk, d, V);
             int64_t lim = allowed_keys(mask_mode, rows[s], Nq, Nk);
             attention_dense(Q, K, V, 1, Nk, d, scale, &lim, S, P, o + (int64_t)s * d,
                             lse ? lse + s : NULL);
@@ -257,17 +267,19 @@ static int check_paged_args(const int* ctx_lens, const int* q_lens, int num_seqs
 
 /*
  * Paged attention, all rows.  q: packed [sum(q_lens), H, d] (request r's rows
- * start at sum_{s<r} q_lens[s]); pool: [num_blocks, 2, H, bs, d];
+ * start at sum_{s<r} q_lens[s]); pool: [num_blocks, 2, Hkv, bs, d] (query
+ * head h reads K/V head kv_head(h, H, Hkv));
  * block_table: int32 [num_seqs][maxb]; ctx_lens includes the q_lens new tokens.
  * Query row i of request r attends keys j <= ctx_r - q_r + i.
  * o: fp64 [sum(q_lens), H, d]; lse: fp64 [sum(q_lens), H] (may be NULL).
  */
 int oracle_paged_attention(const void* q, int q_dtype, const void* pool, int pool_dtype,
                            const int* block_table, const int* ctx_lens, const int* q_lens,
-                           int num_seqs, int H, int d, int bs, int maxb, int num_blocks,
+                           int num_seqs, int H, int Hkv, int d, int bs, int maxb, int num_blocks,
                            double scale, double* o, double* lse)
 {
     if (!q || !pool || !block_table || !ctx_lens || !q_lens || !o) return ORACLE_ERR_ARG;
+    if (Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
     int rc = check_paged_args(ctx_lens, q_lens, num_seqs, H, d, bs, maxb);
     if (rc) return rc;
     int err = ORACLE_OK;
@@ -286,7 +298,8 @@ int oracle_paged_attention(const void* q, int q_dtype, const void* pool, int poo
         int my = ORACLE_OK;
         if (!Q || !K || !V || !S || !P || !O || !L || !lim) my = ORACLE_ERR_ALLOC;
         if (my == ORACLE_OK)
-            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, h, ctx, H, bs, d, K, V);
+            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, kv_head(h, H, Hkv), ctx, Hkv,
+                             bs, d, K, V);
         if (my == ORACLE_OK) {
             for (int64_t i = 0; i < nq; ++i) {
                 for (int c = 0; c < d; ++c) Q[i * d + c] = elem(q, q_dtype, ((row0 + i) * H + h) * d + c);
@@ -311,12 +324,13 @@ int oracle_paged_attention(const void* q, int q_dtype, const void* pool, int poo
  * o: fp64 [n][d]; lse: [n]. */
 int oracle_paged_attention_rows(const void* q, int q_dtype, const void* pool, int pool_dtype,
                                 const int* block_table, const int* ctx_lens, const int* q_lens,
-                                int num_seqs, int H, int d, int bs, int maxb, int num_blocks,
+                                int num_seqs, int H, int Hkv, int d, int bs, int maxb, int num_blocks,
                                 double scale, int n, const int* ridx, const int* hidx,
                                 const int* iidx, double* o, double* lse)
 {
     if (!q || !pool || !block_table || !ctx_lens || !q_lens || !o || !ridx || !hidx || !iidx || n < 0)
         return ORACLE_ERR_ARG;
+    if (Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
     int rc = check_paged_args(ctx_lens, q_lens, num_seqs, H, d, bs, maxb);
     if (rc) return rc;
     for (int s = 0; s < n; ++s)
@@ -337,7 +351,8 @@ int oracle_paged_attention_rows(const void* q, int q_dtype, const void* pool, in
         int my = ORACLE_OK;
         if (!Q || !K || !V || !S || !P) my = ORACLE_ERR_ALLOC;
         if (my == ORACLE_OK)
-            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, h, ctx, H, bs, d, K, V);
+            my = gather_head(pool, pool_dtype, block_table, maxb, num_blocks, r, kv_head(h, H, Hkv), ctx, Hkv,
+                             bs, d, K, V);
         if (my == ORACLE_OK) {
             for (int c = 0; c < d; ++c) Q[c] = elem(q, q_dtype, (row * H + h) * d + c);
             int64_t lim = allowed_keys(1, i, nq, ctx);

@@ -365,6 +365,59 @@ def check_bf16_upcast_exact():
     assert o[0, 0, 0, 0] == 1.0 + 2.0 ** -7
 
 
+def check_gqa_torch_sdpa():
+    """Grouped-query attention ("Sequence length doubles ...", further
+    optimisations: several query heads share one K/V head; MQA when all do)
+    against torch's CPU fp64 SDPA with enable_gqa (consecutive query heads
+    share a K/V head, the K/V heads repeated by repeat_interleave)."""
+    rng = _rng(30)
+    B, n, d, scale = 2, 9, 8, 0.4
+    for H, Hkv in ((4, 2), (6, 3), (4, 1), (3, 3), (8, 2)):
+        q = torch.from_numpy(rng.standard_normal((B, H, n, d)))
+        k = torch.from_numpy(rng.standard_normal((B, Hkv, n, d)))
+        v = torch.from_numpy(rng.standard_normal((B, Hkv, n, d)))
+        for causal in (False, True):
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale,
+                                                                   enable_gqa=True)
+            o, _ = oracle.attention(q, k, v, scale, causal)
+            assert np.allclose(o, ref.numpy(), rtol=0, atol=1e-12), (H, Hkv, causal)
+        # the same through sampled rows
+        o, _ = oracle.attention(q, k, v, scale, True)
+        orow, _ = oracle.attention_rows(q, k, v, scale, True, [1, 0], [H - 1, 0], [n - 1, 3])
+        assert np.array_equal(orow[0], o[1, H - 1, n - 1]) and np.array_equal(orow[1], o[0, 0, 3])
+
+
+def check_gqa_paged_equals_contiguous():
+    """Paged GQA (pool holds Hkv heads) equals contiguous GQA bit for bit."""
+    rng = _rng(31)
+    H, Hkv, d, bs = 6, 2, 8, 4
+    ctx_lens, q_lens = [13, 7], [5, 7]
+    kvs = [rng.standard_normal((2, Hkv, c, d)) for c in ctx_lens]
+    qs = [rng.standard_normal((ql, H, d)) for ql in q_lens]
+    pools, tables, base = [], [], 0
+    for kv in kvs:
+        pl, t = _scatter(kv, bs, rng)
+        pools.append(pl)
+        tables.append(t + base)
+        base += pl.shape[0]
+    pool = np.concatenate(pools)
+    table = np.full((2, max(len(t) for t in tables)), -1, np.int32)
+    for r, t in enumerate(tables):
+        table[r, :len(t)] = t
+    cl, ql = np.array(ctx_lens, np.int32), np.array(q_lens, np.int32)
+    o_p, l_p = oracle.paged_attention(np.concatenate(qs), pool, table, cl, ql, bs, 0.3)
+    orow, lrow = oracle.paged_attention_rows(np.concatenate(qs), pool, table, cl, ql, bs, 0.3, [0, 1], [5, 2],
+                                             [4, 0])
+    assert np.array_equal(orow[0], o_p[4, 5]) and np.array_equal(orow[1], o_p[5, 2])
+    row = 0
+    for r, (kv, qr) in enumerate(zip(kvs, qs)):
+        qc = qr.transpose(1, 0, 2)[None]                       # [1, H, ql, d]
+        oc, lc = oracle.attention(qc, kv[0][None], kv[1][None], 0.3, True)   # bottom-right when ql < ctx
+        assert np.array_equal(oc[0].transpose(1, 0, 2), o_p[row:row + q_lens[r]])
+        assert np.array_equal(lc[0].T, l_p[row:row + q_lens[r]])
+        row += q_lens[r]
+
+
 ALL_CHECKS = [
     check_golden_fixtures,
     check_bruteforce_tiny,
@@ -379,4 +432,6 @@ ALL_CHECKS = [
     check_paged_equals_contiguous_bitexact,
     check_gather_bitexact,
     check_bf16_upcast_exact,
+    check_gqa_torch_sdpa,
+    check_gqa_paged_equals_contiguous,
 ]

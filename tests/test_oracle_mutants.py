@@ -35,6 +35,8 @@ MUTANTS = [
     ("bf16_low_half", "uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]) << 16;",
      "uint32_t bits = ((uint32_t)((const uint16_t*)base)[idx]);"),
     ("prefix_skips_request", "for (int i = 0; i < r; ++i) s += q_lens[i];", "for (int i = 1; i < r; ++i) s += q_lens[i];"),
+    ("gqa_strided_groups", "static int kv_head(int h, int H, int Hkv) { return h / (H / Hkv); }",
+     "static int kv_head(int h, int H, int Hkv) { return h % Hkv; }"),
 ]
 
 
