@@ -71,15 +71,19 @@ def prefill_flops(B, H, N, d, causal):
     return 4.0 * d * pairs * B * H
 
 
-def prefill_bytes(B, H, N, d, elem=2):
-    return B * H * N * d * elem * 4 + B * H * N * 4   # q, k, v read + o written + lse
+def prefill_bytes(B, H, N, d, elem=2, H_kv=None):
+    H_kv = H if H_kv is None else H_kv
+    return B * N * d * elem * (2 * H + 2 * H_kv) + B * H * N * 4   # q, k, v read + o written + lse
 
 
-def paged_bytes(ctx_lens, q_lens, H, d, block_size, elem=2):
+def paged_bytes(ctx_lens, q_lens, H, d, block_size, elem=2, H_kv=None):
+    """K and V of every context token once (for the H_kv K/V heads), q read
+    and o, lse written (H query heads), one table entry per page."""
+    H_kv = H if H_kv is None else H_kv
     ctx = sum(ctx_lens)
     tq = sum(q_lens)
     pages = sum((c + block_size - 1) // block_size for c in ctx_lens)
-    return 2 * ctx * H * d * elem + 2 * tq * H * d * elem + tq * H * 4 + pages * 4
+    return 2 * ctx * H_kv * d * elem + 2 * tq * H * d * elem + tq * H * 4 + pages * 4
 
 
 def paged_flops(ctx_lens, q_lens, d, H):
@@ -225,6 +229,62 @@ def bench_append(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_gqa(args):
+    """Grouped-query variants (32 query heads on 4 K/V heads): the causal
+    16x32x8192x128 prefill (TFLOP/s) and the 64-request decode batch (KV GB/s,
+    K/V of the 4 shared heads counted once)."""
+    import torch
+    import tiled_online_softmax_attention_amd as attn
+    from tiled_online_softmax_attention_amd import inputs
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.library()
+    dev = torch.device("cuda:0")
+    c3, c4 = inputs.C3_GQA8, inputs.C4_GQA8
+    q, k, v = inputs.prefill_inputs(c3, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((c3.B, c3.H, c3.N), dtype=torch.float32, device=dev)
+    pi = inputs.paged_inputs(c4, dev)
+    ctx_list, ql_list = pi.ctx_lens.cpu().tolist(), pi.q_lens.cpu().tolist()
+    ws = torch.empty(max(1, attn.paged_attn_gqa_workspace_bytes(pi.num_seqs, c4.H, c4.H_kv, c4.d, c4.block_size, 1,
+                                                                max(ctx_list))), dtype=torch.uint8, device=dev)
+    od = torch.empty_like(pi.q)
+    lsed = torch.empty(pi.q.shape[:2], dtype=torch.float32, device=dev)
+    t_pre, t_dec = EventTimer(torch), EventTimer(torch)
+    for i in range(args.warmup + args.steps):
+        e = t_pre.start() if i >= args.warmup else None
+        attn.prefill(q, k, v, True, c3.scale, out=o, lse=lse)
+        if e is not None:
+            t_pre.stop(e)
+        e = t_dec.start() if i >= args.warmup else None
+        attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
+                             max_q_len=1, max_ctx_len=max(ctx_list), out=od, lse=lsed, workspace=ws)
+        if e is not None:
+            t_dec.stop(e)
+    torch.cuda.synchronize()
+    ms_p, ms_d = t_pre.mean_ms(), t_dec.mean_ms()
+    fl = prefill_flops(c3.B, c3.H, c3.N, c3.d, True)
+    nb = paged_bytes(ctx_list, ql_list, c4.H, c4.d, c4.block_size, H_kv=c4.H_kv)
+    tf, gbs = fl / (ms_p * 1e-3) / 1e12, nb / (ms_d * 1e-3) / 1e9
+    res = {"metric": "GQA-8 causal prefill TFLOP/s + paged-decode KV GB/s", "value": round(tf, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "causal prefill bf16 16x32x8192x128 with 4 K/V heads + paged decode bf16 64 req x "
+                                  "1 query, ctx U[512,16384], 16-token pages, 32 query heads on 4 K/V heads"},
+           "prefill": {"launch_ms": round(ms_p, 4),
+                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}},
+           "decode": {"launch_ms": round(ms_d, 4), "bytes_per_call": nb, "GB/s": round(gbs, 1),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBPS, 4)}}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -234,11 +294,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa"], default="all")
     args = ap.parse_args()
 
     if args.only == "append":
         return bench_append(args)
+    if args.only == "gqa":
+        return bench_gqa(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -132,6 +132,37 @@ size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size,
                                   int max_q_len, int max_ctx_len);
 
 /*
+ * Grouped-query attention ("Sequence length doubles, inference time
+ * quadruples", further optimisations: several query heads share one key and
+ * value head; with one shared K/V head it is multi-query attention): H query
+ * heads and H_kv K/V heads, H a multiple of H_kv; query head h uses K/V head
+ * h / (H / H_kv) (groups of consecutive query heads).  Everything else is as
+ * for the functions above, which are these with H_kv = H.
+ *
+ * attn_prefill_gqa_fwd: q, o [B, H, N, d]; k, v [B, H_kv, N, d]; lse [B, H, N].
+ *   The query tiles of the heads of one group run next to each other, so K/V
+ *   of a group is read from HBM once and reused through L2.
+ * paged_attn_gqa_fwd: q, o packed [sum(q_lens), H, d], lse [sum(q_lens), H];
+ *   the pool holds H_kv heads per block ([H_kv, block_size, d] per block, so
+ *   kv_block_stride >= H_kv * block_size * d).  On the decode path (q_len <=
+ *   4) one workgroup serves up to 8 query heads of a group, so each K/V page
+ *   is read once for all of them.
+ * paged_attn_gqa_workspace_bytes: the workspace paged_attn_gqa_fwd needs.
+ * H % H_kv != 0 or H_kv < 1 is ATTN_ERR_SHAPE.
+ */
+int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int H_kv, int N, int d, float scale, int causal,
+                         attn_dtype_t dtype, void* stream);
+int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                       int block_size, void* o, float* lse,
+                       int num_seqs, int H, int H_kv, int d, float scale, int max_blocks_per_seq,
+                       int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int block_size,
+                                      int max_q_len, int max_ctx_len);
+
+/*
  * Gather through the block table ("Chunked attention ... 70x slower",
  * section 2.1, the address function): copies K and V of every request,
  * tokens [0, ctx_lens[r]), into packed token-major [sum(ctx_lens), H, d]

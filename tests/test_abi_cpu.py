@@ -171,3 +171,38 @@ def test_release_rejects(kw, code):
     a = dict(blocks=P, n=4, free_blocks=P2, free_count=P3, status=P4, num_blocks=100, stream=NULL)
     a.update(kw)
     assert attn.paged_kv_release(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H_kv=0), E_SHAPE), (dict(H_kv=3), E_SHAPE), (dict(H_kv=16), E_SHAPE), (dict(), E_DEV),
+    (dict(k=NULL), E_NULL), (dict(d=80), E_HD),
+])
+def test_prefill_gqa_rejects(kw, code):
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=NULL, B=1, H=8, H_kv=2, N=64, d=128, scale=0.125, causal=1, dtype=0,
+             stream=NULL)
+    a.update(kw)
+    assert attn.attn_prefill_gqa_fwd(**a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H_kv=0), E_SHAPE), (dict(H_kv=3), E_SHAPE), (dict(H_kv=16), E_SHAPE),
+    (dict(kv_block_stride=2 * 16 * 128 - 16), E_SHAPE),         # below H_kv * bs * d
+    (dict(), E_DEV),
+])
+def test_paged_gqa_rejects(kw, code):
+    a = dict(q=P, k_pool=P2, v_pool=P3, block_table=P4, ctx_lens=P, q_lens=P2, block_size=16, o=P3, lse=NULL,
+             num_seqs=4, H=8, H_kv=2, d=128, scale=0.1, max_blocks_per_seq=64, kv_block_stride=2 * 2 * 16 * 128,
+             num_blocks=100, max_q_len=1, max_ctx_len=1024, dtype=0, workspace=NULL, workspace_bytes=0,
+             stream=NULL)
+    a.update(kw)
+    if code == E_DEV and attn.paged_attn_gqa_workspace_bytes(4, 8, 2, 128, 16, 1, 1024):
+        a["workspace"] = ctypes.c_void_p(8 << 20)
+        a["workspace_bytes"] = attn.paged_attn_gqa_workspace_bytes(4, 8, 2, 128, 16, 1, 1024)
+    assert attn.paged_attn_gqa_fwd(**a) == code
+
+
+def test_gqa_workspace_matches_plain_at_equal_heads():
+    for args in ((64, 32, 128, 16, 1, 16384), (8, 32, 128, 32, 512, 32768), (4, 8, 64, 16, 3, 100)):
+        n, H, d, bs, mq, mc = args
+        assert attn.paged_attn_gqa_workspace_bytes(n, H, H, d, bs, mq, mc) == attn.paged_attn_workspace_bytes(*args)
+    assert attn.paged_attn_gqa_workspace_bytes(4, 8, 3, 128, 16, 1, 100) == 0

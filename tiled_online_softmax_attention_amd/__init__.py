@@ -14,7 +14,8 @@ from pathlib import Path
 __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
-    "paged_kv_append", "paged_kv_release", "attn_strerror", "attn_version", "prefill", "paged_attention",
+    "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
+    "paged_attn_gqa_workspace_bytes", "attn_strerror", "attn_version", "prefill", "paged_attention",
     "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
     "APPEND_INVALID",
 ]
@@ -36,6 +37,9 @@ exported_symbols = (
     "paged_kv_gather",
     "paged_kv_append",
     "paged_kv_release",
+    "attn_prefill_gqa_fwd",
+    "paged_attn_gqa_fwd",
+    "paged_attn_gqa_workspace_bytes",
     "attn_strerror",
     "attn_version",
 )
@@ -75,6 +79,12 @@ def library():
     lib.paged_kv_append.restype = I
     lib.paged_kv_release.argtypes = [P, I, P, P, P, I, P]
     lib.paged_kv_release.restype = I
+    lib.attn_prefill_gqa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_prefill_gqa_fwd.restype = I
+    lib.paged_attn_gqa_fwd.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, F, I, I64, I, I, I, I, P, SZ, P]
+    lib.paged_attn_gqa_fwd.restype = I
+    lib.paged_attn_gqa_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.paged_attn_gqa_workspace_bytes.restype = SZ
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -127,6 +137,24 @@ def paged_kv_append(k_new, v_new, ctx_lens, new_lens, k_pool, v_pool, block_tabl
                                      stream)
 
 
+def attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream):
+    return library().attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H_kv, N, d, float(scale), int(causal), int(dtype),
+                                          stream)
+
+
+def paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, H_kv, d,
+                       scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len, dtype,
+                       workspace, workspace_bytes, stream):
+    return library().paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse,
+                                        num_seqs, H, H_kv, d, float(scale), max_blocks_per_seq, kv_block_stride,
+                                        num_blocks, max_q_len, max_ctx_len, int(dtype), workspace, workspace_bytes,
+                                        stream)
+
+
+def paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len) -> int:
+    return int(library().paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len))
+
+
 def paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream):
     return library().paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream)
 
@@ -154,11 +182,13 @@ def _ptr(t):
 
 def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None, want_lse=True,
             stream=None):
-    """O (and LSE) for q, k, v of shape [B, H, N, d] on the GPU."""
+    """O (and LSE) for q [B, H, N, d] and k, v [B, H_kv, N, d] on the GPU (H_kv < H:
+    grouped-query attention, query head h reads K/V head h // (H // H_kv))."""
     import torch
     B, H, N, d = q.shape
-    if k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share shape [B, H, N, d]")
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != k.shape or H % H_kv != 0:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d] with H a multiple of H_kv")
     for t in (q, k, v):
         if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v must be contiguous, same dtype and device")
@@ -168,8 +198,12 @@ def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=Non
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    rc = attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
-                          1 if causal else 0, _dtype_code(q), _stream(stream))
+    if H_kv == H:
+        rc = attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                              1 if causal else 0, _dtype_code(q), _stream(stream))
+    else:
+        rc = attn_prefill_gqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, N, d, scale,
+                                  1 if causal else 0, _dtype_code(q), _stream(stream))
     if rc != 0:
         raise AttnError(rc, "attn_prefill_fwd")
     return out, lse
@@ -178,15 +212,17 @@ def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=Non
 def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float | None = None,
                     max_q_len: int | None = None, max_ctx_len: int | None = None, out=None, lse=None,
                     want_lse=True, workspace=None, stream=None):
-    """Paged attention over the pool [num_blocks, 2, H, block_size, d] (K at 0, V at 1).
+    """Paged attention over the pool [num_blocks, 2, H_kv, block_size, d] (K at 0, V at 1).
 
-    q: packed [sum(q_lens), H, d] bf16; block_table int32 [num_seqs, max_blocks];
+    q: packed [sum(q_lens), H, d] bf16 with H a multiple of H_kv (grouped-query
+    attention when H_kv < H); block_table int32 [num_seqs, max_blocks];
     ctx_lens, q_lens int32 [num_seqs] on the device.  max_q_len / max_ctx_len are
     host bounds (read from the tensors with a device sync when omitted)."""
     import torch
-    num_blocks, two, H, bs, d = pool.shape
-    if two != 2 or bs != block_size:
-        raise ValueError("pool must be [num_blocks, 2, H, block_size, d]")
+    num_blocks, two, H_kv, bs, d = pool.shape
+    H = q.shape[1]
+    if two != 2 or bs != block_size or H % H_kv != 0:
+        raise ValueError("pool must be [num_blocks, 2, H_kv, block_size, d] with H_kv dividing q's heads")
     if not pool.is_contiguous() or not q.is_contiguous() or not block_table.is_contiguous():
         raise ValueError("pool, q and block_table must be contiguous")
     num_seqs, maxb = block_table.shape
@@ -198,17 +234,24 @@ def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, sca
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    ws_bytes = paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len)
+    ws_bytes = paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    kv_stride = 2 * H * block_size * d
+    kv_stride = 2 * H_kv * block_size * d
     k_ptr = pool.data_ptr()
-    v_ptr = k_ptr + H * block_size * d * pool.element_size()
-    rc = paged_attn_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
-                        _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, d,
-                        d ** -0.5 if scale is None else scale, maxb, kv_stride, num_blocks, max_q_len,
-                        max_ctx_len, _dtype_code(q), _ptr(workspace),
-                        workspace.numel() if workspace is not None else 0, _stream(stream))
+    v_ptr = k_ptr + H_kv * block_size * d * pool.element_size()
+    sc = d ** -0.5 if scale is None else scale
+    wsb = workspace.numel() if workspace is not None else 0
+    if H_kv == H:
+        rc = paged_attn_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
+                            _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, d, sc,
+                            maxb, kv_stride, num_blocks, max_q_len, max_ctx_len, _dtype_code(q), _ptr(workspace),
+                            wsb, _stream(stream))
+    else:
+        rc = paged_attn_gqa_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
+                                _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, H_kv,
+                                d, sc, maxb, kv_stride, num_blocks, max_q_len, max_ctx_len, _dtype_code(q),
+                                _ptr(workspace), wsb, _stream(stream))
     if rc != 0:
         raise AttnError(rc, "paged_attn_fwd")
     return out, lse

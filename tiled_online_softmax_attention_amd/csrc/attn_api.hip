@@ -59,12 +59,12 @@ const char* attn_strerror(int status)
 
 const char* attn_version(void) { return "attn_gfx950 1.0"; }
 
-int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                     int B, int H, int N, int d, float scale, int causal,
-                     attn_dtype_t dtype, void* stream)
+int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int H_kv, int N, int d, float scale, int causal,
+                         attn_dtype_t dtype, void* stream)
 {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
-    if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+    if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_BF16 && dtype != ATTN_F32) return ATTN_ERR_DTYPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
@@ -77,7 +77,7 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     if (rc) return rc;
     attn::PrefillArgs a{};
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.B = B; a.H = H; a.N = N; a.d = d;
+    a.B = B; a.H = H; a.H_kv = H_kv; a.N = N; a.d = d;
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
@@ -95,36 +95,49 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
 
-size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
+int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int causal,
+                     attn_dtype_t dtype, void* stream)
 {
-    if (num_seqs < 1 || H < 1 || (d != 64 && d != 128) || (block_size != 16 && block_size != 32) ||
-        max_q_len < 1 || max_ctx_len < 1)
-        return 0;
-    return attn::plan_paged(num_seqs, H, d, block_size, max_q_len, max_ctx_len).ws_bytes;
+    return attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
 }
 
-int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
-                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
-                   int block_size, void* o, float* lse,
-                   int num_seqs, int H, int d, float scale, int max_blocks_per_seq,
-                   int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
-                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len,
+                                      int max_ctx_len)
+{
+    if (num_seqs < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || H / H_kv > 128 || (d != 64 && d != 128) ||
+        (block_size != 16 && block_size != 32) || max_q_len < 1 || max_ctx_len < 1)
+        return 0;
+    return attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len).ws_bytes;
+}
+
+size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
+{
+    return paged_attn_gqa_workspace_bytes(num_seqs, H, H, d, block_size, max_q_len, max_ctx_len);
+}
+
+int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                       int block_size, void* o, float* lse,
+                       int num_seqs, int H, int H_kv, int d, float scale, int max_blocks_per_seq,
+                       int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
 {
     if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !q_lens || !o) return ATTN_ERR_NULL;
     if (num_seqs < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 1 ||
-        max_ctx_len < 1 || max_q_len > max_ctx_len)
+        max_ctx_len < 1 || max_q_len > max_ctx_len || H_kv < 1 || H % H_kv != 0 || H / H_kv > 128)
         return ATTN_ERR_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
     if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
     if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if ((int64_t)(max_ctx_len + block_size - 1) / block_size > max_blocks_per_seq) return ATTN_ERR_SHAPE;
-    if (kv_block_stride < (int64_t)H * block_size * d) return ATTN_ERR_SHAPE;
+    if (kv_block_stride < (int64_t)H_kv * block_size * d) return ATTN_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
         ((kv_block_stride * 2) & 15) || ((uintptr_t)block_table & 3u) || ((uintptr_t)lse & 3u))
         return ATTN_ERR_ALIGN;
     int rc = check_scale(scale);
     if (rc) return rc;
-    const attn::PagedPlan plan = attn::plan_paged(num_seqs, H, d, block_size, max_q_len, max_ctx_len);
+    const attn::PagedPlan plan = attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len);
     // grid sizes must fit 32 bits
     const int64_t rows = (int64_t)num_seqs * max_q_len;
     if (rows * H * plan.max_splits > (int64_t)INT32_MAX - 8) return ATTN_ERR_SHAPE;
@@ -138,7 +151,7 @@ int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
     a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
     a.block_table = block_table; a.ctx_lens = ctx_lens; a.q_lens = q_lens;
     a.block_size = block_size; a.o = o; a.lse = lse;
-    a.num_seqs = num_seqs; a.H = H; a.d = d; a.scale = scale;
+    a.num_seqs = num_seqs; a.H = H; a.H_kv = H_kv; a.n_chunks = plan.n_chunks; a.d = d; a.scale = scale;
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.kv_block_stride = kv_block_stride;
     a.num_blocks = num_blocks;
@@ -149,6 +162,18 @@ int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
     a.ws_lse = plan.ws_bytes ? (float*)((char*)workspace + plan.ws_o_bytes) : nullptr;
     rc = attn::launch_paged(a, plan, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
+                   const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                   int block_size, void* o, float* lse,
+                   int num_seqs, int H, int d, float scale, int max_blocks_per_seq,
+                   int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                   attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, H,
+                              d, scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len,
+                              dtype, workspace, workspace_bytes, stream);
 }
 
 int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_table,

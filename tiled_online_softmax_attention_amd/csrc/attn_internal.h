@@ -16,10 +16,11 @@ struct PrefillArgs {
     void* o;
     float* lse;
     int B, H, N, d;
+    int H_kv;       // K/V heads (H a multiple of H_kv; query head h reads K/V head h / (H / H_kv))
     float scale;
     int causal;
     int dtype;      // 0 bf16, 1 fp32
-    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t (qb == 1 only)
+    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t
     int n_work;     // filled by the launcher
 };
 
@@ -29,6 +30,8 @@ struct PagedPlan {
     int split_tokens;    // keys per context split (multiple of the page size)
     int max_splits;      // ceil(max_ctx_len / split_tokens)
     int nqt;             // query tiles per request (chunk path)
+    int gc;              // decode path: query heads per workgroup (they share one K/V head)
+    int n_chunks;        // decode path: workgroups per K/V head (= (H / H_kv) / gc)
     size_t ws_o_bytes;   // fp32 partial outputs
     size_t ws_lse_bytes; // fp32 partial log-sum-exps
     size_t ws_bytes;     // total (0 when max_splits == 1)
@@ -45,6 +48,8 @@ struct PagedArgs {
     void* o;
     float* lse;
     int num_seqs, H, d;
+    int H_kv;                  // K/V heads in the pool
+    int n_chunks;              // decode path: workgroups per K/V head (from the plan)
     float scale;
     int max_blocks_per_seq;
     int64_t kv_block_stride;   // elements
@@ -68,9 +73,10 @@ struct GatherArgs {
     void* v_out;
 };
 
-constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode kernel
+constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode kernel ...
+constexpr int kDecodeMfmaGroup = 8; // ... unless this many query heads share a K/V head
 
-PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len);
+PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len);
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream);
 int launch_paged(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream);

@@ -22,24 +22,33 @@
 
 namespace attn {
 
-// One query tile's problem, resolved per workgroup.
+// One query tile's problem, resolved per workgroup.  Tile row t is query
+// position t / rows_per_pos and, within it, head t % rows_per_pos: the rows
+// of the query heads that share one K/V head (grouped-query attention) sit
+// side by side, so each K/V tile staged in LDS serves all of them.  With one
+// row per position it is an ordinary query tile of one head.
 struct TileProblem {
     const char* q;       // query row 0 of the tile (bytes)
-    int64_t q_stride;    // bytes between query rows
+    int64_t q_stride;    // bytes between query positions
+    int64_t q_hstride;   // bytes between the heads of one position
+    int rows_per_pos;    // heads per position in the tile (>= 1)
     int n_rows;          // valid query rows in this tile
-    int q_pos0;          // position of query row 0: row i may see keys
-                         // < min(kv_end, q_pos0 + i + 1) when causal
+    int q_pos0;          // position of row 0: a row at position p may see keys
+                         // < min(kv_end, q_pos0 + p + 1) when causal
     int causal;
     int kv_begin;        // keys [kv_begin, kv_end) are this workgroup's share
     int kv_end;
 };
 
 // Output writer: normalised bf16 rows, or fp32 rows + lse for split partials.
+// Rows are addressed like the query rows (position, head).
 struct TileOut {
     char* o;             // output row 0 of the tile (bytes)
-    int64_t o_stride;    // bytes between output rows
+    int64_t o_stride;    // bytes between positions
+    int64_t o_hstride;   // bytes between heads of one position
     float* lse;          // lse of row 0 (may be null)
-    int64_t lse_stride;  // floats between rows
+    int64_t lse_stride;  // floats between positions
+    int64_t lse_hstride; // floats between heads of one position
     int fp32_out;        // 1: write fp32 normalised O (partials), 0: bf16
 };
 
@@ -137,6 +146,44 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
     pv_tile(ws, pk, buf + C::TILE_BYTES, cx.lane);
 }
 
+// The key loop of one wave: tiles [0, n_full) unmasked, the rest masked.
+// COMPUTE false: the wave only copies its share of every tile and joins the
+// barriers (it has no valid query row).
+template <int D, bool COMPUTE, class KV>
+__device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
+                                         const KV& kv, const TileBuffers& buf, int n_full)
+{
+    using C = TileCfg<D>;
+    // Tile j lives in buffer j % 2.  Its copies are issued while tile j - 1 is
+    // being consumed; "wait for my copies, then barrier" publishes it.
+    if (cx.ntile > 0) {
+        issue_tile_copies<D>(kv, cx, buf.b0, cx.kv_begin);
+        publish_copies();
+    }
+    int j = 0;
+    for (; j + 2 <= n_full; j += 2) {
+        const int kb0 = cx.kv_begin + j * C::BN;
+        issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b0, kb0);
+        publish_copies();
+        if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN);
+        publish_copies();
+    }
+    // j is even here, so tile j is in buffer 0
+    for (; j < cx.ntile; j += 2) {
+        const int kb0 = cx.kv_begin + j * C::BN;
+        if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b0, kb0);
+        publish_copies();
+        if (j + 1 < cx.ntile) {
+            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+            if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN);
+            publish_copies();
+        }
+    }
+}
+
 template <int D, class KV>
 __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
                                                const TileBuffers& buf)
@@ -152,19 +199,22 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     const int g = cx.lane >> 5, r32 = cx.lane & 31;
     cx.w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int qrow = cx.w * 32 + r32;        // this lane's query row in the tile
+    const int qpos = qrow / P.rows_per_pos, qhead = qrow % P.rows_per_pos;
+    const int64_t qoff = qpos * P.q_stride + qhead * P.q_hstride;
 
     // ---- Q^T fragments, key limit ---------------------------------------------
     bf16x8 qf[C::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
         u32x4 val = {0u, 0u, 0u, 0u};
-        if (qrow < P.n_rows) val = *(const u32x4*)(P.q + qrow * P.q_stride + (ks * 2 + g) * 16);
+        if (qrow < P.n_rows) val = *(const u32x4*)(P.q + qoff + (ks * 2 + g) * 16);
         qf[ks] = as_bf16x8(val);
     }
     // rows past n_rows run on zero queries and are never stored
-    cx.q_lim = P.causal ? min(P.kv_end, P.q_pos0 + qrow + 1) : P.kv_end;
+    cx.q_lim = P.causal ? min(P.kv_end, P.q_pos0 + qpos + 1) : P.kv_end;
     // keys the whole tile needs
-    const int t_end = P.causal ? min(P.kv_end, P.q_pos0 + P.n_rows) : P.kv_end;
+    const int t_end =
+        P.causal ? min(P.kv_end, P.q_pos0 + (max(P.n_rows, 1) - 1) / P.rows_per_pos + 1) : P.kv_end;
     cx.kv_begin = P.kv_begin;
     cx.kv_end = P.kv_end;
     cx.ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
@@ -190,41 +240,17 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
         const int lim = P.causal ? min(P.kv_end, P.q_pos0 + 1) : P.kv_end;
         if (lim > P.kv_begin) n_full = min(cx.ntile, (lim - P.kv_begin) / C::BN);
     }
-    // Tile j lives in buffer j % 2.  Its copies are issued while tile j - 1 is
-    // being consumed; "wait for my copies, then barrier" publishes it.
-    if (cx.ntile > 0) {
-        issue_tile_copies<D>(kv, cx, buf.b0, cx.kv_begin);
-        publish_copies();
-    }
-    int j = 0;
-    for (; j + 2 <= n_full; j += 2) {
-        const int kb0 = cx.kv_begin + j * C::BN;
-        issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
-        tile_step<D, false>(ws, qf, cx, buf.b0, kb0);
-        publish_copies();
-        if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
-        tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN);
-        publish_copies();
-    }
-    // j is even here, so tile j is in buffer 0
-    for (; j < cx.ntile; j += 2) {
-        const int kb0 = cx.kv_begin + j * C::BN;
-        if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
-        tile_step<D, true>(ws, qf, cx, buf.b0, kb0);
-        publish_copies();
-        if (j + 1 < cx.ntile) {
-            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
-            tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN);
-            publish_copies();
-        }
-    }
+    // Waves with no valid row (the tail of a partial tile, or the rows past a
+    // short grouped-query tile) only take part in the copies and barriers.
+    if (cx.w * 32 < P.n_rows) key_loop<D, true>(ws, qf, cx, kv, buf, n_full);
+    else key_loop<D, false>(ws, qf, cx, kv, buf, n_full);
 
     // ---- epilogue -------------------------------------------------------------
     const float l_tot = half_sum(ws.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < P.n_rows) {
         if (out.fp32_out) {
-            float* orow = (float*)(out.o + qrow * out.o_stride);
+            float* orow = (float*)(out.o + qpos * out.o_stride + qhead * out.o_hstride);
 #pragma unroll
             for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -237,7 +263,7 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
                     *(f32x4*)(orow + db * 32 + a * 8 + g * 4) = v4;
                 }
         } else {
-            char* orow = out.o + qrow * out.o_stride;
+            char* orow = out.o + qpos * out.o_stride + qhead * out.o_hstride;
 #pragma unroll
             for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
@@ -250,7 +276,8 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
         }
         if (out.lse && g == 0) {
             const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * cx.c2;
-            out.lse[qrow * out.lse_stride] = (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
+            out.lse[qpos * out.lse_stride + qhead * out.lse_hstride] =
+                (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }

@@ -87,30 +87,35 @@ __device__ __forceinline__ int64_t prefix_len(const int32_t* lens, int r, int la
 }
 
 // ============================================================================
-// Decode kernel: one workgroup (4 waves) per (request, query row, head, split).
-// Lanes are grouped by LPR = d/8: a group of LPR lanes holds one token row of
-// a page (16 bytes = 8 channels per lane), so each 16-byte-per-lane load covers
-// 64/LPR consecutive tokens.  q.k uses bf16 dot2 on the raw pairs; the group
-// reduction is DPP; the wave takes pages w, w+4, ... of the split with the next
-// page's loads in flight while the current page is consumed; the four waves'
-// partial (m, l, o) are merged through LDS.
+// Decode kernel: one workgroup (4 waves) per (request, query row, K/V head,
+// group of GC query heads, split).  The GC query heads share that K/V head
+// (grouped-query attention; GC = 1 for plain multi-head attention), so every
+// K/V page is read once for all of them.  Lanes are grouped by LPR = d/8: a
+// group of LPR lanes holds one token row of a page (16 bytes = 8 channels per
+// lane), so each 16-byte-per-lane load covers 64/LPR consecutive tokens.  q.k
+// uses bf16 dot2 on the raw pairs; the group reduction is DPP; the wave takes
+// pages w, w+4, ... of the split with the next page's loads in flight while
+// the current page is consumed; the four waves' partial (m, l, o) of every
+// query head are merged through LDS.
 // ============================================================================
-template <int D, int BS>
+template <int D, int BS, int GC>
 __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 {
     constexpr int LPR = D / 8;
     constexpr int TPL = 64 / LPR;       // tokens per wave-load
     constexpr int LOADS = BS / TPL;     // loads per lane per page (each of K, V)
-    __shared__ float red_o[4][D];
-    __shared__ float red_ml[4][2];
+    __shared__ float red_o[4][GC][D];
+    __shared__ float red_ml[4][GC][2];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int sub = lane / LPR, oct = lane % LPR;
     int bid = blockIdx.x;
     const int split = bid % a.max_splits;
     bid /= a.max_splits;
-    const int h = bid % a.H;
-    bid /= a.H;
+    const int chunk = bid % a.n_chunks;
+    bid /= a.n_chunks;
+    const int hk = bid % a.H_kv;
+    bid /= a.H_kv;
     const int i = bid % a.max_q_len;
     const int r = bid / a.max_q_len;
     const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
@@ -122,17 +127,25 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
     const int kbeg = split * S, kend = min(kbeg + S, lim);
     const int64_t row = prefix_len(a.q_lens, r, lane) + i;
     const float c2 = a.scale * kLog2e;
+    const int h0 = hk * (a.H / a.H_kv) + chunk * GC;   // first query head of this workgroup
 
-    const bf16x8 qb = as_bf16x8(*(const u32x4*)((const char*)a.q + ((row * a.H + h) * D + oct * 8) * 2));
+    bf16x8 qb[GC];
+#pragma unroll
+    for (int g = 0; g < GC; ++g)
+        qb[g] = as_bf16x8(*(const u32x4*)((const char*)a.q + ((row * a.H + h0 + g) * D + oct * 8) * 2));
     const int32_t* table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
     const int64_t blk_bytes = a.kv_block_stride * 2;
-    const char* kbase = (const char*)a.k_pool + (int64_t)h * BS * D * 2 + oct * 16;
-    const char* vbase = (const char*)a.v_pool + (int64_t)h * BS * D * 2 + oct * 16;
+    const char* kbase = (const char*)a.k_pool + (int64_t)hk * BS * D * 2 + oct * 16;
+    const char* vbase = (const char*)a.v_pool + (int64_t)hk * BS * D * 2 + oct * 16;
 
-    float m = -INFINITY, l = 0.f;
-    float o[8];
+    float m[GC], l[GC], o[GC][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    for (int g = 0; g < GC; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    }
 
     const int pbeg = kbeg / BS;
     const int pend = (kend > kbeg) ? (kend + BS - 1) / BS : pbeg;
@@ -160,99 +173,108 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
                 vn[j] = *(const u32x4*)(vp + (j * TPL + sub) * D * 2);
             }
         }
-        // scores of this lane group's tokens
-        float s[LOADS];
+        // scores of this lane group's tokens, for every query head
         const bool tail = (p + 1) * BS > kend;
+        bool dead[LOADS];
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            s[j] = group_sum<LPR>(dot8_bf16(qb, as_bf16x8(kr[j])));
-            if (tail) {
-                const int t = p * BS + j * TPL + sub;
-                if (t >= kend) {
-                    s[j] = -INFINITY;
-                    vr[j] = u32x4{0u, 0u, 0u, 0u};
+            dead[j] = tail && (p * BS + j * TPL + sub >= kend);
+            if (dead[j]) vr[j] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int g = 0; g < GC; ++g) {
+            float s[LOADS];
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                s[j] = group_sum<LPR>(dot8_bf16(qb[g], as_bf16x8(kr[j])));
+                if (dead[j]) s[j] = -INFINITY;
+            }
+            float mt = s[0];
+#pragma unroll
+            for (int j = 1; j < LOADS; ++j) mt = fmaxf(mt, s[j]);
+#pragma unroll
+            for (int x = LPR; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x, 64));
+            const float m_new = fmaxf(m[g], mt);        // finite: every page has a visible key
+            const float ms_new = m_new * c2;
+            const float alpha = (m[g] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[g] * c2 - ms_new);
+            m[g] = m_new;
+            float ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[g][e] *= alpha;
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j) {
+                const float pj = dead[j] ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -ms_new));
+                ps += pj;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[g][2 * e] = __builtin_fmaf(pj, bf16lo(vr[j][e]), o[g][2 * e]);
+                    o[g][2 * e + 1] = __builtin_fmaf(pj, bf16hi(vr[j][e]), o[g][2 * e + 1]);
                 }
             }
+            l[g] = l[g] * alpha + ps;
         }
-        float mt = s[0];
-#pragma unroll
-        for (int j = 1; j < LOADS; ++j) mt = fmaxf(mt, s[j]);
-#pragma unroll
-        for (int x = LPR; x < 64; x <<= 1) mt = fmaxf(mt, __shfl_xor(mt, x, 64));
-        const float m_new = fmaxf(m, mt);            // finite: every page has a visible key
-        const float ms_new = m_new * c2;
-        const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m * c2 - ms_new);
-        m = m_new;
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] *= alpha;
-#pragma unroll
-        for (int j = 0; j < LOADS; ++j) {
-            const float pj = (s[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[j], c2, -ms_new));
-            ps += pj;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                o[2 * e] = __builtin_fmaf(pj, bf16lo(vr[j][e]), o[2 * e]);
-                o[2 * e + 1] = __builtin_fmaf(pj, bf16hi(vr[j][e]), o[2 * e + 1]);
-            }
-        }
-        l = l * alpha + ps;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
             kr[j] = kn[j];
             vr[j] = vn[j];
         }
     }
-    // merge the lane groups of this wave (same channels, different tokens)
+    // merge the lane groups of this wave (same channels, different tokens),
+    // then the four waves through LDS
 #pragma unroll
-    for (int x = LPR; x < 64; x <<= 1) {
-        l += __shfl_xor(l, x, 64);
+    for (int g = 0; g < GC; ++g) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], x, 64);
-    }
-    // merge the four waves
-    if (sub == 0) {
+        for (int x = LPR; x < 64; x <<= 1) {
+            l[g] += __shfl_xor(l[g], x, 64);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red_o[w][oct * 8 + e] = o[e];
-    }
-    if (lane == 0) {
-        red_ml[w][0] = m;
-        red_ml[w][1] = l;
+            for (int e = 0; e < 8; ++e) o[g][e] += __shfl_xor(o[g][e], x, 64);
+        }
+        if (sub == 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_o[w][g][oct * 8 + e] = o[g][e];
+        }
+        if (lane == 0) {
+            red_ml[w][g][0] = m[g];
+            red_ml[w][g][1] = l[g];
+        }
     }
     __syncthreads();
     if (w != 0) return;
-    float M = -INFINITY;
+    for (int g = 0; g < GC; ++g) {
+        float M = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) M = fmaxf(M, red_ml[x][0]);
-    const float Ms = (M == -INFINITY) ? 0.f : M * c2;
-    float sc[4], L = 0.f;
+        for (int x = 0; x < 4; ++x) M = fmaxf(M, red_ml[x][g][0]);
+        const float Ms = (M == -INFINITY) ? 0.f : M * c2;
+        float sc[4], L = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        sc[x] = (red_ml[x][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_ml[x][0] * c2 - Ms);
-        L += sc[x] * red_ml[x][1];
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float lse = L > 0.f ? (Ms + __log2f(L)) * kLn2 : -INFINITY;
-    // lane c writes channels c and c + 64 (d = 64 or 128)
-    if (nsplit == 1) {
-        __bf16* orow = (__bf16*)a.o + (row * a.H + h) * D;
-        for (int c = lane; c < D; c += 64) {
-            float acc = 0.f;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][c];
-            orow[c] = (__bf16)(acc * inv);
+        for (int x = 0; x < 4; ++x) {
+            sc[x] = (red_ml[x][g][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(red_ml[x][g][0] * c2 - Ms);
+            L += sc[x] * red_ml[x][g][1];
         }
-        if (a.lse && lane == 0) a.lse[row * a.H + h] = lse;
-    } else {
-        const int64_t slot = (((int64_t)r * a.max_q_len + i) * a.H + h) * a.max_splits + split;
-        float* wo = a.ws_o + slot * D;
-        for (int c = lane; c < D; c += 64) {
-            float acc = 0.f;
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float lse = L > 0.f ? (Ms + __log2f(L)) * kLn2 : -INFINITY;
+        const int h = h0 + g;
+        // lane c writes channels c and c + 64 (d = 64 or 128)
+        if (nsplit == 1) {
+            __bf16* orow = (__bf16*)a.o + (row * a.H + h) * D;
+            for (int c = lane; c < D; c += 64) {
+                float acc = 0.f;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][c];
-            wo[c] = acc * inv;
+                for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][g][c];
+                orow[c] = (__bf16)(acc * inv);
+            }
+            if (a.lse && lane == 0) a.lse[row * a.H + h] = lse;
+        } else {
+            const int64_t slot = (((int64_t)r * a.max_q_len + i) * a.H + h) * a.max_splits + split;
+            float* wo = a.ws_o + slot * D;
+            for (int c = lane; c < D; c += 64) {
+                float acc = 0.f;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc += sc[x] * red_o[x][g][c];
+                wo[c] = acc * inv;
+            }
+            if (lane == 0) a.ws_lse[slot] = lse;
         }
-        if (lane == 0) a.ws_lse[slot] = lse;
     }
 }
 
@@ -288,55 +310,65 @@ template <int D, int BS>
 __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work)
 {
     using C = TileCfg<D>;
-    constexpr int BM = kTileRows;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
     const TileBuffers buf{lds0, lds1};
+    // A tile holds ppt query positions x G query heads (the heads of one K/V
+    // group), so each K/V tile staged in LDS serves the whole group.
+    const int G = a.H / a.H_kv;
+    const int ppt = kTileRows / G;                     // positions per tile
     const int per = gridDim.x >> 3;
     int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (L >= n_work) return;
-    const int nqt = (a.max_q_len + BM - 1) / BM;
+    const int nqt = (a.max_q_len + ppt - 1) / ppt;
     const int qt = L % nqt;
     L /= nqt;
     const int split = L % a.max_splits;
     L /= a.max_splits;
-    const int h = L % a.H;
-    const int r = L / a.H;
+    const int hk = L % a.H_kv;
+    const int r = L / a.H_kv;
     const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
-    if (qt * BM >= ql) return;
+    if (qt * ppt >= ql) return;
     const int S = a.split_tokens;
     const int nsplit = (ctx + S - 1) / S;
     if (split >= nsplit) return;
     const int lane = threadIdx.x & 63;
-    const int64_t row0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * BM;
+    const int64_t pos0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * ppt;   // packed row of the tile's first position
+    const int h0 = hk * G;                             // first query head of the group
 
     PagedKV<D, BS> kv;
-    kv.kbase = (const char*)a.k_pool + (int64_t)h * BS * D * 2;
-    kv.vbase = (const char*)a.v_pool + (int64_t)h * BS * D * 2;
+    kv.kbase = (const char*)a.k_pool + (int64_t)hk * BS * D * 2;
+    kv.vbase = (const char*)a.v_pool + (int64_t)hk * BS * D * 2;
     kv.table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
     kv.blk_bytes = a.kv_block_stride * 2;
 
     TileProblem P;
-    P.q = (const char*)a.q + (row0 * a.H + h) * D * 2;
+    P.q = (const char*)a.q + (pos0 * a.H + h0) * D * 2;
     P.q_stride = (int64_t)a.H * D * 2;
-    P.n_rows = min(BM, ql - qt * BM);
-    P.q_pos0 = ctx - ql + qt * BM;
+    P.q_hstride = D * 2;
+    P.rows_per_pos = G;
+    P.n_rows = min(ppt, ql - qt * ppt) * G;
+    P.q_pos0 = ctx - ql + qt * ppt;
     P.causal = 1;
     P.kv_begin = split * S;
     P.kv_end = min(ctx, (split + 1) * S);
     TileOut out;
     if (nsplit == 1) {
-        out.o = (char*)a.o + (row0 * a.H + h) * D * 2;
+        out.o = (char*)a.o + (pos0 * a.H + h0) * D * 2;
         out.o_stride = (int64_t)a.H * D * 2;
-        out.lse = a.lse ? a.lse + row0 * a.H + h : nullptr;
+        out.o_hstride = D * 2;
+        out.lse = a.lse ? a.lse + pos0 * a.H + h0 : nullptr;
         out.lse_stride = a.H;
+        out.lse_hstride = 1;
         out.fp32_out = 0;
     } else {
-        const int64_t slot = (((int64_t)r * a.max_q_len + qt * BM) * a.H + h) * a.max_splits + split;
+        const int64_t slot = (((int64_t)r * a.max_q_len + qt * ppt) * a.H + h0) * a.max_splits + split;
         out.o = (char*)(a.ws_o + slot * D);
         out.o_stride = (int64_t)a.H * a.max_splits * D * 4;
+        out.o_hstride = (int64_t)a.max_splits * D * 4;
         out.lse = a.ws_lse + slot;
         out.lse_stride = (int64_t)a.H * a.max_splits;
+        out.lse_hstride = a.max_splits;
         out.fp32_out = 1;
     }
     run_query_tile<D>(P, kv, out, a.scale * kLog2e, buf);
@@ -424,23 +456,45 @@ static int env_int(const char* name, int dflt)
     return atoi(s);
 }
 
-PagedPlan plan_paged(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
+PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len)
 {
     PagedPlan p{};
-    p.path = (max_q_len <= kDecodeMaxQ) ? 0 : 1;
+    const int G = H / H_kv;
+    // The vector decode kernel serves short queries of plain or lightly
+    // grouped heads; from groups of kDecodeMfmaGroup heads up, the group's
+    // rows make the MFMA tile kernel the better fit even for one query row.
+    p.path = (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup) ? 0 : 1;
+    const int env_path = env_int("ATTN_DECODE_PATH", -1);
+    if ((env_path == 0 && max_q_len <= kDecodeMaxQ) || env_path == 1) p.path = env_path;
     const int64_t rows = (int64_t)num_seqs * max_q_len;
+    // decode workgroups serve gc query heads of one K/V group (the largest of
+    // 8, 4, 2, 1 that divides the group; at most 4 with 32-token pages, whose
+    // in-flight page registers leave less room)
+    p.gc = 1;
+    for (int c = (block_size == 32 ? 4 : 8); c > 1; c >>= 1)
+        if (G % c == 0) {
+            p.gc = c;
+            break;
+        }
+    const int env_gc = env_int("ATTN_DECODE_GC", 0);
+    if (env_gc == 1 || env_gc == 2 || env_gc == 4 || env_gc == 8)
+        if (G % env_gc == 0 && !(block_size == 32 && env_gc == 8)) p.gc = env_gc;
+    p.n_chunks = G / p.gc;
     int S;
     if (p.path == 0) {
         // decode: 4 waves x 4 pages per split by default (measured best on the
         // 64-request, 16-token-page decode batch), halved while the batch
-        // would leave the chip short of workgroups
-        const int64_t items = rows * H;
+        // would leave the chip short of workgroups; a workgroup serving
+        // several query heads keeps at least 2 pages per wave
+        const int64_t items = rows * H_kv * p.n_chunks;
         S = 4 * block_size * 4;
-        while (S > 4 * block_size && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
+        const int s_min = (p.gc > 1 ? 2 : 1) * 4 * block_size;
+        while (S > s_min && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         p.nqt = 1;
     } else {
-        p.nqt = (max_q_len + kTileRows - 1) / kTileRows;
-        const int64_t items = (int64_t)num_seqs * p.nqt * H;
+        const int ppt = kTileRows / G;                 // query positions per tile
+        p.nqt = (max_q_len + ppt - 1) / ppt;
+        const int64_t items = (int64_t)num_seqs * p.nqt * H_kv;
         S = 8192;
         while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < 2048) S /= 2;
     }
@@ -466,10 +520,14 @@ template <int D, int BS>
 static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
 {
     if (plan.path == 0) {
-        const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H * a.max_splits;
-        hipLaunchKernelGGL((paged_decode_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+        const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H_kv * plan.n_chunks * a.max_splits;
+        const dim3 g((unsigned)grid), b(256);
+        if (plan.gc == 8) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 8>), g, b, 0, stream, a);
+        else if (plan.gc == 4) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 4>), g, b, 0, stream, a);
+        else if (plan.gc == 2) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 2>), g, b, 0, stream, a);
+        else hipLaunchKernelGGL((paged_decode_kernel<D, BS, 1>), g, b, 0, stream, a);
     } else {
-        const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H * a.max_splits;
+        const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H_kv * a.max_splits;
         const int64_t grid = (n_work + 7) / 8 * 8;
         hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a, (int)n_work);
     }

@@ -56,8 +56,10 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
     const int nqt = (a.N + BM - 1) / BM;
     const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
     const int bh = L / per_bh, t = L % per_bh;
-    const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes
-    ContigKV<D> kv{(const char*)a.k + head_off, (const char*)a.v + head_off, (uint32_t)a.N * (uint32_t)(D * 2)};
+    const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes, q and o
+    const int64_t kv_off =                                 // bytes, k and v of this head's K/V head
+        ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * a.N * D * 2;
+    ContigKV<D> kv{(const char*)a.k + kv_off, (const char*)a.v + kv_off, (uint32_t)a.N * (uint32_t)(D * 2)};
     const float c2 = a.scale * kLog2e;
 
     int tiles[2];
@@ -74,6 +76,8 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
         TileProblem P;
         P.q = (const char*)a.q + head_off + (int64_t)q0 * D * 2;
         P.q_stride = D * 2;
+        P.q_hstride = 0;
+        P.rows_per_pos = 1;
         P.n_rows = min(BM, a.N - q0);
         P.q_pos0 = q0;
         P.causal = a.causal;
@@ -82,6 +86,8 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
         TileOut out;
         out.o = (char*)a.o + head_off + (int64_t)q0 * D * 2;
         out.o_stride = D * 2;
+        out.o_hstride = 0;
+        out.lse_hstride = 0;
         out.lse = a.lse ? a.lse + (int64_t)bh * a.N + q0 : nullptr;
         out.lse_stride = 1;
         out.fp32_out = 0;
@@ -104,9 +110,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a)
     const int tid = threadIdx.x, row = tid >> 2, part = tid & 3;
     const int q0 = qt * BM, qi = q0 + row;
     const int64_t head = (int64_t)bh * a.N * D;
+    const int64_t kv_head = ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * a.N * D;
     const float* qp = (const float*)a.q + head;
-    const float* kp = (const float*)a.k + head;
-    const float* vp = (const float*)a.v + head;
+    const float* kp = (const float*)a.k + kv_head;
+    const float* vp = (const float*)a.v + kv_head;
     const float c2 = a.scale * kLog2e;
 
     float qv[SUB], acc[SUB];

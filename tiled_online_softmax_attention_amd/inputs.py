@@ -38,6 +38,7 @@ class PrefillConfig:
     causal: bool
     seed: int
     tile: int | None = None  # key-tile size the workload names, if any
+    H_kv: int | None = None  # K/V heads (grouped-query attention); None = H
 
     @property
     def scale(self) -> float:
@@ -57,6 +58,7 @@ class PagedConfig:
     prefix_draw: bool    # True: draw the existing context, ctx = drawn + q_len
     seed: int
     dtype: torch.dtype = torch.bfloat16
+    H_kv: int | None = None  # K/V heads in the pool (grouped-query attention); None = H
 
     @property
     def scale(self) -> float:
@@ -70,6 +72,15 @@ C2 = PrefillConfig("c2_causal_bf16_1x32x2048x128", 1, 32, 2048, 128, torch.bfloa
 C3 = PrefillConfig("c3_causal_bf16_16x32x8192x128", 16, 32, 8192, 128, torch.bfloat16, True, 3)
 C4 = PagedConfig("c4_paged_decode_64req_ctx512-16384_bs16", 64, 1, 32, 128, 16, 512, 16384, False, 4)
 C5 = PagedConfig("c5_paged_chunk_8x512_prev4096-32768_bs32", 8, 512, 32, 128, 32, 4096, 32768, True, 5)
+
+# Grouped-query variants of the long prefill and the decode batch: 32 query
+# heads sharing 4 K/V heads (groups of 8, the grouping of the GQA example of
+# "Sequence length doubles, inference time quadruples"); same seeds, so the
+# decode variant draws C4's context lengths.
+C3_GQA8 = PrefillConfig("c3_gqa8_causal_bf16_16x32x8192x128_kv4", 16, 32, 8192, 128, torch.bfloat16, True, 3,
+                        H_kv=4)
+C4_GQA8 = PagedConfig("c4_gqa8_paged_decode_64req_ctx512-16384_bs16_kv4", 64, 1, 32, 128, 16, 512, 16384, False, 4,
+                      H_kv=4)
 
 CONFIGS = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5}
 
@@ -93,15 +104,16 @@ def device_generator(seed: int, device) -> torch.Generator:
 
 
 def prefill_inputs(cfg: PrefillConfig, device="cpu", B=None, H=None, N=None, seed=None):
-    """q, k, v of shape [B, H, N, d] (overrides allow smaller variants)."""
+    """q of shape [B, H, N, d] and k, v of shape [B, H_kv, N, d] (H_kv = H
+    unless the config names fewer K/V heads; overrides allow smaller variants)."""
     B = cfg.B if B is None else B
     H = cfg.H if H is None else H
     N = cfg.N if N is None else N
+    H_kv = H if cfg.H_kv is None else cfg.H_kv
     g = device_generator(cfg.seed if seed is None else seed, device)
-    shape = (B, H, N, cfg.d)
-    q = _randn(shape, g, device, cfg.dtype)
-    k = _randn(shape, g, device, cfg.dtype)
-    v = _randn(shape, g, device, cfg.dtype)
+    q = _randn((B, H, N, cfg.d), g, device, cfg.dtype)
+    k = _randn((B, H_kv, N, cfg.d), g, device, cfg.dtype)
+    v = _randn((B, H_kv, N, cfg.d), g, device, cfg.dtype)
     return q, k, v
 
 
@@ -159,9 +171,10 @@ def draw_lengths(cfg: PagedConfig, num_seqs=None, ctx_lo=None, ctx_hi=None):
 
 
 def build_paged(ctx_lens, q_lens, H, d, block_size, seed, device="cpu", dtype=torch.bfloat16,
-                cpu_gen=None, spare_frac=0.01, poison=True, max_blocks_per_seq=None, extra_blocks=0):
-    """Lay out a scattered paged KV pool for the given lengths (plus
-    extra_blocks unused blocks on top of the ~spare_frac spares)."""
+                cpu_gen=None, spare_frac=0.01, poison=True, max_blocks_per_seq=None, extra_blocks=0, H_q=None):
+    """Lay out a scattered paged KV pool of H heads for the given lengths (plus
+    extra_blocks unused blocks on top of the ~spare_frac spares); q gets H_q
+    heads (default H; more for grouped-query attention)."""
     ctx_lens = torch.as_tensor(ctx_lens, dtype=torch.int32).cpu()
     q_lens = torch.as_tensor(q_lens, dtype=torch.int32).cpu()
     if cpu_gen is None:
@@ -182,7 +195,7 @@ def build_paged(ctx_lens, q_lens, H, d, block_size, seed, device="cpu", dtype=to
 
     g = device_generator(seed, device)
     pool = _randn((num_blocks, 2, H, block_size, d), g, device, dtype)
-    q = _randn((int(q_lens.sum()), H, d), g, device, dtype)
+    q = _randn((int(q_lens.sum()), H if H_q is None else H_q, d), g, device, dtype)
     if poison:
         nan = float("nan")
         if spare_ids:
@@ -199,8 +212,9 @@ def build_paged(ctx_lens, q_lens, H, d, block_size, seed, device="cpu", dtype=to
 
 def paged_inputs(cfg: PagedConfig, device="cpu", num_seqs=None, ctx_lo=None, ctx_hi=None, H=None):
     ctx, ql, g = draw_lengths(cfg, num_seqs, ctx_lo, ctx_hi)
-    return build_paged(ctx, ql, cfg.H if H is None else H, cfg.d, cfg.block_size, cfg.seed, device,
-                       cfg.dtype, cpu_gen=g)
+    H = cfg.H if H is None else H
+    H_kv = H if cfg.H_kv is None else cfg.H_kv
+    return build_paged(ctx, ql, H_kv, cfg.d, cfg.block_size, cfg.seed, device, cfg.dtype, cpu_gen=g, H_q=H)
 
 
 @dataclass
