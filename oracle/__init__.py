@@ -23,6 +23,12 @@ passage of the source pages it follows, is stated in the C file's comments:
 * ``tiled_online``         -- the ipipp.com page's block-wise online-softmax
                               forward, in fp64, for the online == two-pass pin.
 * ``lse_merge``            -- merge of partial (O_s, lse_s) over a key partition.
+* ``attention_bwd``        -- gradients dQ, dK, dV of ``attention`` for a given
+                              output gradient dO (chain rule through the three
+                              forward steps; the ipipp.com page, section 2,
+                              names recomputing S and P in the backward).
+* ``attention_bwd_rows``   -- the same for sampled query rows (dQ) and key
+                              rows (dK, dV).
 
 The KV-append oracle (block allocator and per-token page writes) is plain
 Python in ``oracle/kv_cache.py``.
@@ -70,8 +76,12 @@ def _declare(lib):
     lib.oracle_paged_gather.argtypes = [P, I, P, P, I, I, I, I, I, I, P, P]
     lib.oracle_tiled_online.argtypes = [P, P, P, I, I, I, I, D, I, I, P, P]
     lib.oracle_lse_merge.argtypes = [I, I, P, P, P, P]
+    lib.oracle_attention_bwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, I, P, P, P]
+    lib.oracle_attention_bwd_rows.argtypes = [P, P, P, P, I, I, I, I, I, I, I, D, I,
+                                              I, P, P, P, P, I, P, P, P, P, P]
     lib.oracle_num_threads.argtypes = []
-    for name in ("oracle_attention", "oracle_attention_rows", "oracle_paged_attention",
+    for name in ("oracle_attention", "oracle_attention_rows", "oracle_attention_bwd", "oracle_attention_bwd_rows",
+                 "oracle_paged_attention",
                  "oracle_paged_attention_rows", "oracle_paged_gather", "oracle_tiled_online",
                  "oracle_lse_merge", "oracle_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
@@ -175,6 +185,52 @@ def attention_rows(q, k, v, scale: float, causal: bool, bidx, hidx, rows):
                                         1 if causal else 0, n, _ptr(bi), _ptr(hi), _ptr(ri), _ptr(o),
                                         _ptr(lse)), "attention_rows")
     return o, lse
+
+
+def _bwd_operands(q, k, v, do):
+    qa, dt = _host_array(q)
+    ka, dk = _host_array(k)
+    va, dv = _host_array(v)
+    oa, do_ = _host_array(do)
+    assert dt == dk == dv == do_ is not None
+    B, H, Nq, d = qa.shape
+    Hkv, Nk = ka.shape[1], ka.shape[2]
+    assert ka.shape == (B, Hkv, Nk, d) and va.shape == ka.shape and oa.shape == qa.shape
+    return qa, ka, va, oa, dt, B, H, Hkv, Nq, Nk, d
+
+
+def attention_bwd(q, k, v, do, scale: float, causal: bool = False):
+    """Gradients of ``attention`` for output gradient do ([B,H,Nq,d], same dtype
+    as q).  Returns (dq [B,H,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d]), fp64; a
+    K/V head's dk, dv sum over the query heads of its group."""
+    qa, ka, va, oa, dt, B, H, Hkv, Nq, Nk, d = _bwd_operands(q, k, v, do)
+    dq = np.empty((B, H, Nq, d), np.float64)
+    dk = np.empty((B, Hkv, Nk, d), np.float64)
+    dv = np.empty((B, Hkv, Nk, d), np.float64)
+    _check(load().oracle_attention_bwd(_ptr(qa), _ptr(ka), _ptr(va), _ptr(oa), dt, B, H, Hkv, Nq, Nk, d,
+                                       float(scale), 1 if causal else 0, _ptr(dq), _ptr(dk), _ptr(dv)),
+           "attention_bwd")
+    return dq, dk, dv
+
+
+def attention_bwd_rows(q, k, v, do, scale: float, causal: bool, q_samples=(), k_samples=()):
+    """Sampled rows of ``attention_bwd``: q_samples are (b, h, row) triples
+    (rows of dq), k_samples (b, h_kv, key) triples (rows of dk and dv).
+    Returns (dq_rows [nq,d], dk_rows [nk,d], dv_rows [nk,d]), fp64."""
+    qa, ka, va, oa, dt, B, H, Hkv, Nq, Nk, d = _bwd_operands(q, k, v, do)
+    qs = np.asarray(list(q_samples), dtype=np.int32).reshape(-1, 3)
+    ks = np.asarray(list(k_samples), dtype=np.int32).reshape(-1, 3)
+    qb, qh, qr = (np.ascontiguousarray(qs[:, i]) for i in range(3))
+    kb, kh, kr = (np.ascontiguousarray(ks[:, i]) for i in range(3))
+    dq = np.empty((len(qs), d), np.float64)
+    dk = np.empty((len(ks), d), np.float64)
+    dv = np.empty((len(ks), d), np.float64)
+    _check(load().oracle_attention_bwd_rows(_ptr(qa), _ptr(ka), _ptr(va), _ptr(oa), dt, B, H, Hkv, Nq, Nk, d,
+                                            float(scale), 1 if causal else 0,
+                                            len(qs), _ptr(qb), _ptr(qh), _ptr(qr), _ptr(dq),
+                                            len(ks), _ptr(kb), _ptr(kh), _ptr(kr), _ptr(dk), _ptr(dv)),
+           "attention_bwd_rows")
+    return dq, dk, dv
 
 
 def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float):

@@ -27,6 +27,10 @@
  *     max m and running sum l: oracle_tiled_online() follows that algorithm
  *     step by step in fp64 (plus the mask); it exists only to pin the online
  *     algebra against the two-pass definition.
+ *   - same ipipp.com page, section 2: the forward keeps the softmax statistics
+ *     so that the backward can recompute S and P.  oracle_attention_bwd()
+ *     gives the gradients dQ, dK, dV of the definition (chain rule through
+ *     the three steps of section 1; formulas at that function).
  *
  * Every result is the plain definition, materialised: the full masked score
  * matrix S (-inf outside the allowed set), a two-pass softmax P, then P V.
@@ -217,6 +221,226 @@ int oracle_attention_rows(const void* q, const void* k, const void* v, int dtype
         }
         free(Q); free(K); free(V); free(S); free(P);
     }
+    return err;
+}
+
+/* ---- backward ------------------------------------------------------------ */
+/*
+ * Gradients of the forward above with respect to Q, K and V, given the
+ * gradient dO of the output.  "Flash Attention and Paged Attention", section
+ * 2, keeps the softmax normalisation statistics from the forward so that the
+ * backward can recompute S and P instead of storing them; the pages give no
+ * formulas for the pass itself, so this is the chain rule through the three
+ * forward steps of section 1, for one head:
+ *   O = P V                  ->  dV = P^T dO,  dP = dO V^T
+ *   P = row-softmax(S)       ->  dS[i][j] = P[i][j] (dP[i][j] - D_i),
+ *                                D_i = sum_j P[i][j] dP[i][j]
+ *   S = scale Q K^T          ->  dQ = scale dS K,  dK = scale dS^T Q
+ * Masked keys have P = 0 and contribute nothing.  With Hkv < H a K/V head's
+ * dK and dV are the sums over the query heads of its group.  P is recomputed
+ * here by the plain two-pass softmax of the definition, not from saved
+ * statistics.
+ */
+
+/* One query row: its masked score row against all nk keys, the softmax p,
+ * and ds[j] = p[j] (dp[j] - D) with dp[j] = do_i . V[j], D = sum_j p[j] dp[j].
+ * o: d doubles of scratch (the row's output, unused here). */
+static void grad_row(const double* qi, const double* doi, const double* K, const double* V, int64_t nk, int d,
+                     double scale, int64_t lim, double* p, double* ds, double* o)
+{
+    attention_dense(qi, K, V, 1, nk, d, scale, &lim, ds /* scores; overwritten below */, p, o, NULL);
+    double D = 0.0;
+    for (int64_t j = 0; j < nk; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < d; ++c) acc += doi[c] * V[j * d + c];
+        ds[j] = acc;
+        D += p[j] * acc;
+    }
+    for (int64_t j = 0; j < nk; ++j) ds[j] = p[j] * (ds[j] - D);
+}
+
+/*
+ * Contiguous backward over [B,H,Nq,d] queries and output gradients dout and
+ * [B,Hkv,Nk,d] keys/values.  dq: fp64 [B,H,Nq,d]; dk, dv: fp64 [B,Hkv,Nk,d].
+ */
+int oracle_attention_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                         int B, int H, int Hkv, int Nq, int Nk, int d, double scale, int mask_mode,
+                         double* dq, double* dk, double* dv)
+{
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return ORACLE_ERR_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
+    if (dtype < ORACLE_BF16 || dtype > ORACLE_F64 || mask_mode < 0 || mask_mode > 1) return ORACLE_ERR_ARG;
+    const int G = H / Hkv;
+    int err = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bk = 0; bk < (int64_t)B * Hkv; ++bk) {
+        double* Q = malloc(sizeof(double) * (int64_t)Nq * d);
+        double* dO = malloc(sizeof(double) * (int64_t)Nq * d);
+        double* K = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* V = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* p = malloc(sizeof(double) * Nk);
+        double* ds = malloc(sizeof(double) * Nk);
+        double* o = malloc(sizeof(double) * d);
+        if (!Q || !dO || !K || !V || !p || !ds || !o) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ALLOC;
+        } else {
+            double* dK = dk + bk * Nk * d;
+            double* dV = dv + bk * Nk * d;
+            for (int64_t x = 0; x < (int64_t)Nk * d; ++x) dK[x] = dV[x] = 0.0;
+            load_head(k, dtype, bk, Nk, d, K);
+            load_head(v, dtype, bk, Nk, d, V);
+            const int64_t b = bk / Hkv, hk = bk % Hkv;
+            for (int gh = 0; gh < G; ++gh) {
+                const int64_t bh = b * H + hk * G + gh;
+                load_head(q, dtype, bh, Nq, d, Q);
+                load_head(dout, dtype, bh, Nq, d, dO);
+                for (int64_t i = 0; i < Nq; ++i) {
+                    const double* qi = Q + i * d;
+                    const double* doi = dO + i * d;
+                    grad_row(qi, doi, K, V, Nk, d, scale, allowed_keys(mask_mode, i, Nq, Nk), p, ds, o);
+                    double* dQ = dq + (bh * Nq + i) * d;
+                    for (int c = 0; c < d; ++c) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < Nk; ++j) acc += ds[j] * K[j * d + c];
+                        dQ[c] = scale * acc;
+                    }
+                    for (int64_t j = 0; j < Nk; ++j)
+                        for (int c = 0; c < d; ++c) {
+                            dK[j * d + c] += scale * ds[j] * qi[c];
+                            dV[j * d + c] += p[j] * doi[c];
+                        }
+                }
+            }
+        }
+        free(Q); free(dO); free(K); free(V); free(p); free(ds); free(o);
+    }
+    return err;
+}
+
+/*
+ * Selected rows of the backward, for workloads too large to evaluate whole.
+ *   dQ sample s: query row qrow[s] of head (qb[s], qh[s])        -> dq_rows [nq][d]
+ *   dK/dV sample s: key row krow[s] of K/V head (kb[s], khk[s])  -> dk_rows, dv_rows [nk][d]
+ * A key sample visits every query row of every query head of the group that
+ * may attend that key and materialises its full score row (its softmax needs
+ * all of it).  Query rows are split over threads in fixed contiguous ranges
+ * whose partial sums are added in thread order.
+ */
+int oracle_attention_bwd_rows(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                              int B, int H, int Hkv, int Nq, int Nk, int d, double scale, int mask_mode,
+                              int nq_s, const int* qb, const int* qh, const int* qrow, double* dq_rows,
+                              int nk_s, const int* kb, const int* khk, const int* krow, double* dk_rows,
+                              double* dv_rows)
+{
+    if (!q || !k || !v || !dout || nq_s < 0 || nk_s < 0) return ORACLE_ERR_ARG;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || Hkv < 1 || H % Hkv != 0) return ORACLE_ERR_ARG;
+    if (dtype < ORACLE_BF16 || dtype > ORACLE_F64 || mask_mode < 0 || mask_mode > 1) return ORACLE_ERR_ARG;
+    if (nq_s > 0 && (!qb || !qh || !qrow || !dq_rows)) return ORACLE_ERR_ARG;
+    if (nk_s > 0 && (!kb || !khk || !krow || !dk_rows || !dv_rows)) return ORACLE_ERR_ARG;
+    for (int s = 0; s < nq_s; ++s)
+        if (qb[s] < 0 || qb[s] >= B || qh[s] < 0 || qh[s] >= H || qrow[s] < 0 || qrow[s] >= Nq) return ORACLE_ERR_ARG;
+    for (int s = 0; s < nk_s; ++s)
+        if (kb[s] < 0 || kb[s] >= B || khk[s] < 0 || khk[s] >= Hkv || krow[s] < 0 || krow[s] >= Nk)
+            return ORACLE_ERR_ARG;
+    const int G = H / Hkv;
+    int err = ORACLE_OK;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int s = 0; s < nq_s; ++s) {
+        double* Q = malloc(sizeof(double) * d);
+        double* dO = malloc(sizeof(double) * d);
+        double* K = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* V = malloc(sizeof(double) * (int64_t)Nk * d);
+        double* p = malloc(sizeof(double) * Nk);
+        double* ds = malloc(sizeof(double) * Nk);
+        double* o = malloc(sizeof(double) * d);
+        if (!Q || !dO || !K || !V || !p || !ds || !o) {
+#pragma omp atomic write
+            err = ORACLE_ERR_ALLOC;
+        } else {
+            const int64_t bh = (int64_t)qb[s] * H + qh[s];
+            const int64_t bkv = (int64_t)qb[s] * Hkv + kv_head(qh[s], H, Hkv);
+            for (int c = 0; c < d; ++c) {
+                Q[c] = elem(q, dtype, (bh * Nq + qrow[s]) * d + c);
+                dO[c] = elem(dout, dtype, (bh * Nq + qrow[s]) * d + c);
+            }
+            load_head(k, dtype, bkv, Nk, d, K);
+            load_head(v, dtype, bkv, Nk, d, V);
+            grad_row(Q, dO, K, V, Nk, d, scale, allowed_keys(mask_mode, qrow[s], Nq, Nk), p, ds, o);
+            for (int c = 0; c < d; ++c) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < Nk; ++j) acc += ds[j] * K[j * d + c];
+                dq_rows[(int64_t)s * d + c] = scale * acc;
+            }
+        }
+        free(Q); free(dO); free(K); free(V); free(p); free(ds); free(o);
+    }
+    if (err) return err;
+
+    int nthr = 1;
+#ifdef _OPENMP
+    nthr = omp_get_max_threads();
+#endif
+    double* part = calloc((size_t)nthr * 2 * d, sizeof(double));
+    double* K = malloc(sizeof(double) * (int64_t)Nk * d);
+    double* V = malloc(sizeof(double) * (int64_t)Nk * d);
+    if (!part || !K || !V) err = ORACLE_ERR_ALLOC;
+    for (int s = 0; s < nk_s && !err; ++s) {
+        const int64_t bkv = (int64_t)kb[s] * Hkv + khk[s];
+        const int64_t j = krow[s];
+        load_head(k, dtype, bkv, Nk, d, K);
+        load_head(v, dtype, bkv, Nk, d, V);
+        for (int64_t x = 0; x < (int64_t)nthr * 2 * d; ++x) part[x] = 0.0;
+#pragma omp parallel num_threads(nthr)
+        {
+            int t = 0, nt = 1;
+#ifdef _OPENMP
+            t = omp_get_thread_num();
+            nt = omp_get_num_threads();
+#endif
+            double* acc_k = part + (int64_t)t * 2 * d;
+            double* acc_v = acc_k + d;
+            double* qi = malloc(sizeof(double) * d);
+            double* doi = malloc(sizeof(double) * d);
+            double* p = malloc(sizeof(double) * Nk);
+            double* ds = malloc(sizeof(double) * Nk);
+            double* o = malloc(sizeof(double) * d);
+            if (!qi || !doi || !p || !ds || !o) {
+#pragma omp atomic write
+                err = ORACLE_ERR_ALLOC;
+            } else {
+                const int64_t rows = (int64_t)G * Nq;
+                const int64_t lo = rows * t / nt, hi = rows * (t + 1) / nt;
+                for (int64_t x = lo; x < hi; ++x) {
+                    const int64_t gh = x / Nq, i = x % Nq;
+                    const int64_t lim = allowed_keys(mask_mode, i, Nq, Nk);
+                    if (j >= lim) continue;                  /* row i does not attend key j */
+                    const int64_t bh = (int64_t)kb[s] * H + (int64_t)khk[s] * G + gh;
+                    for (int c = 0; c < d; ++c) {
+                        qi[c] = elem(q, dtype, (bh * Nq + i) * d + c);
+                        doi[c] = elem(dout, dtype, (bh * Nq + i) * d + c);
+                    }
+                    grad_row(qi, doi, K, V, Nk, d, scale, lim, p, ds, o);
+                    for (int c = 0; c < d; ++c) {
+                        acc_k[c] += scale * ds[j] * qi[c];
+                        acc_v[c] += p[j] * doi[c];
+                    }
+                }
+            }
+            free(qi); free(doi); free(p); free(ds); free(o);
+        }
+        for (int c = 0; c < d; ++c) {
+            double sk = 0.0, sv = 0.0;
+            for (int t = 0; t < nthr; ++t) {
+                sk += part[(int64_t)t * 2 * d + c];
+                sv += part[(int64_t)t * 2 * d + d + c];
+            }
+            dk_rows[(int64_t)s * d + c] = sk;
+            dv_rows[(int64_t)s * d + c] = sv;
+        }
+    }
+    free(part); free(K); free(V);
     return err;
 }
 

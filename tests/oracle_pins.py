@@ -12,7 +12,13 @@ Each check raises AssertionError when the oracle disagrees with:
     the block-wise online algorithm equals the two-pass definition for every
     block size; partial results merged by LSE equal the unsplit row; the paged
     path equals the contiguous path bit for bit under any block permutation;
-    the gather copies bits exactly; poisoned slots are never read).
+    the gather copies bits exactly; poisoned slots are never read),
+  * for the backward (gradients dQ, dK, dV of the same definition): central
+    finite differences of the forward oracle; torch's fp64 autograd through an
+    explicitly written masked softmax; the closed form of a two-key softmax
+    (a logistic); and identities the gradients of this function obey at any
+    size (shift invariance of the softmax in K, P rows summing to one in V,
+    <V, dV> = <O, dO>, <Q, dQ> = <K, dK>).
 
 They are plain functions so that the same list can be run both against the
 real oracle (test_oracle_pins.py) and against deliberately broken copies of it
@@ -418,6 +424,155 @@ def check_gqa_paged_equals_contiguous():
         row += q_lens[r]
 
 
+# ---- backward ---------------------------------------------------------------
+
+def _loss(q, k, v, do, scale, causal):
+    o, _ = oracle.attention(q, k, v, scale, causal)
+    return float(np.sum(o * do))
+
+
+def check_bwd_finite_differences():
+    """Every gradient entry of L = sum(O * dO) against central differences of
+    the forward oracle (h = 1e-5; truncation and rounding error both far below
+    the 1e-7 tolerance at these magnitudes), square causal, bottom-right causal
+    (fewer queries than keys) and unmasked, with two query heads on one K/V
+    head."""
+    rng = _rng(40)
+    h = 1e-5
+    for (Nq, Nk, causal) in ((5, 5, True), (3, 6, True), (4, 5, False)):
+        B, H, Hkv, d, scale = 1, 2, 1, 3, 0.7
+        q = rng.standard_normal((B, H, Nq, d))
+        k = rng.standard_normal((B, Hkv, Nk, d))
+        v = rng.standard_normal((B, Hkv, Nk, d))
+        do = rng.standard_normal((B, H, Nq, d))
+        grads = oracle.attention_bwd(q, k, v, do, scale, causal)
+        for x, g in zip((q, k, v), grads):
+            for idx in np.ndindex(*x.shape):
+                keep = x[idx]
+                x[idx] = keep + h
+                up = _loss(q, k, v, do, scale, causal)
+                x[idx] = keep - h
+                dn = _loss(q, k, v, do, scale, causal)
+                x[idx] = keep
+                fd = (up - dn) / (2 * h)
+                assert abs(fd - g[idx]) < 1e-7, (Nq, Nk, causal, idx, fd, g[idx])
+
+
+def check_bwd_torch_autograd():
+    """Against torch's fp64 autograd of softmax(scale Q K^T + mask) V written
+    out explicitly (bottom-right causal mask as a boolean matrix, K/V heads
+    repeated for grouped-query attention, so dK and dV come back summed over
+    each group), for bf16 and fp32 stored inputs."""
+    rng = _rng(41)
+    for (B, H, Hkv, Nq, Nk, d, causal, dt) in ((2, 4, 2, 37, 37, 16, True, torch.bfloat16),
+                                                (1, 3, 3, 11, 29, 8, True, torch.float32),
+                                                (1, 4, 1, 13, 13, 8, False, torch.bfloat16),
+                                                (1, 6, 2, 9, 9, 4, True, torch.float64)):
+        scale = 1.0 / math.sqrt(d)
+        q = torch.from_numpy(rng.standard_normal((B, H, Nq, d))).to(dt)
+        k = torch.from_numpy(rng.standard_normal((B, Hkv, Nk, d))).to(dt)
+        v = torch.from_numpy(rng.standard_normal((B, Hkv, Nk, d))).to(dt)
+        do = torch.from_numpy(rng.standard_normal((B, H, Nq, d))).to(dt)
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, causal)
+        qq, kk, vv = (t.double().requires_grad_() for t in (q, k, v))
+        rep = H // Hkv
+        kr, vr = kk.repeat_interleave(rep, 1), vv.repeat_interleave(rep, 1)
+        s = torch.matmul(qq, kr.transpose(-1, -2)) * scale
+        if causal:
+            allowed = torch.arange(Nk)[None, :] <= torch.arange(Nq)[:, None] + (Nk - Nq)
+            s = s.masked_fill(~allowed, float("-inf"))
+        o = torch.matmul(torch.softmax(s, -1), vr)
+        o.backward(do.double())
+        for name, mine, ref in (("dq", dq, qq.grad), ("dk", dk, kk.grad), ("dv", dv, vv.grad)):
+            assert np.allclose(mine, ref.numpy(), rtol=0, atol=1e-12), (name, B, H, Hkv, Nq, Nk, causal, dt)
+
+
+def check_bwd_two_key_closed_form():
+    """One query, two keys: P = (1 - s, s) with s = logistic(t), t = scale
+    q.(k1 - k0), so O = v0 + s (v1 - v0) and, with s' = s (1 - s):
+    dV0 = (1 - s) dO, dV1 = s dO, dQ = s' (dO.(v1 - v0)) scale (k1 - k0),
+    dK1 = -dK0 = s' (dO.(v1 - v0)) scale q."""
+    rng = _rng(42)
+    d, scale = 5, 0.9
+    q = rng.standard_normal((1, 1, 1, d))
+    k = rng.standard_normal((1, 1, 2, d))
+    v = rng.standard_normal((1, 1, 2, d))
+    do = rng.standard_normal((1, 1, 1, d))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, scale, False)
+    q0, k0, k1, v0, v1, g = q[0, 0, 0], k[0, 0, 0], k[0, 0, 1], v[0, 0, 0], v[0, 0, 1], do[0, 0, 0]
+    t = scale * q0 @ (k1 - k0)
+    sg = 1.0 / (1.0 + math.exp(-t))
+    ds = sg * (1 - sg) * (g @ (v1 - v0))
+    tol = dict(rtol=0, atol=1e-14)
+    assert np.allclose(dv[0, 0, 0], (1 - sg) * g, **tol) and np.allclose(dv[0, 0, 1], sg * g, **tol)
+    assert np.allclose(dq[0, 0, 0], ds * scale * (k1 - k0), **tol)
+    assert np.allclose(dk[0, 0, 1], ds * scale * q0, **tol) and np.allclose(dk[0, 0, 0], -ds * scale * q0, **tol)
+
+
+def check_bwd_identities():
+    """Identities of the gradient at any size, per K/V head (its group of
+    query heads together):
+      sum_j dK_j = 0             (a common shift of all keys moves every
+                                  allowed score of a row by one constant)
+      sum_j dV_j = sum_i dO_i    (every P row sums to one)
+      <V, dV> = <O, dO>          (O is linear in V)
+      <Q, dQ> = <K, dK>          (scaling Q or K scales S alike)
+    plus: a causal row that sees one key has dQ = 0; constant V rows give
+    dQ = dK = 0; scale 0 gives dQ = dK = 0 and dV_j = sum over rows i that
+    see j of dO_i / (number of keys row i sees)."""
+    rng = _rng(43)
+    for (B, H, Hkv, Nq, Nk, d, causal) in ((2, 4, 2, 40, 40, 8, True), (1, 3, 1, 7, 33, 8, True),
+                                          (1, 2, 2, 21, 21, 16, False)):
+        q = rng.standard_normal((B, H, Nq, d))
+        k = rng.standard_normal((B, Hkv, Nk, d))
+        v = rng.standard_normal((B, Hkv, Nk, d))
+        do = rng.standard_normal((B, H, Nq, d))
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.5, causal)
+        o, _ = oracle.attention(q, k, v, 0.5, causal)
+        G = H // Hkv
+        for b in range(B):
+            for hk in range(Hkv):
+                hs = slice(hk * G, (hk + 1) * G)
+                assert np.allclose(dk[b, hk].sum(0), 0.0, rtol=0, atol=1e-11)
+                assert np.allclose(dv[b, hk].sum(0), do[b, hs].sum((0, 1)), rtol=0, atol=1e-11)
+                assert abs(np.sum(v[b, hk] * dv[b, hk]) - np.sum(o[b, hs] * do[b, hs])) < 1e-10
+                assert abs(np.sum(q[b, hs] * dq[b, hs]) - np.sum(k[b, hk] * dk[b, hk])) < 1e-10
+        if causal and Nq == Nk:
+            assert np.all(dq[:, :, 0] == 0.0)
+        vc = np.broadcast_to(rng.standard_normal((B, Hkv, 1, d)), v.shape).copy()
+        dq0, dk0, _ = oracle.attention_bwd(q, k, vc, do, 0.5, causal)
+        assert np.allclose(dq0, 0.0, rtol=0, atol=1e-12) and np.allclose(dk0, 0.0, rtol=0, atol=1e-12)
+        dqz, dkz, dvz = oracle.attention_bwd(q, k, v, do, 0.0, causal)
+        assert np.all(dqz == 0.0) and np.allclose(dkz, 0.0, rtol=0, atol=1e-15)
+        n_see = np.array([min(Nk, Nk - Nq + i + 1) if causal else Nk for i in range(Nq)], np.float64)
+        sees = np.array([[j < n_see[i] for j in range(Nk)] for i in range(Nq)], np.float64)   # [Nq, Nk]
+        for b in range(B):
+            for hk in range(Hkv):
+                ref = np.einsum("ij,hic->jc", sees / n_see[:, None], do[b, hk * G:(hk + 1) * G])
+                assert np.allclose(dvz[b, hk], ref, rtol=0, atol=1e-12)
+
+
+def check_bwd_rows_match_full():
+    """Sampled rows of the backward equal the full backward (grouped heads,
+    bottom-right causal, first/last rows and keys)."""
+    rng = _rng(44)
+    B, H, Hkv, Nq, Nk, d = 2, 6, 2, 9, 14, 8
+    q = rng.standard_normal((B, H, Nq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    do = rng.standard_normal((B, H, Nq, d))
+    for causal in (True, False):
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, 0.3, causal)
+        qs = [(0, 0, 0), (1, 5, Nq - 1), (1, 2, 4), (0, 3, 7)]
+        ks = [(0, 0, 0), (1, 1, Nk - 1), (0, 1, 6), (1, 0, 13), (1, 0, 2)]
+        rq, rk, rv = oracle.attention_bwd_rows(q, k, v, do, 0.3, causal, qs, ks)
+        for n, (b, h, i) in enumerate(qs):
+            assert np.allclose(rq[n], dq[b, h, i], rtol=0, atol=1e-13)
+        for n, (b, hk, j) in enumerate(ks):
+            assert np.allclose(rk[n], dk[b, hk, j], rtol=0, atol=1e-13)
+            assert np.allclose(rv[n], dv[b, hk, j], rtol=0, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_golden_fixtures,
     check_bruteforce_tiny,
@@ -434,4 +589,9 @@ ALL_CHECKS = [
     check_bf16_upcast_exact,
     check_gqa_torch_sdpa,
     check_gqa_paged_equals_contiguous,
+    check_bwd_finite_differences,
+    check_bwd_torch_autograd,
+    check_bwd_two_key_closed_form,
+    check_bwd_identities,
+    check_bwd_rows_match_full,
 ]

@@ -37,6 +37,29 @@ MUTANTS = [
     ("prefix_skips_request", "for (int i = 0; i < r; ++i) s += q_lens[i];", "for (int i = 1; i < r; ++i) s += q_lens[i];"),
     ("gqa_strided_groups", "static int kv_head(int h, int H, int Hkv) { return h / (H / Hkv); }",
      "static int kv_head(int h, int H, int Hkv) { return h % Hkv; }"),
+    # backward
+    ("bwd_dq_unscaled", "dQ[c] = scale * acc;", "dQ[c] = acc;"),
+    ("bwd_ds_sign", "for (int64_t j = 0; j < nk; ++j) ds[j] = p[j] * (ds[j] - D);",
+     "for (int64_t j = 0; j < nk; ++j) ds[j] = p[j] * (D - ds[j]);"),
+    ("bwd_ds_without_row_term", "for (int64_t j = 0; j < nk; ++j) ds[j] = p[j] * (ds[j] - D);",
+     "for (int64_t j = 0; j < nk; ++j) ds[j] = p[j] * ds[j];"),
+    ("bwd_dp_reads_k", "for (int c = 0; c < d; ++c) acc += doi[c] * V[j * d + c];",
+     "for (int c = 0; c < d; ++c) acc += doi[c] * K[j * d + c];"),
+    ("bwd_dv_uses_ds", "dV[j * d + c] += p[j] * doi[c];", "dV[j * d + c] += ds[j] * doi[c];"),
+    ("bwd_dk_wrong_operand", "dK[j * d + c] += scale * ds[j] * qi[c];", "dK[j * d + c] += scale * ds[j] * doi[c];"),
+    ("bwd_dk_unscaled", "dK[j * d + c] += scale * ds[j] * qi[c];", "dK[j * d + c] += ds[j] * qi[c];"),
+    ("bwd_dq_transposed", "for (int64_t j = 0; j < Nk; ++j) acc += ds[j] * K[j * d + c];\n                        dQ[c]",
+     "for (int64_t j = 0; j < Nk; ++j) acc += ds[j] * V[j * d + c];\n                        dQ[c]"),
+    ("bwd_group_strided", "const int64_t bh = b * H + hk * G + gh;", "const int64_t bh = b * H + gh * Hkv + hk;"),
+    ("bwd_group_not_summed", "for (int gh = 0; gh < G; ++gh) {\n                const int64_t bh = b * H",
+     "for (int gh = 0; gh < G; ++gh) {\n                for (int64_t x = 0; x < (int64_t)Nk * d; ++x) "
+     "dK[x] = dV[x] = 0.0;\n                const int64_t bh = b * H"),
+    ("bwd_rows_dq_unscaled", "dq_rows[(int64_t)s * d + c] = scale * acc;", "dq_rows[(int64_t)s * d + c] = acc;"),
+    ("bwd_rows_dv_operand", "acc_v[c] += p[j] * doi[c];", "acc_v[c] += p[j] * qi[c];"),
+    ("bwd_rows_wrong_group_head", "const int64_t bh = (int64_t)kb[s] * H + (int64_t)khk[s] * G + gh;",
+     "const int64_t bh = (int64_t)kb[s] * H + (int64_t)khk[s] + gh;"),
+    ("bwd_rows_last_thread_dropped", "for (int t = 0; t < nthr; ++t) {\n                sk",
+     "for (int t = 0; t + 1 < nthr; ++t) {\n                sk"),
 ]
 
 
