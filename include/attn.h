@@ -163,6 +163,43 @@ size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int 
                                       int max_q_len, int max_ctx_len);
 
 /*
+ * Backward of the prefill attention ("Flash Attention and Paged Attention",
+ * section 2: the forward keeps only O and the softmax statistics so that the
+ * backward can recompute S and P tile by tile).  Gradients of
+ * O = softmax(scale * Q K^T) V (causal or not, as in attn_prefill_gqa_fwd)
+ * for an output gradient dO, by the chain rule through the forward's three
+ * steps (same page, section 1):
+ *   P  = exp(scale * Q K^T - LSE) (recomputed per tile from the saved LSE)
+ *   dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ * With H_kv < H the dK and dV of a K/V head sum over its group of query heads
+ * (query head h uses K/V head h / (H / H_kv)).
+ *
+ *   q, o, dout, dq : [B, H, N, d] bf16 (o: the forward's output).
+ *   k, v, dk, dv   : [B, H_kv, N, d] bf16.
+ *   lse            : [B, H, N] fp32, the forward's log-sum-exp (natural log).
+ *   workspace      : device scratch of at least attn_prefill_bwd_workspace_bytes
+ *                    (B, H, N) bytes (8 bytes per query row), 16-byte aligned;
+ *                    contents on entry are ignored.
+ *   dtype          : ATTN_BF16 only (ATTN_ERR_DTYPE otherwise).
+ * q, k, v, o and lse must be the inputs and outputs of one forward call with
+ * the same scale and causal flag.  dq, dk, dv and the workspace must not
+ * overlap each other or any input.  Every element of dq, dk and dv is
+ * written (fp32 accumulation, one bf16 rounding at the end).
+ *
+ * Launches: one kernel for dQ (it also stores each row's LSE and D in the
+ * workspace) and one for dK and dV.  Deterministic: the same inputs give the
+ * same bits (no atomics).
+ */
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int H, int H_kv, int N, int d, float scale, int causal,
+                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_prefill_bwd needs (0 for invalid sizes). */
+size_t attn_prefill_bwd_workspace_bytes(int B, int H, int N);
+
+/*
  * Gather through the block table ("Chunked attention ... 70x slower",
  * section 2.1, the address function): copies K and V of every request,
  * tokens [0, ctx_lens[r]), into packed token-major [sum(ctx_lens), H, d]

@@ -48,6 +48,18 @@ P4 = ctypes.c_void_p(4 << 20)
 NULL = None
 
 
+@pytest.fixture(autouse=True)
+def _no_launch_on_fake_pointers(request):
+    """A case whose arguments pass every host check ends at the device check
+    (E_DEV) here; with a GPU present it would launch on the fake pointers
+    these tests pass, so it is skipped there."""
+    callspec = getattr(request.node, "callspec", None)
+    if callspec is not None and callspec.params.get("code") == E_DEV:
+        import torch
+        if torch.cuda.device_count() > 0:
+            pytest.skip("valid arguments on fake pointers would launch on the GPU")
+
+
 def prefill(**kw):
     a = dict(q=P, k=P2, v=P3, o=P4, lse=NULL, B=1, H=2, N=64, d=128, scale=0.125, causal=1, dtype=0, stream=NULL)
     a.update(kw)
@@ -206,3 +218,32 @@ def test_gqa_workspace_matches_plain_at_equal_heads():
         n, H, d, bs, mq, mc = args
         assert attn.paged_attn_gqa_workspace_bytes(n, H, H, d, bs, mq, mc) == attn.paged_attn_workspace_bytes(*args)
     assert attn.paged_attn_gqa_workspace_bytes(4, 8, 3, 128, 16, 1, 100) == 0
+
+
+def bwd(**kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=P, dout=P2, dq=P3, dk=P4, dv=P, B=2, H=8, H_kv=2, N=100, d=128, scale=0.125,
+             causal=1, dtype=0, workspace=P2, workspace_bytes=2 * 8 * 100 * 8, stream=NULL)
+    a.update(kw)
+    return attn.attn_prefill_bwd(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=NULL), E_NULL), (dict(lse=NULL), E_NULL), (dict(dout=NULL), E_NULL), (dict(dv=NULL), E_NULL),
+    (dict(B=0), E_SHAPE), (dict(N=0), E_SHAPE), (dict(H_kv=3), E_SHAPE), (dict(H_kv=0), E_SHAPE),
+    (dict(d=96), E_HD), (dict(dtype=1), E_DT),
+    (dict(dq=ctypes.c_void_p((3 << 20) + 8)), E_AL), (dict(lse=ctypes.c_void_p((1 << 20) + 2)), E_AL),
+    (dict(scale=-1.0), E_SCALE), (dict(scale=float("nan")), E_SCALE),
+    (dict(workspace=NULL), E_WS), (dict(workspace_bytes=2 * 8 * 100 * 8 - 1), E_WS),
+    (dict(workspace=ctypes.c_void_p((2 << 20) + 8)), E_AL),
+    (dict(N=1 << 24), E_SHAPE),                                  # N * d * 2 bytes must stay below 4 GiB
+    (dict(), E_DEV),
+])
+def test_bwd_rejects(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_workspace_bytes():
+    assert attn.attn_prefill_bwd_workspace_bytes(2, 8, 100) == 2 * 8 * 100 * 8
+    assert attn.attn_prefill_bwd_workspace_bytes(16, 32, 8192) == 16 * 32 * 8192 * 8
+    for bad in ((0, 8, 100), (2, 0, 100), (2, 8, 0), (-1, 8, 100)):
+        assert attn.attn_prefill_bwd_workspace_bytes(*bad) == 0

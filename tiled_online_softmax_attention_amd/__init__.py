@@ -15,7 +15,8 @@ __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
     "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
-    "paged_attn_gqa_workspace_bytes", "attn_strerror", "attn_version", "prefill", "paged_attention",
+    "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "attn_strerror",
+    "attn_version", "prefill", "prefill_bwd", "paged_attention",
     "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
     "APPEND_INVALID",
 ]
@@ -40,6 +41,8 @@ exported_symbols = (
     "attn_prefill_gqa_fwd",
     "paged_attn_gqa_fwd",
     "paged_attn_gqa_workspace_bytes",
+    "attn_prefill_bwd",
+    "attn_prefill_bwd_workspace_bytes",
     "attn_strerror",
     "attn_version",
 )
@@ -85,6 +88,10 @@ def library():
     lib.paged_attn_gqa_fwd.restype = I
     lib.paged_attn_gqa_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
     lib.paged_attn_gqa_workspace_bytes.restype = SZ
+    lib.attn_prefill_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, SZ, P]
+    lib.attn_prefill_bwd.restype = I
+    lib.attn_prefill_bwd_workspace_bytes.argtypes = [I, I, I]
+    lib.attn_prefill_bwd_workspace_bytes.restype = SZ
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -159,6 +166,16 @@ def paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, str
     return library().paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream)
 
 
+def attn_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
+                     workspace_bytes, stream):
+    return library().attn_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, float(scale),
+                                      int(causal), int(dtype), workspace, workspace_bytes, stream)
+
+
+def attn_prefill_bwd_workspace_bytes(B, H, N) -> int:
+    return int(library().attn_prefill_bwd_workspace_bytes(B, H, N))
+
+
 # ---- torch-tensor conveniences (marshalling only) -----------------------------
 
 def _dtype_code(t):
@@ -207,6 +224,39 @@ def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=Non
     if rc != 0:
         raise AttnError(rc, "attn_prefill_fwd")
     return out, lse
+
+
+def prefill_bwd(q, k, v, o, lse, dout, causal: bool, scale: float | None = None, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of ``prefill`` for the output gradient dout, from
+    the forward's q, k, v, o and lse (q, o, dout [B, H, N, d]; k, v [B, H_kv,
+    N, d]; lse [B, H, N] fp32); bf16 only."""
+    import torch
+    B, H, N, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, N, d) or v.shape != k.shape or H % H_kv != 0:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, H_kv, N, d] with H a multiple of H_kv")
+    for t in (q, k, v, o, dout):
+        if not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v, o, dout must be contiguous, same dtype and device")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 [B, H, N] tensor")
+    if scale is None:
+        scale = d ** -0.5
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_prefill_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    rc = attn_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                          B, H, H_kv, N, d, scale, 1 if causal else 0, _dtype_code(q), _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_prefill_bwd")
+    return dq, dk, dv
 
 
 def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float | None = None,

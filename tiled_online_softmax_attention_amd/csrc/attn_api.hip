@@ -8,6 +8,7 @@
 
 #include "attn.h"
 #include "append_internal.h"
+#include "bwd_internal.h"
 #include "attn_internal.h"
 
 namespace {
@@ -100,6 +101,44 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
                      attn_dtype_t dtype, void* stream)
 {
     return attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
+}
+
+size_t attn_prefill_bwd_workspace_bytes(int B, int H, int N)
+{
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return attn::bwd_workspace_bytes(B, H, N);
+}
+
+int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int H, int H_kv, int N, int d, float scale, int causal,
+                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+    if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
+        return ATTN_ERR_ALIGN;
+    int rc = check_scale(scale);
+    if (rc) return rc;
+    if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_SHAPE;
+    if ((int64_t)N * d * 2 >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;   // 32-bit row offsets
+    const size_t need = attn::bwd_workspace_bytes(B, H, N);
+    if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15u) return ATTN_ERR_ALIGN;
+    rc = check_device();
+    if (rc) return rc;
+    attn::BwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.ws = (float*)workspace;
+    a.B = B; a.H = H; a.H_kv = H_kv; a.N = N; a.d = d;
+    a.scale = scale;
+    a.causal = causal ? 1 : 0;
+    rc = attn::launch_bwd(a, (hipStream_t)stream);
+    return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
 
 size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len,

@@ -1,0 +1,570 @@
+// bwd_gfx950.hip -- backward of the fused causal/dense attention for gfx950
+// (bf16 inputs, fp32 accumulation, bf16 gradients).
+//
+// "Flash Attention and Paged Attention" (section 2) keeps only O and the
+// softmax normalisation statistics from the forward, so that the backward
+// recomputes S and P tile by tile instead of reading an N x N matrix back.
+// With the saved LSE the recomputed P = exp(scale q.k - LSE) is final for
+// every tile on its own (no running maximum), and the gradients follow from
+// the chain rule through the forward's three steps (section 1):
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = dO_i . O_i,
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// (D_i = sum_j P_ij dP_ij because O_i = sum_j P_ij V_j.)
+//
+// Two kernels, both deterministic: every output element is accumulated by
+// one lane in a fixed order, with no atomics.
+//   bwd_dq_kernel    one workgroup per (batch, head, 128-query tile).  First
+//                    writes (LSE log2 e, D) of its rows to the workspace, then
+//                    streams 32-key K/V tiles through LDS as the forward does,
+//                    recomputes S^T and dP^T and accumulates dQ^T += K^T dS^T.
+//   bwd_dkdv_kernel  one workgroup per (batch, K/V head, 128-key block).  The
+//                    block's K and V stay in registers; 32-query tiles of Q,
+//                    dO and the rows' (LSE log2 e, D), for every query head of
+//                    the K/V head's group, stream through LDS;
+//                    dV^T += dO^T P and dK^T += Q^T dS.
+// Computing dQ apart from dK/dV costs a second recomputation of S and dP (7
+// matrix products per (query tile, key tile) pair instead of 5) and saves a
+// float atomic read-modify-write of dQ for every such pair.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16, one lane per output column):
+//  * dQ kernel: S^T = K Q^T and dP^T = V dO^T put one query per lane (its Q
+//    and dO fragments stay in registers, as Q does in the forward); dS^T is
+//    the B operand of dQ^T += K^T dS^T straight from the accumulators, and
+//    K^T comes from transposing LDS reads of the K tile.
+//  * dK/dV kernel: S = Q K^T and dP = dO V^T put one key per lane (K and V
+//    fragments in registers); P and dS are the B operands of dV^T += dO^T P
+//    and dK^T += Q^T dS, and dO^T, Q^T come from transposing reads.
+// Every streamed tile is read both ways -- MFMA row reads (16 consecutive
+// rows at one 16-byte chunk) and transposing reads (4 consecutive rows x 4
+// consecutive chunks) -- so tiles are stored row-major with an XOR swizzle of
+// the chunk index that keeps both patterns free of LDS bank conflicts
+// (dual_xor).  Tiles are copied global -> LDS directly (buffer loads to LDS,
+// no registers), one tile ahead into two buffers, one barrier per tile.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_mfma_core.h"
+#include "bwd_internal.h"
+
+namespace attn {
+
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+struct BwdCfg {
+    static constexpr int kWaves = 4;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BT = 32;                     // rows per streamed tile
+    static constexpr int BLK = 32 * kWaves;           // stationary rows per workgroup
+    static constexpr int KCPR = D / 8;                // 16-byte chunks per row
+    static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dimension
+    static constexpr int DBLK = D / 32;               // 32-wide blocks of the head dimension
+    static constexpr int ROW_BYTES = D * 2;
+    static constexpr int TILE_BYTES = BT * ROW_BYTES;
+    static constexpr int RPD = 1024 / ROW_BYTES;      // rows per wave-wide 16 B/lane copy
+    static constexpr int COPIES = TILE_BYTES / 1024;  // wave-wide copies per tile
+    static constexpr int PAIR_BYTES = BT * 8;         // (LSE log2 e, D) of a tile's rows
+};
+
+// XOR applied to the 16-byte chunk index of tile row `row`, chosen so that
+//  (a) 16 consecutive 16-aligned rows at one logical chunk (an MFMA row read
+//      by 16 lanes) fall on 16 distinct 16-byte bank groups, and
+//  (b) 4 consecutive 4-aligned rows x 4 consecutive 4-aligned chunks (one
+//      32-lane pass of a transposing read) fall on 16 distinct bank groups.
+// D = 128: a row spans all 64 banks; xor = 4 (row & 3) + ((row >> 2) & 3).
+// D = 64: two rows share a 256-byte bank window (row & 1 picks the half);
+//         xor = 4 ((row >> 1) & 1) + ((row >> 2) & 3).
+template <int D>
+__device__ __forceinline__ uint32_t dual_xor(uint32_t row)
+{
+    return (D == 128) ? (((row & 3u) << 2) | ((row >> 2) & 3u)) : ((((row >> 1) & 1u) << 2) | ((row >> 2) & 3u));
+}
+
+template <int D>
+__device__ __forceinline__ uint32_t dual_ofs(uint32_t row, uint32_t chunk)
+{
+    return row * (uint32_t)BwdCfg<D>::ROW_BYTES + ((chunk ^ dual_xor<D>(row)) << 4);
+}
+
+// MFMA operand of 8 consecutive channels (chunk) of tile row `row`.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int chunk)
+{
+    return as_bf16x8(*(const u32x4*)(tile + dual_ofs<D>((uint32_t)row, (uint32_t)chunk)));
+}
+
+// Transposed MFMA operand: for this lane one channel (col_byte / 2 + lane
+// offset, see the transposing read below) over tile rows row .. row + 3 and
+// row + 8 .. row + 11.  In each 16-lane group, lane i of a transposing read
+// receives element j from the 8-byte segment addressed by lane 4j + i/4, at
+// position i % 4.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int row, uint32_t col_byte)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + dual_ofs<D>((uint32_t)row, col_byte >> 4) + (col_byte & 15u)));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(tile + dual_ofs<D>((uint32_t)row + 8u, col_byte >> 4) + (col_byte & 15u)));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Lane addressing of the transposing reads: lane (16-lane group G, i = lane
+// % 16, half g = lane / 32) reads row 4g + i/4 (+16h per half-tile), the 4
+// channels starting at 16 (G % 2) + 4 (i % 4) of the 32-channel block, so it
+// receives channel 16 (G % 2) + i over rows 16h + 4g + {0..3, 8..11} -- the
+// rows (keys or queries) that its accumulator registers 8h .. 8h + 7 hold.
+__device__ __forceinline__ int tr_row_of(int lane) { return (lane >> 5) * 4 + ((lane & 15) >> 2); }
+__device__ __forceinline__ uint32_t tr_col_of(int lane)
+{
+    return (uint32_t)((((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2);
+}
+
+// Linear work id after the XCD-contiguous remap (workgroups are dealt to the
+// 8 XCDs round-robin; the grid is padded to a multiple of 8): consecutive
+// ids, i.e. the tiles of one head, share one XCD's L2.
+__device__ __forceinline__ int xcd_linear_id(int bid, int grid)
+{
+    const int per = grid >> 3;
+    return (bid & 7) * per + (bid >> 3);
+}
+
+__device__ __forceinline__ void publish_copies()
+{
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0): this wave's copies have landed
+    __syncthreads();
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// Copies pieces c0 .. c0 + NC - 1 of the BT-row tile starting at row row0 of
+// a row-major [n_rows][D] slab into `tile` in the dual layout; rows at or
+// past n_rows are fetched from row n_rows - 1 (valid data, masked later).
+// Piece c holds tile rows c * RPD .. c * RPD + RPD - 1: lane l lands at row
+// c * RPD + l / KCPR, physical chunk l % KCPR, which holds logical chunk
+// (l % KCPR) ^ dual_xor(row).
+template <int D, int NC>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* tile, int row0, int n_rows, int c0,
+                                          int lane)
+{
+    using C = BwdCfg<D>;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = c0 + i;
+        const uint32_t row = (uint32_t)(c * C::RPD + lane / C::KCPR);
+        const uint32_t src = (uint32_t)min(row0 + (int)row, n_rows - 1);
+        const uint32_t voff = src * (uint32_t)C::ROW_BYTES + ((((uint32_t)lane % C::KCPR) ^ dual_xor<D>(row)) << 4);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(tile + c * 1024), 16, voff, 0, 0, 0);
+    }
+}
+
+// (LSE log2 e, D) of tile rows row0 .. row0 + BT - 1 (clamped): 4 bytes per
+// lane, lane l copies float l of the tile's BT pairs.
+__device__ __forceinline__ void copy_pairs(__amdgpu_buffer_rsrc_t r, char* dst, int row0, int n_rows, int lane)
+{
+    const uint32_t row = (uint32_t)min(row0 + (lane >> 1), n_rows - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst), 4, row * 8u + (uint32_t)(lane & 1) * 4u, 0, 0, 0);
+}
+#endif
+
+// Runs tiles [tb, te) of a stream of nt tiles double-buffered in b0 / b1
+// (tile t lives in buffer t % 2), all with one step variant.  On entry tile
+// tb has been published; each step is preceded by the copies of the next
+// tile into the other buffer and followed by "wait for my copies, barrier",
+// which publishes that tile and frees the one just read.  The buffers are
+// chosen statically (the loop is unrolled by two, with an odd first tile
+// peeled), so LDS reads of one buffer are never ordered behind copies in
+// flight into the other.
+template <class Issue, class Step>
+__device__ __forceinline__ void run_tiles(char* b0, char* b1, int tb, int te, int nt, const Issue& issue,
+                                          const Step& step)
+{
+    int t = tb;
+    if ((t & 1) && t < te) {
+        if (t + 1 < nt) issue(b0, t + 1);
+        step(b1, t);
+        publish_copies();
+        ++t;
+    }
+    for (; t + 2 <= te; t += 2) {
+        issue(b1, t + 1);
+        step(b0, t);
+        publish_copies();
+        if (t + 2 < nt) issue(b0, t + 2);
+        step(b1, t + 1);
+        publish_copies();
+    }
+    if (t < te) {
+        if (t + 1 < nt) issue(b1, t + 1);
+        step(b0, t);
+        publish_copies();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one 32-key tile (K at buf, V at buf + TILE_BYTES) for this wave's 32
+// queries.  Lane: query (lane % 32) with lse2 = its LSE * log2 e and dd = D;
+// accumulator register i of S^T / dP^T holds key key0 + (i/4)*8 + 4g + i%4.
+// MASKED: keys >= q_lim get P = 0.
+template <int D, bool MASKED>
+__device__ __forceinline__ void dq_tile(f32x16 (&dq)[BwdCfg<D>::DBLK], const bf16x8 (&qf)[BwdCfg<D>::KSTEPS],
+                                        const bf16x8 (&df)[BwdCfg<D>::KSTEPS], float lse2, float dd, const char* buf,
+                                        int lane, float c2, int key0, int q_lim)
+{
+    using C = BwdCfg<D>;
+    const char* tk = buf;
+    const char* tv = buf + C::TILE_BYTES;
+    const int g = lane >> 5, r32 = lane & 31;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    {
+        bf16x8 kf[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = row_frag<D>(tk, r32, ks * 2 + g);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma32(kf[ks], qf[ks], s);
+    }
+    {
+        bf16x8 vf[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) vf[ks] = row_frag<D>(tv, r32, ks * 2 + g);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) dp = mfma32(vf[ks], df[ks], dp);
+    }
+    bf16x2 dsk[8];
+    const int lim_rel = q_lim - key0 - 4 * g;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+        float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2));
+        float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c2, -lse2));
+        if (MASKED) {
+            const int off = (i >> 2) * 8 + (i & 3);
+            p0 = (off < lim_rel) ? p0 : 0.f;
+            p1 = (off + 1 < lim_rel) ? p1 : 0.f;
+        }
+        dsk[i >> 1] = pack2(p0 * (dp[i] - dd), p1 * (dp[i + 1] - dd));
+    }
+    const int tr_row = tr_row_of(lane);
+    const uint32_t tr_col = tr_col_of(lane);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16x8 b = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+            dq[db] = mfma32(tr_frag<D>(tk, 16 * h + tr_row, tr_col + db * 64), b, dq[db]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
+{
+    using C = BwdCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= n_work) return;
+    const int N = a.N;
+    const int nqt = (N + C::BLK - 1) / C::BLK;
+    const int bh = L / nqt;
+    const int q0 = (nqt - 1 - L % nqt) * C::BLK;            // heaviest (most keys) first within a head
+    const int G = a.H / a.H_kv;
+    const int64_t head_off = (int64_t)bh * N * C::ROW_BYTES;
+    const int64_t kv_off = ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / G) * N * C::ROW_BYTES;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, r32 = lane & 31;
+    const int qi = q0 + 32 * w + r32;                       // this lane's query
+    const bool valid = qi < N;
+    const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+
+    // ---- Q and dO fragments (channels 16 ks + 8 g .. + 7), D = dO . O ----------
+    bf16x8 qf[C::KSTEPS], df[C::KSTEPS];
+    float dpart = 0.f;
+    {
+        const int64_t row = head_off + (int64_t)qi * C::ROW_BYTES;
+        const char* qp = (const char*)a.q + row;
+        const char* dp = (const char*)a.dout + row;
+        const char* op = (const char*)a.o + row;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
+            if (valid) {
+                x = *(const u32x4*)(qp + (ks * 2 + g) * 16);
+                y = *(const u32x4*)(dp + (ks * 2 + g) * 16);
+                z = *(const u32x4*)(op + (ks * 2 + g) * 16);
+            }
+            qf[ks] = as_bf16x8(x);
+            df[ks] = as_bf16x8(y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dpart = __builtin_fmaf(bf16lo(y[e]), bf16lo(z[e]), dpart);
+                dpart = __builtin_fmaf(bf16hi(y[e]), bf16hi(z[e]), dpart);
+            }
+        }
+    }
+    const float dd = half_sum(dpart);
+    float lse2 = INFINITY;                                  // rows past N: P = 0
+    if (valid) {
+        const float l = a.lse[(int64_t)bh * N + qi];
+        lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;    // a row with no key has P = 0
+        if (g == 0) *(f32x2*)(a.ws + ((int64_t)bh * N + qi) * 2) = f32x2{lse2, dd};
+    }
+
+    // ---- key loop -------------------------------------------------------------
+    f32x16 dq[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) dq[db] = f32x16{};
+    const int kend = a.causal ? min(N, q0 + C::BLK) : N;    // keys this tile needs
+    const int nt = (kend + C::BT - 1) / C::BT;
+    const int q_lim = a.causal ? min(N, qi + 1) : N;
+    const int sel = w >> 1;                                 // waves 0, 1 copy K; 2, 3 copy V
+    const int c0 = (w & 1) * (C::COPIES / 2);
+    // Tiles [0, n_full) are seen in full by every query of the tile (keys
+    // below its first query, all inside the context); the rest (diagonal and
+    // a ragged tail) are masked, for every wave: a tile wholly above a wave's
+    // queries adds exactly nothing (P = 0).  Waves with no valid query only
+    // take part in the copies and barriers.
+    const int n_full = a.causal ? min(nt, q0 / C::BT) : N / C::BT;
+    auto issue = [&](char* buf, int t) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const char* src = (const char*)(sel ? a.v : a.k) + kv_off;
+        copy_tile<D, C::COPIES / 2>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * C::TILE_BYTES, t * C::BT,
+                                    N, c0, lane);
+#endif
+    };
+    auto full = [&](const char* buf, int t) { dq_tile<D, false>(dq, qf, df, lse2, dd, buf, lane, c2, t * C::BT, q_lim); };
+    auto masked = [&](const char* buf, int t) { dq_tile<D, true>(dq, qf, df, lse2, dd, buf, lane, c2, t * C::BT, q_lim); };
+    auto none = [&](const char*, int) {};
+    if (nt > 0) {
+        issue(lds0, 0);
+        publish_copies();
+    }
+    if (q0 + 32 * w < N) {
+        run_tiles(lds0, lds1, 0, n_full, nt, issue, full);
+        run_tiles(lds0, lds1, n_full, nt, nt, issue, masked);
+    } else {
+        run_tiles(lds0, lds1, 0, nt, nt, issue, none);
+    }
+
+    // ---- dQ = scale * dQ^T, bf16 ----------------------------------------------
+    if (valid) {
+        char* orow = (char*)a.dq + head_off + (int64_t)qi * C::ROW_BYTES;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u32x2 w2;
+                w2[0] = pack_bf16(dq[db][r * 4 + 0] * a.scale, dq[db][r * 4 + 1] * a.scale);
+                w2[1] = pack_bf16(dq[db][r * 4 + 2] * a.scale, dq[db][r * 4 + 3] * a.scale);
+                *(u32x2*)(orow + (db * 32 + r * 8 + g * 4) * 2) = w2;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one 32-query tile (Q at buf, dO at buf + TILE_BYTES, the rows'
+// (lse2, D) pairs after them) for this wave's 32 keys.  Lane: key `key`;
+// accumulator register i of S / dP holds query q0 + (i/4)*8 + 4g + i%4.
+// MASKED: queries >= n, and (causal) queries before the key, get P = 0.
+template <int D, bool MASKED>
+__device__ __forceinline__ void dkdv_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
+                                          const bf16x8 (&kf)[BwdCfg<D>::KSTEPS], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
+                                          const char* buf, int lane, float c2, int q0, int key, int n, int causal)
+{
+    using C = BwdCfg<D>;
+    const char* tq = buf;
+    const char* td = buf + C::TILE_BYTES;
+    const float* pr = (const float*)(buf + 2 * C::TILE_BYTES);
+    const int g = lane >> 5, r32 = lane & 31;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    {
+        bf16x8 x[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) x[ks] = row_frag<D>(tq, r32, ks * 2 + g);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma32(x[ks], kf[ks], s);
+    }
+    {
+        bf16x8 x[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) x[ks] = row_frag<D>(td, r32, ks * 2 + g);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) dp = mfma32(x[ks], vf[ks], dp);
+    }
+    bf16x2 pk[8], dsk[8];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        // registers 4 a4 .. 4 a4 + 3 <-> tile rows 8 a4 + 4 g .. + 3
+        const f32x4 x0 = *(const f32x4*)(pr + (a4 * 8 + 4 * g) * 2);
+        const f32x4 x1 = *(const f32x4*)(pr + (a4 * 8 + 4 * g) * 2 + 4);
+        const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
+        const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
+        float p[4], ds[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * a4 + j;
+            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2[j]));
+            if (MASKED) {
+                const int qq = q0 + a4 * 8 + 4 * g + j;
+                pj = (qq < n && (!causal || key <= qq)) ? pj : 0.f;
+            }
+            p[j] = pj;
+            ds[j] = pj * (dp[i] - dd[j]);
+        }
+        pk[2 * a4] = pack2(p[0], p[1]);
+        pk[2 * a4 + 1] = pack2(p[2], p[3]);
+        dsk[2 * a4] = pack2(ds[0], ds[1]);
+        dsk[2 * a4 + 1] = pack2(ds[2], ds[3]);
+    }
+    const int tr_row = tr_row_of(lane);
+    const uint32_t tr_col = tr_col_of(lane);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16x8 bp = cat8(pk[4 * h + 0], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
+        const bf16x8 bs = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) {
+            dv[db] = mfma32(tr_frag<D>(td, 16 * h + tr_row, tr_col + db * 64), bp, dv[db]);
+            dk[db] = mfma32(tr_frag<D>(tq, 16 * h + tr_row, tr_col + db * 64), bs, dk[db]);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int n_work)
+{
+    using C = BwdCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES + C::PAIR_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES + C::PAIR_BYTES];
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= n_work) return;
+    const int N = a.N;
+    const int nkb = (N + C::BLK - 1) / C::BLK;
+    const int bhk = L / nkb;
+    const int k0 = (L % nkb) * C::BLK;                      // heaviest (most query tiles) first
+    const int b = bhk / a.H_kv, hk = bhk % a.H_kv;
+    const int G = a.H / a.H_kv;
+    const int64_t kv_off = (int64_t)bhk * N * C::ROW_BYTES;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 5, r32 = lane & 31;
+    const int key = k0 + 32 * w + r32;                      // this lane's key
+    const bool kvalid = key < N;
+    const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+
+    bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+    {
+        const char* kp = (const char*)a.k + kv_off + (int64_t)key * C::ROW_BYTES;
+        const char* vp = (const char*)a.v + kv_off + (int64_t)key * C::ROW_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+            if (kvalid) {
+                x = *(const u32x4*)(kp + (ks * 2 + g) * 16);
+                y = *(const u32x4*)(vp + (ks * 2 + g) * 16);
+            }
+            kf[ks] = as_bf16x8(x);
+            vf[ks] = as_bf16x8(y);
+        }
+    }
+    f32x16 dk[C::DBLK], dv[C::DBLK];
+#pragma unroll
+    for (int db = 0; db < C::DBLK; ++db) {
+        dk[db] = f32x16{};
+        dv[db] = f32x16{};
+    }
+
+    // query tiles [qt0, nqt) of every query head of the group
+    const int qt0 = a.causal ? k0 / C::BT : 0;
+    const int nqt = (N + C::BT - 1) / C::BT;
+    const int per_head = nqt - qt0;
+    const int nt = G * per_head;
+    const int sel = w >> 1;                                 // waves 0, 1 copy Q; 2, 3 copy dO
+    const int c0 = (w & 1) * (C::COPIES / 2);
+    auto issue = [&](char* buf, int t) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        const int gh = t / per_head, qt = qt0 + t % per_head;
+        const int64_t bh = (int64_t)b * a.H + hk * G + gh;
+        const char* src = (const char*)(sel ? a.dout : a.q) + bh * N * C::ROW_BYTES;
+        copy_tile<D, C::COPIES / 2>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * C::TILE_BYTES, qt * C::BT,
+                                    N, c0, lane);
+        if (w == 0) copy_pairs(raw_rsrc(a.ws + bh * N * 2, (uint32_t)N * 8u), buf + 2 * C::TILE_BYTES, qt * C::BT, N, lane);
+#endif
+    };
+    auto q_of = [&](int t) { return (qt0 + t % per_head) * C::BT; };
+    auto full = [&](const char* buf, int t) {
+        dkdv_tile<D, false>(dk, dv, kf, vf, buf, lane, c2, q_of(t), key, N, a.causal);
+    };
+    auto masked = [&](const char* buf, int t) {
+        dkdv_tile<D, true>(dk, dv, kf, vf, buf, lane, c2, q_of(t), key, N, a.causal);
+    };
+    auto none = [&](const char*, int) {};
+    // Per query head: the first min(4, per_head) tiles of a causal launch
+    // (they hold the diagonal of every wave's keys) and a ragged last tile
+    // are masked, for every wave (a tile wholly before a wave's keys adds
+    // exactly nothing); the tiles between are seen in full.  Waves with no
+    // valid key only take part in the copies and barriers.
+    const int n_head_masked = a.causal ? min(C::kWaves, per_head) : 0;
+    const int n_tail_masked = (N % C::BT != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
+    if (nt > 0) {
+        issue(lds0, 0);
+        publish_copies();
+    }
+    if (k0 + 32 * w < N) {
+        for (int gh = 0; gh < G; ++gh) {
+            const int tb = gh * per_head;
+            run_tiles(lds0, lds1, tb, tb + n_head_masked, nt, issue, masked);
+            run_tiles(lds0, lds1, tb + n_head_masked, tb + per_head - n_tail_masked, nt, issue, full);
+            run_tiles(lds0, lds1, tb + per_head - n_tail_masked, tb + per_head, nt, issue, masked);
+        }
+    } else {
+        run_tiles(lds0, lds1, 0, nt, nt, issue, none);
+    }
+
+    // ---- dK = scale * dK^T, dV = dV^T, bf16 -------------------------------------
+    if (kvalid) {
+        char* krow = (char*)a.dk + kv_off + (int64_t)key * C::ROW_BYTES;
+        char* vrow = (char*)a.dv + kv_off + (int64_t)key * C::ROW_BYTES;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                u32x2 wk, wv;
+                wk[0] = pack_bf16(dk[db][r * 4 + 0] * a.scale, dk[db][r * 4 + 1] * a.scale);
+                wk[1] = pack_bf16(dk[db][r * 4 + 2] * a.scale, dk[db][r * 4 + 3] * a.scale);
+                wv[0] = pack_bf16(dv[db][r * 4 + 0], dv[db][r * 4 + 1]);
+                wv[1] = pack_bf16(dv[db][r * 4 + 2], dv[db][r * 4 + 3]);
+                *(u32x2*)(krow + (db * 32 + r * 8 + g * 4) * 2) = wk;
+                *(u32x2*)(vrow + (db * 32 + r * 8 + g * 4) * 2) = wv;
+            }
+    }
+}
+
+}  // namespace
+
+int launch_bwd(const BwdArgs& a, hipStream_t stream)
+{
+    constexpr int BLK = 128;
+    const int64_t nblk = (a.N + BLK - 1) / BLK;
+    const int64_t n_dq = (int64_t)a.B * a.H * nblk;
+    const int64_t n_kv = (int64_t)a.B * a.H_kv * nblk;
+    if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
+    const int grid_dq = (int)((n_dq + 7) / 8 * 8);
+    const int grid_kv = (int)((n_kv + 7) / 8 * 8);
+    if (a.d == 128) {
+        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a, (int)n_dq);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(grid_kv), dim3(BwdCfg<128>::kThreads), 0, stream, a,
+                           (int)n_kv);
+    } else {
+        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a, (int)n_dq);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(grid_kv), dim3(BwdCfg<64>::kThreads), 0, stream, a, (int)n_kv);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace attn
