@@ -13,6 +13,10 @@ measured with HIP events on the launch stream) and the decode KV GB/s
 the block table) under "decode".  The oracle (fp64, CPU) is timed on a
 bounded sample of the same prefill workload as `cpu_baseline`.
 
+Other modes (--only): prefill, decode, c2, c5 (single workloads), append (KV
+append), gqa (grouped-query prefill and decode), bwd (the backward of the
+causal prefill, MHA and GQA-8).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -37,6 +41,7 @@ METRIC = "causal prefill TFLOP/s + paged-decode KV GB/s (and % roofline), 1 MI35
 KERNEL_SOURCES = {
     "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "prefill_gfx950.hip", "attn_internal.h"],
     "decode_c4": ["paged_gfx950.hip", "attn_internal.h"],
+    "bwd_c3": ["attn_mfma_core.h", "bwd_gfx950.hip", "bwd_internal.h"],
 }
 
 
@@ -76,6 +81,20 @@ def prefill_bytes(B, H, N, d, elem=2, H_kv=None):
     return B * N * d * elem * (2 * H + 2 * H_kv) + B * H * N * 4   # q, k, v read + o written + lse
 
 
+def bwd_flops(B, H, N, d, causal):
+    """Algorithmic FLOPs of the backward: five products (S recomputed, dP,
+    dV, dK, dQ) of 2*d FLOPs per allowed (query, key) pair."""
+    pairs = N * (N + 1) // 2 if causal else N * N
+    return 10.0 * d * pairs * B * H
+
+
+def bwd_bytes(B, H, N, d, elem=2, H_kv=None):
+    """q, o, dO read and dQ written (H heads); k, v read and dK, dV written
+    (H_kv heads); lse read; the per-row (lse, D) workspace written and read."""
+    H_kv = H if H_kv is None else H_kv
+    return B * N * d * elem * (4 * H + 4 * H_kv) + B * H * N * 4 + 2 * B * H * N * 8
+
+
 def paged_bytes(ctx_lens, q_lens, H, d, block_size, elem=2, H_kv=None):
     """K and V of every context token once (for the H_kv K/V heads), q read
     and o, lse written (H query heads), one table entry per page."""
@@ -91,6 +110,19 @@ def paged_flops(ctx_lens, q_lens, d, H):
     for c, q in zip(ctx_lens, q_lens):
         pairs += q * (c - q) + q * (q + 1) // 2
     return 4.0 * d * pairs * H
+
+
+def probe_copy(torch, dev):
+    """One 1 GiB device-to-device copy: the reference kernel whose PMC byte
+    counters calibrate FETCH_SIZE / WRITE_SIZE."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    print("probe copy: 1073741824 bytes read and written", file=sys.stderr, flush=True)
 
 
 class EventTimer:
@@ -159,6 +191,108 @@ def cpu_baseline_decode(pi, budget_s, oracle):
             break
     return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
+
+
+def cpu_baseline_bwd(q, k, v, do, cfg, budget_s, oracle):
+    """Oracle backward on sampled dQ rows of the causal workload until
+    ~budget_s of CPU work: seeded (b, h) heads, 64 seeded rows each.  Each
+    row's work is its S row, dP row and dQ row, i.e. three of the five
+    products of the backward, counted as 6*d FLOPs per allowed key."""
+    from tiled_online_softmax_attention_amd import inputs
+    heads = inputs.sample_triples(cfg.seed + 3000, 4096, (cfg.B, cfg.H))
+    done_rows, done_heads, flops, t_total = 0, 0, 0.0, 0.0
+    for hi, (b, h) in enumerate(heads):
+        rows = [r for (r,) in inputs.sample_triples(cfg.seed + 4000 + hi, 64, (cfg.N,))]
+        hk = h // (cfg.H // (cfg.H_kv or cfg.H))
+        qs, dos = (x[b, h].unsqueeze(0).unsqueeze(0).cpu() for x in (q, do))
+        ks, vs = (x[b, hk].unsqueeze(0).unsqueeze(0).cpu() for x in (k, v))
+        t0 = time.perf_counter()
+        oracle.attention_bwd_rows(qs, ks, vs, dos, cfg.scale, True, [(0, 0, r) for r in rows], [])
+        t_total += time.perf_counter() - t0
+        done_rows += len(rows)
+        done_heads += 1
+        flops += sum(6.0 * cfg.d * (r + 1) for r in rows)
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d seeded dQ rows (64 per head, %d seeded heads) of the 16x32x8192x128 causal backward, "
+                      "full-length fp64 rows (S, dP, dQ products; 6*d FLOPs per allowed key), %.1f s of oracle "
+                      "time" % (done_rows, done_heads, t_total)}
+
+
+def bench_bwd(args):
+    """Backward of the causal 16x32x8192x128 prefill (attn_prefill_bwd: dQ
+    kernel + dK/dV kernel) and of its grouped-query variant (4 K/V heads);
+    TFLOP/s on the algorithmic FLOPs of the backward (five products of 2*d
+    FLOPs per allowed pair), the call's average duration from HIP events on
+    its stream.  Inputs, the forward's O and LSE, and dO are resident in HBM
+    before timing."""
+    import torch
+    import tiled_online_softmax_attention_amd as attn
+    from tiled_online_softmax_attention_amd import inputs
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.library()
+    dev = torch.device("cuda:0")
+    res = {"metric": "causal prefill backward TFLOP/s (dQ, dK, dV), 1 MI355X", "value": None, "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "causal prefill backward bf16 16x32x8192x128, dO iid N(0,1)",
+                      "global_batch": inputs.C3.B, "seq_len": inputs.C3.N, "parallelism": "none (1 GPU)"}}
+    if args.probe_copy:
+        probe_copy(torch, dev)
+    variants = [("mha", inputs.C3), ("gqa8", inputs.C3_GQA8)]
+    if args.bwd_mha_only:
+        variants = variants[:1]
+    for key, cfg in variants:
+        q, k, v = inputs.prefill_inputs(cfg, dev)
+        do = inputs.grad_output(cfg, dev)
+        o, lse = attn.prefill(q, k, v, True, cfg.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(attn.attn_prefill_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N), dtype=torch.uint8, device=dev)
+        timer = EventTimer(torch)
+        for _ in range(args.warmup):
+            attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            e = timer.start()
+            attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+            timer.stop(e)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = timer.mean_ms()
+        fl = bwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
+        tf = fl / (ms * 1e-3) / 1e12
+        entry = {"launch_ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                              "traffic": read_traffic("bwd_c3") if key == "mha" else None,
+                              "kernels": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
+                              "flops_per_launch": fl,
+                              "executed_flops_per_launch": fl * 7 / 5,
+                              "algorithmic_bytes_per_launch": bwd_bytes(cfg.B, cfg.H, cfg.N, cfg.d,
+                                                                        H_kv=cfg.H_kv)}}
+        if key == "mha":
+            res["value"] = entry["TFLOP/s"]
+            res["ms_per_step"] = round(wall * 1e3 / args.steps, 4)
+            res["roofline"] = entry["roofline"]
+            res["launch_ms"] = entry["launch_ms"]
+            if not args.no_cpu_baseline:
+                import oracle
+                print("timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+                res["cpu_baseline"] = cpu_baseline_bwd(q, k, v, do, cfg, args.cpu_seconds, oracle)
+        else:
+            res["gqa8"] = dict(entry, workload="causal prefill backward bf16 16x32x8192x128, 32 query heads on "
+                                                "4 K/V heads")
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    print(json.dumps(res), flush=True)
 
 
 def append_bytes(new_lens, H, d, elem=2):
@@ -294,13 +428,18 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa", "bwd"],
+                    default="all")
+    ap.add_argument("--bwd-mha-only", action="store_true",
+                    help="--only bwd: skip the grouped-query variant (profiling runs)")
     args = ap.parse_args()
 
     if args.only == "append":
         return bench_append(args)
     if args.only == "gqa":
         return bench_gqa(args)
+    if args.only == "bwd":
+        return bench_bwd(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -324,14 +463,7 @@ def main():
     do_decode = args.only in ("all", "decode")
 
     if args.probe_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        print("probe copy: 1073741824 bytes read and written", file=sys.stderr, flush=True)
+        probe_copy(torch, dev)
 
     print("generating inputs", file=sys.stderr, flush=True)
     if do_prefill:

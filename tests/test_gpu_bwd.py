@@ -48,15 +48,10 @@ def check_grad(name, got, ref):
     assert err.mean() <= MEAN_RMS * rms, (name, float(err.mean()), rms)
 
 
-def dout_like(q, seed):
-    g = torch.Generator(device="cpu").manual_seed(seed)
-    return torch.randn(q.shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(q.device)
-
-
-def run(cfg, seed=0, nan_outputs=True, scale=None):
+def run(cfg, nan_outputs=True, scale=None):
     scale = cfg.scale if scale is None else scale
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    do = dout_like(q, 1000 + cfg.seed + seed)
+    do = inputs.grad_output(cfg, DEV)
     o, lse = attn.prefill(q, k, v, cfg.causal, scale)
     dq = torch.full_like(q, float("nan")) if nan_outputs else None
     dk = torch.full_like(k, float("nan")) if nan_outputs else None
@@ -120,7 +115,7 @@ def test_bwd_workspace_contents_ignored():
     """A workspace full of garbage on entry gives the same gradients."""
     cfg = inputs.PrefillConfig("bwd_ws", 1, 2, 300, 128, torch.bfloat16, True, 8)
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    do = dout_like(q, 11)
+    do = inputs.grad_output(cfg, DEV)
     o, lse = attn.prefill(q, k, v, True, cfg.scale)
     ref = attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale)
     ws = torch.full((attn.attn_prefill_bwd_workspace_bytes(1, 2, 300) // 4,), float("nan"), device=DEV)

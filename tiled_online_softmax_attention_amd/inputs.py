@@ -18,6 +18,8 @@ Recipe (the same for every workload):
     and the slots past each request's context in its last block, are
     overwritten with NaN so that any stray read shows up in the output.
   * Unused block-table entries are -1.
+  * The output gradient dO of a backward workload is iid N(0, 1) like Q,
+    drawn from its own generator (seed + 7919), rounded to bf16.
 """
 from __future__ import annotations
 
@@ -115,6 +117,15 @@ def prefill_inputs(cfg: PrefillConfig, device="cpu", B=None, H=None, N=None, see
     k = _randn((B, H_kv, N, cfg.d), g, device, cfg.dtype)
     v = _randn((B, H_kv, N, cfg.d), g, device, cfg.dtype)
     return q, k, v
+
+
+def grad_output(cfg: PrefillConfig, device="cpu", B=None, H=None, N=None):
+    """dO of shape [B, H, N, d] for a backward workload (own seeded stream)."""
+    B = cfg.B if B is None else B
+    H = cfg.H if H is None else H
+    N = cfg.N if N is None else N
+    g = device_generator(cfg.seed + 7919, device)
+    return _randn((B, H, N, cfg.d), g, device, cfg.dtype)
 
 
 @dataclass
