@@ -88,29 +88,6 @@ __device__ __forceinline__ uint32_t dual_ofs(uint32_t row, uint32_t chunk)
     return row * (uint32_t)BwdCfg<D>::ROW_BYTES + ((chunk ^ dual_xor<D>(row)) << 4);
 }
 
-// MFMA operand of 8 consecutive channels (chunk) of tile row `row`.
-template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const char* tile, int row, int chunk)
-{
-    return as_bf16x8(*(const u32x4*)(tile + dual_ofs<D>((uint32_t)row, (uint32_t)chunk)));
-}
-
-// Transposed MFMA operand: for this lane one channel (col_byte / 2 + lane
-// offset, see the transposing read below) over tile rows row .. row + 3 and
-// row + 8 .. row + 11.  In each 16-lane group, lane i of a transposing read
-// receives element j from the 8-byte segment addressed by lane 4j + i/4, at
-// position i % 4.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int row, uint32_t col_byte)
-{
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(tile + dual_ofs<D>((uint32_t)row, col_byte >> 4) + (col_byte & 15u)));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(tile + dual_ofs<D>((uint32_t)row + 8u, col_byte >> 4) + (col_byte & 15u)));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 // Lane addressing of the transposing reads: lane (16-lane group G, i = lane
 // % 16, half g = lane / 32) reads row 4g + i/4 (+16h per half-tile), the 4
 // channels starting at 16 (G % 2) + 4 (i % 4) of the 32-channel block, so it
@@ -120,6 +97,50 @@ __device__ __forceinline__ int tr_row_of(int lane) { return (lane >> 5) * 4 + ((
 __device__ __forceinline__ uint32_t tr_col_of(int lane)
 {
     return (uint32_t)((((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2);
+}
+
+// Per-lane byte offsets of every LDS read a tile step makes, relative to the
+// tile (computed once per kernel).  The swizzle only looks at row bits 0..3,
+// so tile row r32 + 32 sb and row tr_row + 16 h + 32 sb share the offsets of
+// rows r32 and tr_row plus (32 sb + 16 h) * ROW_BYTES, which, like the tile's
+// own position in LDS, goes into the read's immediate offset: no address
+// arithmetic is left inside the loop.
+template <int D>
+struct LaneOfs {
+    uint32_t row[BwdCfg<D>::KSTEPS];    // MFMA row reads: row r32, chunk 2 ks + g
+    uint32_t tlo[BwdCfg<D>::DBLK];      // transposing reads: row tr_row, d-block db
+    uint32_t thi[BwdCfg<D>::DBLK];      //                    row tr_row + 8
+};
+
+template <int D>
+__device__ __forceinline__ LaneOfs<D> lane_offsets(int lane)
+{
+    LaneOfs<D> o;
+    const int g = lane >> 5, r32 = lane & 31;
+    const int tr_row = tr_row_of(lane);
+    const uint32_t tr_col = tr_col_of(lane);
+#pragma unroll
+    for (int ks = 0; ks < BwdCfg<D>::KSTEPS; ++ks) o.row[ks] = dual_ofs<D>((uint32_t)r32, (uint32_t)(ks * 2 + g));
+#pragma unroll
+    for (int db = 0; db < BwdCfg<D>::DBLK; ++db) {
+        const uint32_t col = tr_col + db * 64;
+        o.tlo[db] = dual_ofs<D>((uint32_t)tr_row, col >> 4) + (col & 15u);
+        o.thi[db] = dual_ofs<D>((uint32_t)tr_row + 8u, col >> 4) + (col & 15u);
+    }
+    return o;
+}
+
+__device__ __forceinline__ bf16x8 lds_row(const char* p)
+{
+    return as_bf16x8(*(const u32x4*)p);
+}
+
+__device__ __forceinline__ bf16x8 lds_tr(const char* lo, const char* hi)
+{
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)lo);
+    const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)hi);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Linear work id after the XCD-contiguous remap (workgroups are dealt to the
@@ -215,27 +236,38 @@ __device__ __forceinline__ void run_tiles(char* b0, char* b1, int tb, int te, in
 template <int D, bool MASKED>
 __device__ __forceinline__ void dq_tile(f32x16 (&dq)[BwdCfg<D>::DBLK], const bf16x8 (&qf)[BwdCfg<D>::KSTEPS],
                                         const bf16x8 (&df)[BwdCfg<D>::KSTEPS], float lse2, float dd, const char* buf,
-                                        int lane, float c2, int key0, int q_lim)
+                                        const LaneOfs<D>& lo, int lane, float c2, int key0, int q_lim)
 {
     using C = BwdCfg<D>;
     const char* tk = buf;
     const char* tv = buf + C::TILE_BYTES;
-    const int g = lane >> 5, r32 = lane & 31;
+    const int g = lane >> 5;
+    // stages fenced as in the dK/dV kernel: row reads, then the S / dP
+    // MFMAs, then the transposing K reads (ahead of the exponentials), then
+    // the dQ MFMAs
     f32x16 s = f32x16{}, dp = f32x16{};
     {
-        bf16x8 kf[C::KSTEPS];
+        bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) kf[ks] = row_frag<D>(tk, r32, ks * 2 + g);
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            kf[ks] = lds_row(tk + lo.row[ks]);
+            vf[ks] = lds_row(tv + lo.row[ks]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma32(kf[ks], qf[ks], s);
+        for (int ks = 0; ks < C::KSTEPS; ++ks) {
+            s = mfma32(kf[ks], qf[ks], s);
+            dp = mfma32(vf[ks], df[ks], dp);
+        }
     }
-    {
-        bf16x8 vf[C::KSTEPS];
+    bf16x8 kt[2][C::DBLK];
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) vf[ks] = row_frag<D>(tv, r32, ks * 2 + g);
+    for (int h = 0; h < 2; ++h) {
+        const char* th = tk + 16 * h * C::ROW_BYTES;
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) dp = mfma32(vf[ks], df[ks], dp);
+        for (int db = 0; db < C::DBLK; ++db) kt[h][db] = lds_tr(th + lo.tlo[db], th + lo.thi[db]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     bf16x2 dsk[8];
     const int lim_rel = q_lim - key0 - 4 * g;
 #pragma unroll
@@ -249,14 +281,12 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[BwdCfg<D>::DBLK], const bf1
         }
         dsk[i >> 1] = pack2(p0 * (dp[i] - dd), p1 * (dp[i + 1] - dd));
     }
-    const int tr_row = tr_row_of(lane);
-    const uint32_t tr_col = tr_col_of(lane);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const bf16x8 b = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
 #pragma unroll
-        for (int db = 0; db < C::DBLK; ++db)
-            dq[db] = mfma32(tr_frag<D>(tk, 16 * h + tr_row, tr_col + db * 64), b, dq[db]);
+        for (int db = 0; db < C::DBLK; ++db) dq[db] = mfma32(kt[h][db], b, dq[db]);
     }
 }
 
@@ -337,8 +367,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
                                     N, c0, lane);
 #endif
     };
-    auto full = [&](const char* buf, int t) { dq_tile<D, false>(dq, qf, df, lse2, dd, buf, lane, c2, t * C::BT, q_lim); };
-    auto masked = [&](const char* buf, int t) { dq_tile<D, true>(dq, qf, df, lse2, dd, buf, lane, c2, t * C::BT, q_lim); };
+    const LaneOfs<D> lo = lane_offsets<D>(lane);
+    auto full = [&](const char* buf, int t) {
+        dq_tile<D, false>(dq, qf, df, lse2, dd, buf, lo, lane, c2, t * C::BT, q_lim);
+    };
+    auto masked = [&](const char* buf, int t) {
+        dq_tile<D, true>(dq, qf, df, lse2, dd, buf, lo, lane, c2, t * C::BT, q_lim);
+    };
     auto none = [&](const char*, int) {};
     if (nt > 0) {
         issue(lds0, 0);
@@ -367,80 +402,190 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one 32-query tile (Q at buf, dO at buf + TILE_BYTES, the rows'
-// (lse2, D) pairs after them) for this wave's 32 keys.  Lane: key `key`;
-// accumulator register i of S / dP holds query q0 + (i/4)*8 + 4g + i%4.
-// MASKED: queries >= n, and (causal) queries before the key, get P = 0.
-template <int D, bool MASKED>
-__device__ __forceinline__ void dkdv_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
-                                          const bf16x8 (&kf)[BwdCfg<D>::KSTEPS], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
-                                          const char* buf, int lane, float c2, int q0, int key, int n, int causal)
+// dK, dV.  A streamed query tile holds QB blocks of 32 queries (QT = 32 QB
+// rows of Q, then QT rows of dO, then the rows' (lse2, D) pairs).  The QB
+// blocks are independent until they add into dK / dV, which gives the one
+// wave of a SIMD (the accumulators and K/V fragments take ~350 registers)
+// work to overlap: the exponentials of one block with the MFMAs of another.
+template <int D, int QB>
+struct QTileCfg {
+    static constexpr int QT = 32 * QB;                              // query rows per tile
+    static constexpr int TILE_BYTES = QT * BwdCfg<D>::ROW_BYTES;    // one of Q or dO
+    static constexpr int COPIES = TILE_BYTES / 1024;
+    static constexpr int PAIR_BYTES = QT * 8;
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES + PAIR_BYTES;
+};
+
+// One query tile for this wave's 32 keys, in stages over its 32-query
+// blocks.  Lane: key `key`; accumulator register i of block sb of S / dP
+// holds query q0 + 32 sb + (i/4)*8 + 4g + i%4.  MASKED: queries >= n, and
+// (causal) queries before the key, get P = 0.
+template <int D>
+struct DkdvBlock {
+    f32x16 s, dp;                          // S and dP of one 32-query block
+};
+
+template <int D>
+struct DkdvOperands {
+    bf16x8 tq[2][BwdCfg<D>::DBLK];         // Q^T (transposing reads), per half-block h and d-block
+    bf16x8 tdo[2][BwdCfg<D>::DBLK];        // dO^T
+    f32x4 pr[8];                           // (lse2, D) pairs of the lane's 16 queries
+};
+
+// S = Q K^T, dP = dO V^T for block sb (row reads issued first, then the
+// MFMAs, so the LDS latency is paid once per block).
+template <int D>
+__device__ __forceinline__ void dkdv_scores(DkdvBlock<D>& blk, const bf16x8 (&kf)[BwdCfg<D>::KSTEPS],
+                                            const bf16x8 (&vf)[BwdCfg<D>::KSTEPS], const char* tq, const char* td,
+                                            const LaneOfs<D>& lo, int sb)
 {
     using C = BwdCfg<D>;
-    const char* tq = buf;
-    const char* td = buf + C::TILE_BYTES;
-    const float* pr = (const float*)(buf + 2 * C::TILE_BYTES);
-    const int g = lane >> 5, r32 = lane & 31;
-    f32x16 s = f32x16{}, dp = f32x16{};
-    {
-        bf16x8 x[C::KSTEPS];
+    bf16x8 x[C::KSTEPS], y[C::KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) x[ks] = row_frag<D>(tq, r32, ks * 2 + g);
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma32(x[ks], kf[ks], s);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        x[ks] = lds_row(tq + 32 * sb * C::ROW_BYTES + lo.row[ks]);
+        y[ks] = lds_row(td + 32 * sb * C::ROW_BYTES + lo.row[ks]);
     }
-    {
-        bf16x8 x[C::KSTEPS];
+    __builtin_amdgcn_sched_barrier(0);
+    blk.s = f32x16{};
+    blk.dp = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) x[ks] = row_frag<D>(td, r32, ks * 2 + g);
-#pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) dp = mfma32(x[ks], vf[ks], dp);
+    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+        blk.s = mfma32(x[ks], kf[ks], blk.s);
+        blk.dp = mfma32(y[ks], vf[ks], blk.dp);
     }
-    bf16x2 pk[8], dsk[8];
+}
+
+// The transposed Q / dO operands and the (lse2, D) pairs of block sb.
+template <int D>
+__device__ __forceinline__ void dkdv_load(DkdvOperands<D>& op, const char* tq, const char* td, const float* pr,
+                                          const LaneOfs<D>& lo, int lane, int sb)
+{
+    using C = BwdCfg<D>;
+    const int g = lane >> 5;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rofs = (32 * sb + 16 * h) * C::ROW_BYTES;
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) {
+            op.tdo[h][db] = lds_tr(td + rofs + lo.tlo[db], td + rofs + lo.thi[db]);
+            op.tq[h][db] = lds_tr(tq + rofs + lo.tlo[db], tq + rofs + lo.thi[db]);
+        }
+    }
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) {
-        // registers 4 a4 .. 4 a4 + 3 <-> tile rows 8 a4 + 4 g .. + 3
-        const f32x4 x0 = *(const f32x4*)(pr + (a4 * 8 + 4 * g) * 2);
-        const f32x4 x1 = *(const f32x4*)(pr + (a4 * 8 + 4 * g) * 2 + 4);
+        // registers 4 a4 .. 4 a4 + 3 <-> block rows 8 a4 + 4 g .. + 3
+        const float* pp = pr + (32 * sb + a4 * 8 + 4 * g) * 2;
+        op.pr[2 * a4] = *(const f32x4*)(pp);
+        op.pr[2 * a4 + 1] = *(const f32x4*)(pp + 4);
+    }
+}
+
+// P = exp2(s c2 - lse2) (masked), dS = P (dP - D), both rounded to bf16 in
+// the B-operand layout.
+template <int D, bool MASKED>
+__device__ __forceinline__ void dkdv_softmax(bf16x2 (&pk)[8], bf16x2 (&dsk)[8], const DkdvBlock<D>& blk,
+                                             const DkdvOperands<D>& op, int lane, float c2, int q0, int key, int n,
+                                             int causal, int sb)
+{
+    const int g = lane >> 5;
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        const f32x4 x0 = op.pr[2 * a4], x1 = op.pr[2 * a4 + 1];
         const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
         const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
         float p[4], ds[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int i = 4 * a4 + j;
-            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -l2[j]));
+            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(blk.s[i], c2, -l2[j]));
             if (MASKED) {
-                const int qq = q0 + a4 * 8 + 4 * g + j;
+                const int qq = q0 + 32 * sb + a4 * 8 + 4 * g + j;
                 pj = (qq < n && (!causal || key <= qq)) ? pj : 0.f;
             }
             p[j] = pj;
-            ds[j] = pj * (dp[i] - dd[j]);
+            ds[j] = pj * (blk.dp[i] - dd[j]);
         }
         pk[2 * a4] = pack2(p[0], p[1]);
         pk[2 * a4 + 1] = pack2(p[2], p[3]);
         dsk[2 * a4] = pack2(ds[0], ds[1]);
         dsk[2 * a4 + 1] = pack2(ds[2], ds[3]);
     }
-    const int tr_row = tr_row_of(lane);
-    const uint32_t tr_col = tr_col_of(lane);
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_accumulate(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
+                                                const bf16x2 (&pk)[8], const bf16x2 (&dsk)[8],
+                                                const DkdvOperands<D>& op)
+{
+    using C = BwdCfg<D>;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const bf16x8 bp = cat8(pk[4 * h + 0], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
         const bf16x8 bs = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db) {
-            dv[db] = mfma32(tr_frag<D>(td, 16 * h + tr_row, tr_col + db * 64), bp, dv[db]);
-            dk[db] = mfma32(tr_frag<D>(tq, 16 * h + tr_row, tr_col + db * 64), bs, dk[db]);
+            dv[db] = mfma32(op.tdo[h][db], bp, dv[db]);
+            dk[db] = mfma32(op.tq[h][db], bs, dk[db]);
         }
     }
 }
+
+// The stages are fenced so that the scheduler keeps each block's LDS reads
+// ahead of the MFMAs that use them (left alone it issues every transposing
+// read next to its MFMA and waits for it), and so that each block's
+// exponentials sit in the same stretch as the other block's MFMAs, which the
+// one wave of the SIMD runs while the MFMAs execute:
+//   S/dP(0) | loads(1), T(0) | S/dP(1) + softmax(0) | T(1) | dV/dK(0) + softmax(1) | dV/dK(1)
+// (T: transposed operands and pairs).  With one block per tile the stages
+// simply run in order.
+template <int D, int QB, bool MASKED>
+__device__ __forceinline__ void dkdv_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
+                                          const bf16x8 (&kf)[BwdCfg<D>::KSTEPS], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
+                                          const char* buf, const LaneOfs<D>& lo, int lane, float c2, int q0, int key,
+                                          int n, int causal)
+{
+    using Q = QTileCfg<D, QB>;
+    static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per tile");
+    const char* tq = buf;
+    const char* td = buf + Q::TILE_BYTES;
+    const float* pr = (const float*)(buf + 2 * Q::TILE_BYTES);
+    DkdvBlock<D> b0, b1;
+    DkdvOperands<D> o0, o1;
+    bf16x2 pk0[8], dsk0[8], pk1[8], dsk1[8];
+    dkdv_scores(b0, kf, vf, tq, td, lo, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    dkdv_load(o0, tq, td, pr, lo, lane, 0);
+    if (QB == 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_scores(b1, kf, vf, tq, td, lo, 1);
+    }
+    dkdv_softmax<D, MASKED>(pk0, dsk0, b0, o0, lane, c2, q0, key, n, causal, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (QB == 2) {
+        dkdv_load(o1, tq, td, pr, lo, lane, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_softmax<D, MASKED>(pk1, dsk1, b1, o1, lane, c2, q0, key, n, causal, 1);
+    }
+    dkdv_accumulate(dk, dv, pk0, dsk0, o0);
+    if (QB == 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        dkdv_accumulate(dk, dv, pk1, dsk1, o1);
+    }
+}
+
+#ifndef ATTN_BWD_QB
+#define ATTN_BWD_QB 2
+#endif
 
 template <int D>
 __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int n_work)
 {
     using C = BwdCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES + C::PAIR_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES + C::PAIR_BYTES];
+    constexpr int QB = (D == 128) ? ATTN_BWD_QB : 1;
+    using Q = QTileCfg<D, QB>;
+    __shared__ __attribute__((aligned(16))) char lds0[Q::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[Q::BUF_BYTES];
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= n_work) return;
     const int N = a.N;
@@ -480,37 +625,40 @@ __global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs
     }
 
     // query tiles [qt0, nqt) of every query head of the group
-    const int qt0 = a.causal ? k0 / C::BT : 0;
-    const int nqt = (N + C::BT - 1) / C::BT;
+    const int qt0 = a.causal ? k0 / Q::QT : 0;
+    const int nqt = (N + Q::QT - 1) / Q::QT;
     const int per_head = nqt - qt0;
     const int nt = G * per_head;
     const int sel = w >> 1;                                 // waves 0, 1 copy Q; 2, 3 copy dO
-    const int c0 = (w & 1) * (C::COPIES / 2);
+    const int c0 = (w & 1) * (Q::COPIES / 2);
     auto issue = [&](char* buf, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)
         const int gh = t / per_head, qt = qt0 + t % per_head;
         const int64_t bh = (int64_t)b * a.H + hk * G + gh;
         const char* src = (const char*)(sel ? a.dout : a.q) + bh * N * C::ROW_BYTES;
-        copy_tile<D, C::COPIES / 2>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * C::TILE_BYTES, qt * C::BT,
+        copy_tile<D, Q::COPIES / 2>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * Q::TILE_BYTES, qt * Q::QT,
                                     N, c0, lane);
-        if (w == 0) copy_pairs(raw_rsrc(a.ws + bh * N * 2, (uint32_t)N * 8u), buf + 2 * C::TILE_BYTES, qt * C::BT, N, lane);
+        if (w < QB)
+            copy_pairs(raw_rsrc(a.ws + bh * N * 2, (uint32_t)N * 8u), buf + 2 * Q::TILE_BYTES + w * 256,
+                       qt * Q::QT + 32 * w, N, lane);
 #endif
     };
-    auto q_of = [&](int t) { return (qt0 + t % per_head) * C::BT; };
+    auto q_of = [&](int t) { return (qt0 + t % per_head) * Q::QT; };
+    const LaneOfs<D> lo = lane_offsets<D>(lane);
     auto full = [&](const char* buf, int t) {
-        dkdv_tile<D, false>(dk, dv, kf, vf, buf, lane, c2, q_of(t), key, N, a.causal);
+        dkdv_tile<D, QB, false>(dk, dv, kf, vf, buf, lo, lane, c2, q_of(t), key, N, a.causal);
     };
     auto masked = [&](const char* buf, int t) {
-        dkdv_tile<D, true>(dk, dv, kf, vf, buf, lane, c2, q_of(t), key, N, a.causal);
+        dkdv_tile<D, QB, true>(dk, dv, kf, vf, buf, lo, lane, c2, q_of(t), key, N, a.causal);
     };
     auto none = [&](const char*, int) {};
-    // Per query head: the first min(4, per_head) tiles of a causal launch
-    // (they hold the diagonal of every wave's keys) and a ragged last tile
-    // are masked, for every wave (a tile wholly before a wave's keys adds
-    // exactly nothing); the tiles between are seen in full.  Waves with no
-    // valid key only take part in the copies and barriers.
-    const int n_head_masked = a.causal ? min(C::kWaves, per_head) : 0;
-    const int n_tail_masked = (N % C::BT != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
+    // Per query head: the first tiles of a causal launch, up to the block's
+    // last key (they hold the diagonal of every wave's keys), and a ragged
+    // last tile are masked, for every wave (a tile wholly before a wave's
+    // keys adds exactly nothing); the tiles between are seen in full.  Waves
+    // with no valid key only take part in the copies and barriers.
+    const int n_head_masked = a.causal ? min(C::BLK / Q::QT, per_head) : 0;
+    const int n_tail_masked = (N % Q::QT != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
     if (nt > 0) {
         issue(lds0, 0);
         publish_copies();
