@@ -17,11 +17,14 @@
 //                    writes (LSE log2 e, D) of its rows to the workspace, then
 //                    streams 32-key K/V tiles through LDS as the forward does,
 //                    recomputes S^T and dP^T and accumulates dQ^T += K^T dS^T.
-//   bwd_dkdv_kernel  one workgroup per (batch, K/V head, 128-key block).  The
-//                    block's K and V stay in registers; 32-query tiles of Q,
-//                    dO and the rows' (LSE log2 e, D), for every query head of
-//                    the K/V head's group, stream through LDS;
-//                    dV^T += dO^T P and dK^T += Q^T dS.
+//   bwd_dkdv_kernel  one workgroup of 8 waves per (batch, K/V head, 128-key
+//                    block); 32-query tiles of Q, dO and the rows' (LSE log2 e,
+//                    D), for every query head of the K/V head's group, stream
+//                    through LDS.  Each 32-key block has two waves: the P wave
+//                    (its keys' K in registers) computes S and P, passes P on
+//                    through LDS and accumulates dV^T += dO^T P; the dS wave
+//                    (V in registers) computes dP, then dS = P (dP - D), and
+//                    accumulates dK^T += Q^T dS.
 // Computing dQ apart from dK/dV costs a second recomputation of S and dP (7
 // matrix products per (query tile, key tile) pair instead of 5) and saves a
 // float atomic read-modify-write of dQ for every such pair.
@@ -31,9 +34,10 @@
 //    and dO fragments stay in registers, as Q does in the forward); dS^T is
 //    the B operand of dQ^T += K^T dS^T straight from the accumulators, and
 //    K^T comes from transposing LDS reads of the K tile.
-//  * dK/dV kernel: S = Q K^T and dP = dO V^T put one key per lane (K and V
-//    fragments in registers); P and dS are the B operands of dV^T += dO^T P
-//    and dK^T += Q^T dS, and dO^T, Q^T come from transposing reads.
+//  * dK/dV kernel: S = Q K^T (P wave) and dP = dO V^T (dS wave) put one key
+//    per lane (K or V fragments in registers); P and dS are the B operands of
+//    dV^T += dO^T P and dK^T += Q^T dS, and dO^T, Q^T come from transposing
+//    reads.
 // Every streamed tile is read both ways -- MFMA row reads (16 consecutive
 // rows at one 16-byte chunk) and transposing reads (4 consecutive rows x 4
 // consecutive chunks) -- so tiles are stored row-major with an XOR swizzle of
@@ -50,7 +54,6 @@ namespace attn {
 
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct BwdCfg {
@@ -65,7 +68,6 @@ struct BwdCfg {
     static constexpr int TILE_BYTES = BT * ROW_BYTES;
     static constexpr int RPD = 1024 / ROW_BYTES;      // rows per wave-wide 16 B/lane copy
     static constexpr int COPIES = TILE_BYTES / 1024;  // wave-wide copies per tile
-    static constexpr int PAIR_BYTES = BT * 8;         // (LSE log2 e, D) of a tile's rows
 };
 
 // XOR applied to the 16-byte chunk index of tile row `row`, chosen so that
@@ -185,13 +187,6 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, char* tile, 
     }
 }
 
-// (LSE log2 e, D) of tile rows row0 .. row0 + BT - 1 (clamped): 4 bytes per
-// lane, lane l copies float l of the tile's BT pairs.
-__device__ __forceinline__ void copy_pairs(__amdgpu_buffer_rsrc_t r, char* dst, int row0, int n_rows, int lane)
-{
-    const uint32_t row = (uint32_t)min(row0 + (lane >> 1), n_rows - 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst), 4, row * 8u + (uint32_t)(lane & 1) * 4u, 0, 0, 0);
-}
 #endif
 
 // Runs tiles [tb, te) of a stream of nt tiles double-buffered in b0 / b1
@@ -342,7 +337,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
     if (valid) {
         const float l = a.lse[(int64_t)bh * N + qi];
         lse2 = (l == -INFINITY) ? INFINITY : l * kLog2e;    // a row with no key has P = 0
-        if (g == 0) *(f32x2*)(a.ws + ((int64_t)bh * N + qi) * 2) = f32x2{lse2, dd};
+        if (g == 0) {                                       // planar: lse2 of the head's rows, then D
+            a.ws[(int64_t)bh * N * 2 + qi] = lse2;
+            a.ws[(int64_t)bh * N * 2 + N + qi] = dd;
+        }
     }
 
     // ---- key loop -------------------------------------------------------------
@@ -402,293 +400,257 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  A streamed query tile holds QB blocks of 32 queries (QT = 32 QB
-// rows of Q, then QT rows of dO, then the rows' (lse2, D) pairs).  The QB
-// blocks are independent until they add into dK / dV, which gives the one
-// wave of a SIMD (the accumulators and K/V fragments take ~350 registers)
-// work to overlap: the exponentials of one block with the MFMAs of another.
-template <int D, int QB>
-struct QTileCfg {
-    static constexpr int QT = 32 * QB;                              // query rows per tile
-    static constexpr int TILE_BYTES = QT * BwdCfg<D>::ROW_BYTES;    // one of Q or dO
-    static constexpr int COPIES = TILE_BYTES / 1024;
-    static constexpr int PAIR_BYTES = QT * 8;
-    static constexpr int BUF_BYTES = 2 * TILE_BYTES + PAIR_BYTES;
-};
+// dK, dV with two wave roles per 32-key block.  A workgroup of 8 waves owns
+// 128 keys; wave k (0..3) is the P wave of keys k0 + 32k .. + 31 and wave
+// 4 + k its dS wave (the hardware puts both on SIMD k).  With one wave per
+// key block holding K, V, dK and dV (~350 registers) only one wave fits a
+// SIMD and nothing hides its exponentials; split in two, two waves fit.
+// Per 32-query tile:
+//   P wave : S = Q K^T, P = exp2(s c2 - lse2) (masked), P to LDS (bf16),
+//            dV^T += dO^T P
+//   dS wave: dP = dO V^T; after the barrier that publishes P,
+//            dS = P (dP - D), dK^T += Q^T dS
+// Each wave holds half the stationary state (K or V, dV or dK), which leaves
+// room for two waves per SIMD: one's exponentials or dS run beside the
+// other's MFMAs.  The workspace rows are planar here: lse2 of a head's N rows,
+// then D of its N rows.
+constexpr int kRoleKB = 4;                     // 32-key blocks per workgroup
+constexpr int kRoleWaves = 2 * kRoleKB;
 
-// One query tile for this wave's 32 keys, in stages over its 32-query
-// blocks.  Lane: key `key`; accumulator register i of block sb of S / dP
-// holds query q0 + 32 sb + (i/4)*8 + 4g + i%4.  MASKED: queries >= n, and
-// (causal) queries before the key, get P = 0.
-template <int D>
-struct DkdvBlock {
-    f32x16 s, dp;                          // S and dP of one 32-query block
-};
-
-template <int D>
-struct DkdvOperands {
-    bf16x8 tq[2][BwdCfg<D>::DBLK];         // Q^T (transposing reads), per half-block h and d-block
-    bf16x8 tdo[2][BwdCfg<D>::DBLK];        // dO^T
-    f32x4 pr[8];                           // (lse2, D) pairs of the lane's 16 queries
-};
-
-// S = Q K^T, dP = dO V^T for block sb (row reads issued first, then the
-// MFMAs, so the LDS latency is paid once per block).
-template <int D>
-__device__ __forceinline__ void dkdv_scores(DkdvBlock<D>& blk, const bf16x8 (&kf)[BwdCfg<D>::KSTEPS],
-                                            const bf16x8 (&vf)[BwdCfg<D>::KSTEPS], const char* tq, const char* td,
-                                            const LaneOfs<D>& lo, int sb)
+#if defined(__HIP_DEVICE_COMPILE__)
+// lse2 (lanes 0..31) and D (lanes 32..63) of rows row0 .. row0 + 31, clamped.
+__device__ __forceinline__ void copy_rowstats(__amdgpu_buffer_rsrc_t r, char* dst, int row0, int n_rows, int lane)
 {
-    using C = BwdCfg<D>;
-    bf16x8 x[C::KSTEPS], y[C::KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        x[ks] = lds_row(tq + 32 * sb * C::ROW_BYTES + lo.row[ks]);
-        y[ks] = lds_row(td + 32 * sb * C::ROW_BYTES + lo.row[ks]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    blk.s = f32x16{};
-    blk.dp = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        blk.s = mfma32(x[ks], kf[ks], blk.s);
-        blk.dp = mfma32(y[ks], vf[ks], blk.dp);
-    }
+    const uint32_t row = (uint32_t)min(row0 + (lane & 31), n_rows - 1);
+    const uint32_t off = ((lane >> 5) ? (uint32_t)n_rows * 4u : 0u) + row * 4u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst), 4, off, 0, 0, 0);
 }
-
-// The transposed Q / dO operands and the (lse2, D) pairs of block sb.
-template <int D>
-__device__ __forceinline__ void dkdv_load(DkdvOperands<D>& op, const char* tq, const char* td, const float* pr,
-                                          const LaneOfs<D>& lo, int lane, int sb)
-{
-    using C = BwdCfg<D>;
-    const int g = lane >> 5;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int rofs = (32 * sb + 16 * h) * C::ROW_BYTES;
-#pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) {
-            op.tdo[h][db] = lds_tr(td + rofs + lo.tlo[db], td + rofs + lo.thi[db]);
-            op.tq[h][db] = lds_tr(tq + rofs + lo.tlo[db], tq + rofs + lo.thi[db]);
-        }
-    }
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-        // registers 4 a4 .. 4 a4 + 3 <-> block rows 8 a4 + 4 g .. + 3
-        const float* pp = pr + (32 * sb + a4 * 8 + 4 * g) * 2;
-        op.pr[2 * a4] = *(const f32x4*)(pp);
-        op.pr[2 * a4 + 1] = *(const f32x4*)(pp + 4);
-    }
-}
-
-// P = exp2(s c2 - lse2) (masked), dS = P (dP - D), both rounded to bf16 in
-// the B-operand layout.
-template <int D, bool MASKED>
-__device__ __forceinline__ void dkdv_softmax(bf16x2 (&pk)[8], bf16x2 (&dsk)[8], const DkdvBlock<D>& blk,
-                                             const DkdvOperands<D>& op, int lane, float c2, int q0, int key, int n,
-                                             int causal, int sb)
-{
-    const int g = lane >> 5;
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-        const f32x4 x0 = op.pr[2 * a4], x1 = op.pr[2 * a4 + 1];
-        const float l2[4] = {x0[0], x0[2], x1[0], x1[2]};
-        const float dd[4] = {x0[1], x0[3], x1[1], x1[3]};
-        float p[4], ds[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * a4 + j;
-            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(blk.s[i], c2, -l2[j]));
-            if (MASKED) {
-                const int qq = q0 + 32 * sb + a4 * 8 + 4 * g + j;
-                pj = (qq < n && (!causal || key <= qq)) ? pj : 0.f;
-            }
-            p[j] = pj;
-            ds[j] = pj * (blk.dp[i] - dd[j]);
-        }
-        pk[2 * a4] = pack2(p[0], p[1]);
-        pk[2 * a4 + 1] = pack2(p[2], p[3]);
-        dsk[2 * a4] = pack2(ds[0], ds[1]);
-        dsk[2 * a4 + 1] = pack2(ds[2], ds[3]);
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void dkdv_accumulate(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
-                                                const bf16x2 (&pk)[8], const bf16x2 (&dsk)[8],
-                                                const DkdvOperands<D>& op)
-{
-    using C = BwdCfg<D>;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const bf16x8 bp = cat8(pk[4 * h + 0], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
-        const bf16x8 bs = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
-#pragma unroll
-        for (int db = 0; db < C::DBLK; ++db) {
-            dv[db] = mfma32(op.tdo[h][db], bp, dv[db]);
-            dk[db] = mfma32(op.tq[h][db], bs, dk[db]);
-        }
-    }
-}
-
-// The stages are fenced so that the scheduler keeps each block's LDS reads
-// ahead of the MFMAs that use them (left alone it issues every transposing
-// read next to its MFMA and waits for it), and so that each block's
-// exponentials sit in the same stretch as the other block's MFMAs, which the
-// one wave of the SIMD runs while the MFMAs execute:
-//   S/dP(0) | loads(1), T(0) | S/dP(1) + softmax(0) | T(1) | dV/dK(0) + softmax(1) | dV/dK(1)
-// (T: transposed operands and pairs).  With one block per tile the stages
-// simply run in order.
-template <int D, int QB, bool MASKED>
-__device__ __forceinline__ void dkdv_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], f32x16 (&dv)[BwdCfg<D>::DBLK],
-                                          const bf16x8 (&kf)[BwdCfg<D>::KSTEPS], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
-                                          const char* buf, const LaneOfs<D>& lo, int lane, float c2, int q0, int key,
-                                          int n, int causal)
-{
-    using Q = QTileCfg<D, QB>;
-    static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per tile");
-    const char* tq = buf;
-    const char* td = buf + Q::TILE_BYTES;
-    const float* pr = (const float*)(buf + 2 * Q::TILE_BYTES);
-    DkdvBlock<D> b0, b1;
-    DkdvOperands<D> o0, o1;
-    bf16x2 pk0[8], dsk0[8], pk1[8], dsk1[8];
-    dkdv_scores(b0, kf, vf, tq, td, lo, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    dkdv_load(o0, tq, td, pr, lo, lane, 0);
-    if (QB == 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_scores(b1, kf, vf, tq, td, lo, 1);
-    }
-    dkdv_softmax<D, MASKED>(pk0, dsk0, b0, o0, lane, c2, q0, key, n, causal, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (QB == 2) {
-        dkdv_load(o1, tq, td, pr, lo, lane, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_softmax<D, MASKED>(pk1, dsk1, b1, o1, lane, c2, q0, key, n, causal, 1);
-    }
-    dkdv_accumulate(dk, dv, pk0, dsk0, o0);
-    if (QB == 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        dkdv_accumulate(dk, dv, pk1, dsk1, o1);
-    }
-}
-
-#ifndef ATTN_BWD_QB
-#define ATTN_BWD_QB 2
 #endif
 
 template <int D>
-__global__ __launch_bounds__(256, D == 128 ? 1 : 2) void bwd_dkdv_kernel(BwdArgs a, int n_work)
+struct RoleCfg {
+    static constexpr int TILE_BYTES = 32 * BwdCfg<D>::ROW_BYTES;   // 32 rows of Q or of dO
+    static constexpr int COPIES = TILE_BYTES / 1024;
+    static constexpr int STAT_BYTES = 256;                          // lse2[32], D[32]
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES + STAT_BYTES;
+    static constexpr int XCH_BYTES = 64 * 32;                       // P of one key block: 16 bf16 per lane
+};
+
+// P wave, one tile: S = Q K^T, P to LDS, the barrier that publishes it,
+// then dV^T += dO^T P.
+template <int D, bool MASKED>
+__device__ __forceinline__ void role_p_tile(f32x16 (&dv)[BwdCfg<D>::DBLK], const bf16x8 (&kf)[BwdCfg<D>::KSTEPS],
+                                            const char* buf, char* xch, const LaneOfs<D>& lo, int lane, float c2,
+                                            int q0, int key, int n, int causal)
 {
     using C = BwdCfg<D>;
-    constexpr int QB = (D == 128) ? ATTN_BWD_QB : 1;
-    using Q = QTileCfg<D, QB>;
-    __shared__ __attribute__((aligned(16))) char lds0[Q::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[Q::BUF_BYTES];
+    using R = RoleCfg<D>;
+    const char* tq = buf;
+    const char* td = buf + R::TILE_BYTES;
+    const float* st = (const float*)(buf + 2 * R::TILE_BYTES);
+    const int g = lane >> 5;
+    f32x16 s = f32x16{};
+    {
+        bf16x8 x[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) x[ks] = lds_row(tq + lo.row[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) s = mfma32(x[ks], kf[ks], s);
+    }
+    bf16x8 tdo[2][C::DBLK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+            tdo[h][db] = lds_tr(td + 16 * h * C::ROW_BYTES + lo.tlo[db], td + 16 * h * C::ROW_BYTES + lo.thi[db]);
+    f32x4 l2[4];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) l2[a4] = *(const f32x4*)(st + a4 * 8 + 4 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x2 pk[8];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        float p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float pj = __builtin_amdgcn_exp2f(__builtin_fmaf(s[4 * a4 + j], c2, -l2[a4][j]));
+            if (MASKED) {
+                const int qq = q0 + a4 * 8 + 4 * g + j;
+                pj = (qq < n && (!causal || key <= qq)) ? pj : 0.f;
+            }
+            p[j] = pj;
+        }
+        pk[2 * a4] = pack2(p[0], p[1]);
+        pk[2 * a4 + 1] = pack2(p[2], p[3]);
+    }
+    *(bf16x8*)(xch + lane * 32) = cat8(pk[0], pk[1], pk[2], pk[3]);
+    *(bf16x8*)(xch + lane * 32 + 16) = cat8(pk[4], pk[5], pk[6], pk[7]);
+    __syncthreads();   // P of this tile is visible to the dS wave
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16x8 bp = cat8(pk[4 * h + 0], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) dv[db] = mfma32(tdo[h][db], bp, dv[db]);
+    }
+}
+
+// dS wave, one tile: dP = dO V^T, the barrier after which P is in LDS,
+// dS = P (dP - D), dK^T += Q^T dS.
+template <int D>
+__device__ __forceinline__ void role_ds_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
+                                             const char* buf, const char* xch, const LaneOfs<D>& lo, int lane)
+{
+    using C = BwdCfg<D>;
+    using R = RoleCfg<D>;
+    const char* tq = buf;
+    const char* td = buf + R::TILE_BYTES;
+    const float* st = (const float*)(buf + 2 * R::TILE_BYTES);
+    const int g = lane >> 5;
+    f32x16 dp = f32x16{};
+    {
+        bf16x8 y[C::KSTEPS];
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) y[ks] = lds_row(td + lo.row[ks]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks) dp = mfma32(y[ks], vf[ks], dp);
+    }
+    bf16x8 tqo[2][C::DBLK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db)
+            tqo[h][db] = lds_tr(tq + 16 * h * C::ROW_BYTES + lo.tlo[db], tq + 16 * h * C::ROW_BYTES + lo.thi[db]);
+    f32x4 dd[4];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) dd[a4] = *(const f32x4*)(st + 32 + a4 * 8 + 4 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();   // the P wave's P of this tile is in xch
+    const u32x4 p0 = *(const u32x4*)(xch + lane * 32);
+    const u32x4 p1 = *(const u32x4*)(xch + lane * 32 + 16);
+    const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+    bf16x2 dsk[8];
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+        float ds[4];
+#pragma unroll
+        for (int j = 0; j < 4; j += 2) {
+            const uint32_t w2 = pw[2 * a4 + j / 2];
+            ds[j] = bf16lo(w2) * (dp[4 * a4 + j] - dd[a4][j]);
+            ds[j + 1] = bf16hi(w2) * (dp[4 * a4 + j + 1] - dd[a4][j + 1]);
+        }
+        dsk[2 * a4] = pack2(ds[0], ds[1]);
+        dsk[2 * a4 + 1] = pack2(ds[2], ds[3]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const bf16x8 bs = cat8(dsk[4 * h + 0], dsk[4 * h + 1], dsk[4 * h + 2], dsk[4 * h + 3]);
+#pragma unroll
+        for (int db = 0; db < C::DBLK; ++db) dk[db] = mfma32(tqo[h][db], bs, dk[db]);
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kRoleWaves, 1) void bwd_dkdv_kernel(BwdArgs a, int n_work)
+{
+    using C = BwdCfg<D>;
+    using R = RoleCfg<D>;
+    constexpr int KB = kRoleKB, BLK = 32 * KB;
+    __shared__ __attribute__((aligned(16))) char lds0[R::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[R::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char xch_all[KB * R::XCH_BYTES];
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= n_work) return;
     const int N = a.N;
-    const int nkb = (N + C::BLK - 1) / C::BLK;
+    const int nkb = (N + BLK - 1) / BLK;
     const int bhk = L / nkb;
-    const int k0 = (L % nkb) * C::BLK;                      // heaviest (most query tiles) first
+    const int k0 = (L % nkb) * BLK;                         // heaviest (most query tiles) first
     const int b = bhk / a.H_kv, hk = bhk % a.H_kv;
     const int G = a.H / a.H_kv;
     const int64_t kv_off = (int64_t)bhk * N * C::ROW_BYTES;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kb = w % KB;                                  // key block of this wave
+    const bool p_role = w < KB;
     const int g = lane >> 5, r32 = lane & 31;
-    const int key = k0 + 32 * w + r32;                      // this lane's key
+    const int key = k0 + 32 * kb + r32;                     // this lane's key
     const bool kvalid = key < N;
     const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+    char* xch = xch_all + kb * R::XCH_BYTES;
 
-    bf16x8 kf[C::KSTEPS], vf[C::KSTEPS];
+    // K (P wave) or V (dS wave) fragments of the lane's key
+    bf16x8 kvf[C::KSTEPS];
     {
-        const char* kp = (const char*)a.k + kv_off + (int64_t)key * C::ROW_BYTES;
-        const char* vp = (const char*)a.v + kv_off + (int64_t)key * C::ROW_BYTES;
+        const char* src = (const char*)(p_role ? a.k : a.v) + kv_off + (int64_t)key * C::ROW_BYTES;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-            if (kvalid) {
-                x = *(const u32x4*)(kp + (ks * 2 + g) * 16);
-                y = *(const u32x4*)(vp + (ks * 2 + g) * 16);
-            }
-            kf[ks] = as_bf16x8(x);
-            vf[ks] = as_bf16x8(y);
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (kvalid) x = *(const u32x4*)(src + (ks * 2 + g) * 16);
+            kvf[ks] = as_bf16x8(x);
         }
     }
-    f32x16 dk[C::DBLK], dv[C::DBLK];
+    f32x16 acc[C::DBLK];                                    // dV (P wave) or dK (dS wave)
 #pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) {
-        dk[db] = f32x16{};
-        dv[db] = f32x16{};
-    }
+    for (int db = 0; db < C::DBLK; ++db) acc[db] = f32x16{};
 
-    // query tiles [qt0, nqt) of every query head of the group
-    const int qt0 = a.causal ? k0 / Q::QT : 0;
-    const int nqt = (N + Q::QT - 1) / Q::QT;
+    const int qt0 = a.causal ? k0 / 32 : 0;
+    const int nqt = (N + 31) / 32;
     const int per_head = nqt - qt0;
     const int nt = G * per_head;
-    const int sel = w >> 1;                                 // waves 0, 1 copy Q; 2, 3 copy dO
-    const int c0 = (w & 1) * (Q::COPIES / 2);
+    const int sel = w / KB;                                 // P waves copy Q, dS waves copy dO
+    const int c0 = (w % KB) * (R::COPIES / KB);
     auto issue = [&](char* buf, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)
         const int gh = t / per_head, qt = qt0 + t % per_head;
         const int64_t bh = (int64_t)b * a.H + hk * G + gh;
         const char* src = (const char*)(sel ? a.dout : a.q) + bh * N * C::ROW_BYTES;
-        copy_tile<D, Q::COPIES / 2>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * Q::TILE_BYTES, qt * Q::QT,
-                                    N, c0, lane);
-        if (w < QB)
-            copy_pairs(raw_rsrc(a.ws + bh * N * 2, (uint32_t)N * 8u), buf + 2 * Q::TILE_BYTES + w * 256,
-                       qt * Q::QT + 32 * w, N, lane);
+        copy_tile<D, R::COPIES / KB>(raw_rsrc(src, (uint32_t)N * C::ROW_BYTES), buf + sel * R::TILE_BYTES, qt * 32,
+                                     N, c0, lane);
+        if (w == 0)
+            copy_rowstats(raw_rsrc(a.ws + bh * N * 2, (uint32_t)N * 8u), buf + 2 * R::TILE_BYTES, qt * 32, N, lane);
 #endif
     };
-    auto q_of = [&](int t) { return (qt0 + t % per_head) * Q::QT; };
+    auto q_of = [&](int t) { return (qt0 + t % per_head) * 32; };
     const LaneOfs<D> lo = lane_offsets<D>(lane);
-    auto full = [&](const char* buf, int t) {
-        dkdv_tile<D, QB, false>(dk, dv, kf, vf, buf, lo, lane, c2, q_of(t), key, N, a.causal);
+    auto p_full = [&](const char* buf, int t) {
+        role_p_tile<D, false>(acc, kvf, buf, xch, lo, lane, c2, q_of(t), key, N, a.causal);
     };
-    auto masked = [&](const char* buf, int t) {
-        dkdv_tile<D, QB, true>(dk, dv, kf, vf, buf, lo, lane, c2, q_of(t), key, N, a.causal);
+    auto p_masked = [&](const char* buf, int t) {
+        role_p_tile<D, true>(acc, kvf, buf, xch, lo, lane, c2, q_of(t), key, N, a.causal);
     };
-    auto none = [&](const char*, int) {};
-    // Per query head: the first tiles of a causal launch, up to the block's
-    // last key (they hold the diagonal of every wave's keys), and a ragged
-    // last tile are masked, for every wave (a tile wholly before a wave's
-    // keys adds exactly nothing); the tiles between are seen in full.  Waves
-    // with no valid key only take part in the copies and barriers.
-    const int n_head_masked = a.causal ? min(C::BLK / Q::QT, per_head) : 0;
-    const int n_tail_masked = (N % Q::QT != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
+    auto ds_step = [&](const char* buf, int) { role_ds_tile<D>(acc, kvf, buf, xch, lo, lane); };
+    auto none = [&](const char*, int) { __syncthreads(); };
+    const int n_head_masked = a.causal ? min(KB, per_head) : 0;
+    const int n_tail_masked = (N % 32 != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
     if (nt > 0) {
         issue(lds0, 0);
         publish_copies();
     }
-    if (k0 + 32 * w < N) {
+    if (k0 + 32 * kb >= N) {
+        run_tiles(lds0, lds1, 0, nt, nt, issue, none);
+    } else if (p_role) {
         for (int gh = 0; gh < G; ++gh) {
             const int tb = gh * per_head;
-            run_tiles(lds0, lds1, tb, tb + n_head_masked, nt, issue, masked);
-            run_tiles(lds0, lds1, tb + n_head_masked, tb + per_head - n_tail_masked, nt, issue, full);
-            run_tiles(lds0, lds1, tb + per_head - n_tail_masked, tb + per_head, nt, issue, masked);
+            run_tiles(lds0, lds1, tb, tb + n_head_masked, nt, issue, p_masked);
+            run_tiles(lds0, lds1, tb + n_head_masked, tb + per_head - n_tail_masked, nt, issue, p_full);
+            run_tiles(lds0, lds1, tb + per_head - n_tail_masked, tb + per_head, nt, issue, p_masked);
         }
     } else {
-        run_tiles(lds0, lds1, 0, nt, nt, issue, none);
+        run_tiles(lds0, lds1, 0, nt, nt, issue, ds_step);
     }
 
-    // ---- dK = scale * dK^T, dV = dV^T, bf16 -------------------------------------
     if (kvalid) {
-        char* krow = (char*)a.dk + kv_off + (int64_t)key * C::ROW_BYTES;
-        char* vrow = (char*)a.dv + kv_off + (int64_t)key * C::ROW_BYTES;
+        char* row = (char*)(p_role ? a.dv : a.dk) + kv_off + (int64_t)key * C::ROW_BYTES;
+        const float f = p_role ? 1.f : a.scale;
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                u32x2 wk, wv;
-                wk[0] = pack_bf16(dk[db][r * 4 + 0] * a.scale, dk[db][r * 4 + 1] * a.scale);
-                wk[1] = pack_bf16(dk[db][r * 4 + 2] * a.scale, dk[db][r * 4 + 3] * a.scale);
-                wv[0] = pack_bf16(dv[db][r * 4 + 0], dv[db][r * 4 + 1]);
-                wv[1] = pack_bf16(dv[db][r * 4 + 2], dv[db][r * 4 + 3]);
-                *(u32x2*)(krow + (db * 32 + r * 8 + g * 4) * 2) = wk;
-                *(u32x2*)(vrow + (db * 32 + r * 8 + g * 4) * 2) = wv;
+                u32x2 w2;
+                w2[0] = pack_bf16(acc[db][r * 4 + 0] * f, acc[db][r * 4 + 1] * f);
+                w2[1] = pack_bf16(acc[db][r * 4 + 2] * f, acc[db][r * 4 + 3] * f);
+                *(u32x2*)(row + (db * 32 + r * 8 + g * 4) * 2) = w2;
             }
     }
 }
@@ -700,17 +662,16 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
     constexpr int BLK = 128;
     const int64_t nblk = (a.N + BLK - 1) / BLK;
     const int64_t n_dq = (int64_t)a.B * a.H * nblk;
-    const int64_t n_kv = (int64_t)a.B * a.H_kv * nblk;
+    const int64_t n_kv = (int64_t)a.B * a.H_kv * ((a.N + 32 * kRoleKB - 1) / (32 * kRoleKB));
     if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
     const int grid_dq = (int)((n_dq + 7) / 8 * 8);
     const int grid_kv = (int)((n_kv + 7) / 8 * 8);
     if (a.d == 128) {
         hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a, (int)n_dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(grid_kv), dim3(BwdCfg<128>::kThreads), 0, stream, a,
-                           (int)n_kv);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
     } else {
         hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a, (int)n_dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(grid_kv), dim3(BwdCfg<64>::kThreads), 0, stream, a, (int)n_kv);
+        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

@@ -19,7 +19,7 @@ struct BwdArgs {
     void* dq;            // [B, H, N, d] bf16
     void* dk;            // [B, H_kv, N, d] bf16
     void* dv;            // [B, H_kv, N, d] bf16
-    float* ws;           // [B * H, N, 2] fp32: (lse * log2 e, D = dO . O) per query row
+    float* ws;           // [B * H][2][N] fp32: lse * log2 e of each query row, then D = dO . O
     int B, H, H_kv, N, d;
     float scale;
     int causal;
