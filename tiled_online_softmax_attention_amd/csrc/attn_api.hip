@@ -91,6 +91,11 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
         if (env && *env) pair = atoi(env) ? 1 : 0;
         if (!a.causal || N <= 128) pair = 0;
         a.pair = pair;
+        // tile order of small causal grids (see launch_prefill);
+        // ATTN_PREFILL_ORDER=0 / 1 forces heavy-first / complementary
+        a.order = -1;
+        const char* oenv = getenv("ATTN_PREFILL_ORDER");
+        if (oenv && *oenv) a.order = atoi(oenv) ? 1 : 0;
     }
     rc = attn::launch_prefill(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);

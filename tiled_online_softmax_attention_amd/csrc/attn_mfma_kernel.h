@@ -184,26 +184,26 @@ __device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[Ti
     }
 }
 
-template <int D, class KV>
-__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
-                                               const TileBuffers& buf)
+// Per-wave set-up of one query tile: the Q^T fragments of this lane's query,
+// its key limit, and the key tiles the whole tile needs.  Returns the number
+// of key tiles from P.kv_begin; *n_full receives how many of them every row
+// of the tile sees in full (below the diagonal of its first row and before
+// kv_end).  cx.kv_begin / kv_end / ntile / voff are left to the caller.
+template <int D>
+__device__ __forceinline__ int init_query_tile(const TileProblem& P, WaveCtx& cx, bf16x8 (&qf)[TileCfg<D>::KSTEPS],
+                                               float c2_in, int w, int* n_full)
 {
     using C = TileCfg<D>;
-    WaveCtx cx;
     // scale * log2(e); a zero scale becomes a tiny positive factor (every
     // allowed key still gets p = 2^0 = 1 exactly, masked keys 2^-inf = 0)
     cx.c2 = fmaxf(c2_in, 1e-30f);
     cx.thr = kRescaleLog2 / cx.c2;
-    const int tid = threadIdx.x;
-    cx.lane = tid & 63;
+    cx.lane = threadIdx.x & 63;
+    cx.w = w;
     const int g = cx.lane >> 5, r32 = cx.lane & 31;
-    cx.w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int qrow = cx.w * 32 + r32;        // this lane's query row in the tile
+    const int qrow = w * 32 + r32;            // this lane's query row in the tile
     const int qpos = qrow / P.rows_per_pos, qhead = qrow % P.rows_per_pos;
     const int64_t qoff = qpos * P.q_stride + qhead * P.q_hstride;
-
-    // ---- Q^T fragments, key limit ---------------------------------------------
-    bf16x8 qf[C::KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < C::KSTEPS; ++ks) {
         u32x4 val = {0u, 0u, 0u, 0u};
@@ -215,37 +215,50 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
     // keys the whole tile needs
     const int t_end =
         P.causal ? min(P.kv_end, P.q_pos0 + (max(P.n_rows, 1) - 1) / P.rows_per_pos + 1) : P.kv_end;
-    cx.kv_begin = P.kv_begin;
-    cx.kv_end = P.kv_end;
-    cx.ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
-    cx.voff = (cx.w >= C::GROUPS)
-                  ? (uint32_t)v_dma_row<D>(cx.lane) * C::ROW_BYTES + v_dma_col<D>(cx.lane)
-                  : (uint32_t)k_dma_row<D>(cx.lane) * C::ROW_BYTES + k_dma_col<D>(cx.lane);
-
-    WaveState<D> ws;
-#pragma unroll
-    for (int db = 0; db < C::DBLK; ++db) ws.o[db] = f32x16{};
-    ws.m = -INFINITY;
-    ws.l = 0.f;
-
+    const int ntile = (t_end > P.kv_begin) ? (t_end - P.kv_begin + C::BN - 1) / C::BN : 0;
     // Tiles [0, n_full) are seen in full by every row of the tile (below the
-    // diagonal of query row 0 and before kv_end): no masking.  The rest
-    // (diagonal and tail) go through the masked step, for every wave: a tile
-    // fully masked for a lane adds exactly nothing (p = 0, and the offset
-    // only moves on a finite score), and waves past the last valid row run on
-    // zero queries and never store.  Keeping the per-tile code free of
-    // per-wave branches also keeps O in one register set across the loop.
-    int n_full = 0;
+    // diagonal of query row 0 and before kv_end).  The rest (diagonal and
+    // tail) go through the masked step, for every wave: a tile fully masked
+    // for a lane adds exactly nothing (p = 0, and the offset only moves on a
+    // finite score), and waves past the last valid row run on zero queries
+    // and never store.  Keeping the per-tile code free of per-wave branches
+    // also keeps O in one register set across the loop.
+    int nf = 0;
     {
         const int lim = P.causal ? min(P.kv_end, P.q_pos0 + 1) : P.kv_end;
-        if (lim > P.kv_begin) n_full = min(cx.ntile, (lim - P.kv_begin) / C::BN);
+        if (lim > P.kv_begin) nf = min(ntile, (lim - P.kv_begin) / C::BN);
     }
-    // Waves with no valid row (the tail of a partial tile, or the rows past a
-    // short grouped-query tile) only take part in the copies and barriers.
-    if (cx.w * 32 < P.n_rows) key_loop<D, true>(ws, qf, cx, kv, buf, n_full);
-    else key_loop<D, false>(ws, qf, cx, kv, buf, n_full);
+    *n_full = nf;
+    return ntile;
+}
 
-    // ---- epilogue -------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ uint32_t copy_voff(int w, int lane)
+{
+    using C = TileCfg<D>;
+    return (w >= C::GROUPS) ? (uint32_t)v_dma_row<D>(lane) * C::ROW_BYTES + v_dma_col<D>(lane)
+                            : (uint32_t)k_dma_row<D>(lane) * C::ROW_BYTES + k_dma_col<D>(lane);
+}
+
+template <int D>
+__device__ __forceinline__ void clear_state(WaveState<D>& ws)
+{
+#pragma unroll
+    for (int db = 0; db < TileCfg<D>::DBLK; ++db) ws.o[db] = f32x16{};
+    ws.m = -INFINITY;
+    ws.l = 0.f;
+}
+
+// Epilogue of one wave: O / l (bf16, or fp32 partials) and the log-sum-exp
+// of its valid rows.
+template <int D>
+__device__ __forceinline__ void store_query_rows(const WaveState<D>& ws, const TileProblem& P, const TileOut& out,
+                                                 const WaveCtx& cx)
+{
+    using C = TileCfg<D>;
+    const int g = cx.lane >> 5, r32 = cx.lane & 31;
+    const int qrow = cx.w * 32 + r32;
+    const int qpos = qrow / P.rows_per_pos, qhead = qrow % P.rows_per_pos;
     const float l_tot = half_sum(ws.l);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < P.n_rows) {
@@ -280,6 +293,26 @@ __device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& k
                 (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
+}
+
+template <int D, class KV>
+__device__ __forceinline__ void run_query_tile(const TileProblem& P, const KV& kv, const TileOut& out, float c2_in,
+                                               const TileBuffers& buf)
+{
+    WaveCtx cx;
+    bf16x8 qf[TileCfg<D>::KSTEPS];
+    int n_full;
+    cx.ntile = init_query_tile<D>(P, cx, qf, c2_in, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), &n_full);
+    cx.kv_begin = P.kv_begin;
+    cx.kv_end = P.kv_end;
+    cx.voff = copy_voff<D>(cx.w, cx.lane);
+    WaveState<D> ws;
+    clear_state(ws);
+    // Waves with no valid row (the tail of a partial tile, or the rows past a
+    // short grouped-query tile) only take part in the copies and barriers.
+    if (cx.w * 32 < P.n_rows) key_loop<D, true>(ws, qf, cx, kv, buf, n_full);
+    else key_loop<D, false>(ws, qf, cx, kv, buf, n_full);
+    store_query_rows(ws, P, out, cx);
 }
 
 }  // namespace attn

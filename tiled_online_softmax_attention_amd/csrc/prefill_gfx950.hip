@@ -2,7 +2,7 @@
 //
 //  * bf16: fused MFMA kernel (attn_mfma_kernel.h), one workgroup of 4 waves per
 //    128-row query tile (or per pair of tiles, see below), K/V streamed through
-//    LDS in 64-key tiles, causal key tiles above the diagonal never loaded.
+//    LDS in 32-key tiles, causal key tiles above the diagonal never loaded.
 //  * fp32: a vector-ALU kernel with the same online softmax (fp32 storage has
 //    no dense matrix path worth using at these sizes).
 //
@@ -12,7 +12,12 @@
 // XCD's L2 for their K/V.  Within a head, tiles run heaviest (most keys) first.
 // For causal launches with few tiles ("pair" mode), a workgroup instead takes
 // tile t and tile n-1-t, so that every workgroup does the same number of key
-// tiles and the chip stays balanced.
+// tiles and the chip stays balanced.  A causal grid of about one dispatch
+// round (all its workgroups resident at once, two or three per CU) instead
+// deals each XCD's tiles in a complementary order -- the heavy half
+// descending, then the light half ascending -- so that the workgroups one CU
+// receives together add up to the same work (heavy-first per head pairs
+// heavy with heavy there, and the most loaded CU sets the time).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,7 +60,19 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
     if (L >= a.n_work) return;
     const int nqt = (a.N + BM - 1) / BM;
     const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
-    const int bh = L / per_bh, t = L % per_bh;
+    int bh = L / per_bh, t = L % per_bh;
+    if (!PAIR && a.order == 1) {
+        // Complementary order: an XCD's share is whole heads; position j of
+        // the share takes the (j / heads)-th tile of the sequence heaviest,
+        // next heaviest, ... down to the middle, then lightest upwards, so
+        // that positions j and j + share/2 (the two workgroups one CU
+        // receives when the grid fits one dispatch round) sum to the same
+        // work.
+        const int per = gridDim.x >> 3, hpx = per / nqt;
+        const int j = blockIdx.x >> 3, k = j / hpx, half = nqt / 2;
+        bh = (blockIdx.x & 7) * hpx + j % hpx;
+        t = (k < half) ? k : (nqt - 1) - (k - half);   // tiles[0] = nqt - 1 - t below
+    }
     const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes, q and o
     const int64_t kv_off =                                 // bytes, k and v of this head's K/V head
         ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * a.N * D * 2;
@@ -95,6 +112,10 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
         run_query_tile<D>(P, kv, out, c2, buf);
     }
 }
+
+// Causal grids of at most this many query tiles (about one dispatch round)
+// take the complementary tile order.
+constexpr int64_t kOrderMaxTiles = 1024;
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64 query rows per workgroup, 4 threads per row (each owns d/4
@@ -186,6 +207,9 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
         const int grid = (int)((n_work + 7) / 8 * 8);
+        // complementary order needs whole heads per XCD share (grid = n_work, a multiple of 8 * nqt)
+        const bool can_order = a.causal && !a.pair && n_work % 8 == 0 && (n_work / 8) % nqt == 0;
+        a.order = can_order ? (a.order < 0 ? (n_work <= kOrderMaxTiles ? 1 : 0) : a.order) : 0;
 #define ATTN_LAUNCH_PREFILL(DD, PP) \
     hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
         if (a.d == 128) {
