@@ -495,8 +495,14 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         const int ppt = kTileRows / G;                 // query positions per tile
         p.nqt = (max_q_len + ppt - 1) / ppt;
         const int64_t items = (int64_t)num_seqs * p.nqt * H_kv;
+        // Decode-length queries (grouped heads on this path) leave one wave of
+        // the tile with rows, so a workgroup is latency-bound and more, shorter
+        // splits keep more of them in flight (64 requests x 4 K/V heads, 16-token
+        // pages: 1024-key splits 4.27 TB/s, 2048-key 3.50); longer queries
+        // have full tiles and want fewer partials to combine.
+        const int64_t target = (max_q_len <= kDecodeMaxQ) ? 4096 : 2048;
         S = 8192;
-        while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < 2048) S /= 2;
+        while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < target) S /= 2;
     }
     const int env = env_int("ATTN_SPLIT_TOKENS", 0);
     if (env > 0) S = env;
