@@ -76,7 +76,8 @@ struct GatherArgs {
 };
 
 constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode kernel ...
-constexpr int kDecodeMfmaGroup = 8; // ... unless this many query heads share a K/V head
+constexpr int kDecodeMfmaGroup = 4; // ... unless this many query heads share a K/V head
+constexpr int kChunkMaxSplit = 8192;  // most keys per split on the MFMA tile path (multiple of 64)
 
 PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len);
 

@@ -292,15 +292,23 @@ template <int D, int BS>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
     const char* vbase;
-    const int32_t* table;    // this request's block-table row
+    const int32_t* ptab;     // LDS copy of the block-table entries of pages p0, p0 + 1, ...
+    int p0;                  // first page of this workgroup's keys
     int64_t blk_bytes;
+    // The page of every key tile comes from the workgroup's LDS copy of its
+    // pages' table entries (staged once; a global table read at the head of
+    // each tile step would hold up that tile's copies by a memory latency).
+    __device__ __forceinline__ int64_t page_of(int key, int kv_end) const
+    {
+        return (int64_t)__builtin_amdgcn_readfirstlane(ptab[min(key, kv_end - 1) / BS - p0]);
+    }
     __device__ __forceinline__ const char* k_group(int key, int kv_end) const
     {
-        return kbase + (int64_t)table[min(key, kv_end - 1) / BS] * blk_bytes;
+        return kbase + page_of(key, kv_end) * blk_bytes;
     }
     __device__ __forceinline__ const char* v_group(int key, int kv_end) const
     {
-        return vbase + (int64_t)table[min(key, kv_end - 1) / BS] * blk_bytes;
+        return vbase + page_of(key, kv_end) * blk_bytes;
     }
     __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1) % BS; }
     __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
@@ -312,6 +320,7 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    __shared__ int32_t ptab[kChunkMaxSplit / BS];
     const TileBuffers buf{lds0, lds1};
     // A tile holds ppt query positions x G query heads (the heads of one K/V
     // group), so each K/V tile staged in LDS serves the whole group.
@@ -336,10 +345,18 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     const int64_t pos0 = prefix_len(a.q_lens, r, lane) + (int64_t)qt * ppt;   // packed row of the tile's first position
     const int h0 = hk * G;                             // first query head of the group
 
+    // this split's pages: [kv_begin, kv_end) is page-aligned at its start
+    // and spans at most kChunkMaxSplit keys (the plan caps the split size)
+    const int kb = split * S, ke = min(ctx, (split + 1) * S);
+    const int p0 = kb / BS, np = (ke - 1) / BS - p0 + 1;
+    const int32_t* table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
+    for (int i = threadIdx.x; i < np; i += C::kThreads) ptab[i] = table[p0 + i];
+    __syncthreads();
     PagedKV<D, BS> kv;
     kv.kbase = (const char*)a.k_pool + (int64_t)hk * BS * D * 2;
     kv.vbase = (const char*)a.v_pool + (int64_t)hk * BS * D * 2;
-    kv.table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
+    kv.ptab = ptab;
+    kv.p0 = p0;
     kv.blk_bytes = a.kv_block_stride * 2;
 
     TileProblem P;
@@ -350,8 +367,8 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     P.n_rows = min(ppt, ql - qt * ppt) * G;
     P.q_pos0 = ctx - ql + qt * ppt;
     P.causal = 1;
-    P.kv_begin = split * S;
-    P.kv_end = min(ctx, (split + 1) * S);
+    P.kv_begin = kb;
+    P.kv_end = ke;
     TileOut out;
     if (nsplit == 1) {
         out.o = (char*)a.o + (pos0 * a.H + h0) * D * 2;
@@ -506,6 +523,8 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     }
     const int env = env_int("ATTN_SPLIT_TOKENS", 0);
     if (env > 0) S = env;
+    // a tile-path workgroup stages its split's block-table entries in LDS
+    if (p.path == 1 && S > kChunkMaxSplit) S = kChunkMaxSplit;
     // whole pages, and whole 64-key tiles on the MFMA path
     const int unit = (p.path == 0) ? block_size : (block_size > 64 ? block_size : 64);
     S = ((S + unit - 1) / unit) * unit;
