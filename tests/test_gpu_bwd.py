@@ -143,3 +143,24 @@ def test_c3_bwd_full_size_sampled_rows():
     check_grad("c3 dq rows", gq, rq)
     check_grad("c3 dk rows", gk, rk)
     check_grad("c3 dv rows", gv, rv)
+
+
+def test_c3_gqa8_bwd_full_size_sampled_rows():
+    """The grouped-query variant of the same workload (32 query heads on 4
+    K/V heads) at full size: 24 seeded dQ rows, and dK/dV rows of keys that
+    the oracle can afford to visit with every query head of their group
+    (the last key, one 100 keys from the end, one in the last quarter)."""
+    cfg = inputs.C3_GQA8
+    log("c3 gqa8 bwd full size")
+    (q, k, v, do), (dq, dk, dv) = run(cfg, nan_outputs=False)
+    N = cfg.N
+    qs = inputs.sample_triples(cfg.seed + 60, 24, (cfg.B, cfg.H, N), edge=[(0, 31, N - 1), (9, 8, 0)])
+    ks = [(0, 0, N - 1), (15, 3, N - 100), (7, 2, 7 * N // 8 + 13)]
+    log("  oracle: %d dq rows, %d dk/dv rows" % (len(qs), len(ks)))
+    rq, rk, rv = oracle.attention_bwd_rows(q, k, v, do, cfg.scale, True, qs, ks)
+    gq = torch.stack([dq[b, h, i] for b, h, i in qs])
+    gk = torch.stack([dk[b, h, j] for b, h, j in ks])
+    gv = torch.stack([dv[b, h, j] for b, h, j in ks])
+    check_grad("c3 gqa8 dq rows", gq, rq)
+    check_grad("c3 gqa8 dk rows", gk, rk)
+    check_grad("c3 gqa8 dv rows", gv, rv)
