@@ -144,9 +144,10 @@ size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size,
  *   of a group is read from HBM once and reused through L2.
  * paged_attn_gqa_fwd: q, o packed [sum(q_lens), H, d], lse [sum(q_lens), H];
  *   the pool holds H_kv heads per block ([H_kv, block_size, d] per block, so
- *   kv_block_stride >= H_kv * block_size * d).  On the decode path (q_len <=
- *   4) one workgroup serves up to 8 query heads of a group, so each K/V page
- *   is read once for all of them.
+ *   kv_block_stride >= H_kv * block_size * d).  Each K/V page is read once
+ *   for all the query heads of a group that one workgroup serves: all of them
+ *   on the MFMA tile kernel (from 4 heads per group, or query lengths > 4),
+ *   up to 8 on the vector decode kernel (groups of 2, q_len <= 4).
  * paged_attn_gqa_workspace_bytes: the workspace paged_attn_gqa_fwd needs.
  * H % H_kv != 0 or H_kv < 1 is ATTN_ERR_SHAPE.
  */
