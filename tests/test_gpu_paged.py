@@ -86,8 +86,9 @@ def test_chunk_ragged(bs, d, split):
 
 @pytest.mark.parametrize("split", [64, 128, 192])
 def test_chunk_split_tile_counts(split):
-    """Splits of one, two and three 64-key tiles, with ragged tails: every
-    length of the software-pipelined key loop (one tile, odd and even counts)."""
+    """Splits of 64, 128 and 192 keys (2, 4 and 6 key tiles of 32), with
+    ragged tails: several lengths of the double-buffered key loop, odd and
+    even tile counts."""
     ctx = [300, 1200, 40, 130]
     ql = [300, 260, 7, 129]
     pi = make(ctx, ql, H=2, bs=32, seed=17)

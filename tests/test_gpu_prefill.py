@@ -101,8 +101,9 @@ def test_tile_order_bit_identical(B, H, N, d):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_key_tile_counts(N, d, causal):
-    """One to six 64-key tiles per query tile: odd and even tile counts and
-    the boundary between unmasked and masked tiles of the pipelined loop."""
+    """Two to twelve 32-key tiles per query tile: odd and even tile counts and
+    the boundary between unmasked and masked tiles of the double-buffered
+    key loop."""
     run_case(1, 2, N, d, torch.bfloat16, causal, 400 + N + d)
 
 

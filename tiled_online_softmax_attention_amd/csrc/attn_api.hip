@@ -82,7 +82,7 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
-    // bf16 query tiles: 128 rows (32 queries per wave, two workgroups per CU).
+    // bf16 query tiles: 128 rows (32 queries per wave, three workgroups per CU).
     // Pairing tiles t and n-1-t (equal work per workgroup) is opt-in for
     // causal launches with ATTN_PREFILL_PAIR=1.
     {

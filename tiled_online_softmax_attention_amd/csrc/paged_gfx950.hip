@@ -525,7 +525,8 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     if (env > 0) S = env;
     // a tile-path workgroup stages its split's block-table entries in LDS
     if (p.path == 1 && S > kChunkMaxSplit) S = kChunkMaxSplit;
-    // whole pages, and whole 64-key tiles on the MFMA path
+    // whole pages; on the MFMA path a multiple of 64 keys (whole pages of 16
+    // or 32 tokens, so every split starts on a page boundary)
     const int unit = (p.path == 0) ? block_size : (block_size > 64 ? block_size : 64);
     S = ((S + unit - 1) / unit) * unit;
     p.split_tokens = S;
