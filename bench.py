@@ -15,7 +15,10 @@ bounded sample of the same prefill workload as `cpu_baseline`.
 
 Other modes (--only): prefill, decode, c2, c5 (single workloads), append (KV
 append), gqa (grouped-query prefill and decode), bwd (the backward of the
-causal prefill, MHA and GQA-8).
+causal prefill, MHA and GQA-8), ceiling (the sustained bf16 matrix-core rate
+alone).  With the prefill, the line also carries roofline.mfma_sustained: the
+rate the matrix cores hold on random and on constant operands
+(attn_probe_mfma), i.e. how much of the published peak real data can reach.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -142,8 +145,59 @@ class EventTimer:
         e1.record()
         self.pairs.append((e0, e1))
 
+    def times_ms(self):
+        return sorted(a.elapsed_time(b) for a, b in self.pairs)
+
     def mean_ms(self):
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+        t = self.times_ms()
+        return sum(t) / max(1, len(t))
+
+    def median_ms(self):
+        t = self.times_ms()
+        return t[len(t) // 2] if len(t) % 2 else 0.5 * (t[len(t) // 2 - 1] + t[len(t) // 2])
+
+    def min_ms(self):
+        return self.times_ms()[0]
+
+
+def mfma_ceiling(torch, attn, dev, launches=10, warm=2, iters=163840, blocks=2048):
+    """Sustained rate of the bf16 matrix-core instruction the kernels use
+    (attn_probe_mfma) on random operands (seeded N(0,1) rounded to bf16, the
+    kind of data attention multiplies) and on constant operands.  The chip
+    lowers its clock to stay within its power limit, and random operands draw
+    more power, so the random-operand rate is the ceiling a bf16 contraction
+    can reach on real data.  A loop of nothing but MFMAs issues at a rate that
+    depends on where it lands in instruction memory, so each of the probe's
+    16 loop placements is tried (one untimed and two timed launches of about
+    20 ms) and the fastest is then timed over `launches` launches after `warm`
+    untimed ones (median)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(4242)
+    frags = {"random_operands": torch.randn(65536 * 8, generator=g, device=dev).to(torch.bfloat16),
+             "constant_operands": torch.full((65536 * 8,), 0.5, dtype=torch.bfloat16, device=dev)}
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+    def rate(f, placement, n_warm, n_timed):
+        t = EventTimer(torch)
+        flops = 0
+        for i in range(n_warm + n_timed):
+            e = t.start() if i >= n_warm else None
+            _, flops = attn.probe_mfma(f, iters, blocks, placement=placement, out=out)
+            if e is not None:
+                t.stop(e)
+        torch.cuda.synchronize()
+        return flops / (t.median_ms() * 1e-3) / 1e12
+
+    res = {}
+    for name, f in frags.items():
+        sweep = [rate(f, pl, 1, 2) for pl in range(attn.PROBE_PLACEMENTS)]
+        best = max(range(len(sweep)), key=lambda pl: sweep[pl])
+        res[name] = round(rate(f, best, warm, launches), 1)
+        res[name + "_placements"] = [round(x, 1) for x in sweep]
+    res["unit"] = "TFLOP/s"
+    res["kind"] = ("sustained v_mfma_f32_32x32x16_bf16 (attn_probe_mfma): 2048 x 4 waves, 4 accumulation chains "
+                   "per wave, ~20 ms launches, fastest of 16 loop placements")
+    return res
 
 
 def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle):
@@ -419,16 +473,39 @@ def bench_gqa(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_ceiling(args):
+    """--only ceiling: the sustained matrix-core rate alone (one JSON line)."""
+    import torch
+    import tiled_online_softmax_attention_amd as attn
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    attn.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    c = mfma_ceiling(torch, attn, dev, launches=args.steps, warm=args.warmup)
+    res = {"metric": "sustained bf16 MFMA TFLOP/s, 1 MI355X", "value": c["random_operands"], "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic", "config": {"workload": "attn_probe_mfma, 2048 x 256 lanes, 163840 MFMAs per wave"},
+           "peak": PEAK_BF16_TFLOPS, "frac": round(c["random_operands"] / PEAK_BF16_TFLOPS, 4), "ceiling": c}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the sustained matrix-core rate measurement (attn_probe_mfma)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa", "bwd"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa", "bwd", "ceiling"],
                     default="all")
     ap.add_argument("--bwd-mha-only", action="store_true",
                     help="--only bwd: skip the grouped-query variant (profiling runs)")
@@ -440,6 +517,8 @@ def main():
         return bench_gqa(args)
     if args.only == "bwd":
         return bench_bwd(args)
+    if args.only == "ceiling":
+        return bench_ceiling(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -484,6 +563,10 @@ def main():
         q2, k2, v2 = inputs.prefill_inputs(c2, dev)
         o2 = torch.empty_like(q2)
         l2 = torch.empty((c2.B, c2.H, c2.N), dtype=torch.float32, device=dev)
+        # C2's 67 MB of inputs and outputs fit in the 256 MB last-level cache:
+        # the cold variant overwrites 1 GiB between launches (outside the
+        # timed events) so that each launch starts from HBM.
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     if args.only == "c5":
         c5 = inputs.C5
         p5 = inputs.paged_inputs(c5, dev)
@@ -499,6 +582,7 @@ def main():
     t_pre = EventTimer(torch)
     t_dec = EventTimer(torch)
     t_aux = EventTimer(torch)
+    t_cold = EventTimer(torch)
 
     def step(record):
         if do_prefill:
@@ -517,6 +601,11 @@ def main():
             attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
             if record:
                 t_aux.stop(e)
+            flush.fill_(1.0)
+            e = t_cold.start() if record else None
+            attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
+            if record:
+                t_cold.stop(e)
         if args.only == "c5":
             e = t_aux.start() if record else None
             attn.paged_attention(p5.q, p5.pool, p5.block_table, p5.ctx_lens, p5.q_lens, p5.block_size, p5.scale,
@@ -550,6 +639,7 @@ def main():
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                            "kernel": "prefill_bf16_kernel<128>", "launch_ms": round(ms, 4),
+                           "launch_ms_median": round(t_pre.median_ms(), 4), "launch_ms_min": round(t_pre.min_ms(), 4),
                            "flops_per_launch": fl, "algorithmic_bytes_per_launch":
                                prefill_bytes(c3.B, c3.H, c3.N, c3.d)}
     if do_decode:
@@ -557,7 +647,8 @@ def main():
         nb = paged_bytes(ctx_list, ql_list, pi.H, pi.d, pi.block_size)
         gbs = nb / (ms * 1e-3) / 1e9
         res["decode"] = {"metric": "paged-decode KV GB/s", "value": round(gbs, 1), "unit": "GB/s",
-                         "launch_ms": round(ms, 4), "bytes_per_call": nb, "sum_ctx": sum(ctx_list),
+                         "launch_ms": round(ms, 4), "launch_ms_median": round(t_dec.median_ms(), 4),
+                         "launch_ms_min": round(t_dec.min_ms(), 4), "bytes_per_call": nb, "sum_ctx": sum(ctx_list),
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4),
                                       "traffic": read_traffic("decode_c4"),
@@ -571,6 +662,12 @@ def main():
         res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
         res["config"]["workload"] = "causal prefill bf16 1x32x2048x128"
         res["launch_ms"] = round(ms, 4)
+        res["launch_ms_median"] = round(t_aux.median_ms(), 4)
+        res["launch_ms_min"] = round(t_aux.min_ms(), 4)
+        ms_c = t_cold.mean_ms()
+        res["cold"] = {"value": round(fl / (ms_c * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "launch_ms": round(ms_c, 4),
+                       "launch_ms_median": round(t_cold.median_ms(), 4), "launch_ms_min": round(t_cold.min_ms(), 4),
+                       "note": "1 GiB written between launches, outside the timed events"}
     if args.only == "c5":
         ms = t_aux.mean_ms()
         fl = paged_flops(ctx5, ql5, p5.d, p5.H)
@@ -579,6 +676,14 @@ def main():
         res["config"]["workload"] = "paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], 32-token pages"
         res["launch_ms"] = round(ms, 4)
         res["kv_gbps"] = round(nb / (ms * 1e-3) / 1e9, 1)
+        res["launch_ms_median"] = round(t_aux.median_ms(), 4)
+        res["launch_ms_min"] = round(t_aux.min_ms(), 4)
+
+    if do_prefill and not args.no_ceiling:
+        print("measuring the sustained matrix-core rate", file=sys.stderr, flush=True)
+        ceil = mfma_ceiling(torch, attn, dev)
+        ceil["prefill_frac_of_random"] = round(res["roofline"]["achieved"] / ceil["random_operands"], 4)
+        res["roofline"]["mfma_sustained"] = ceil
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill", "decode"):
         import oracle

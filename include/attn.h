@@ -285,6 +285,32 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* ctx_len
 int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t* free_count, int32_t* status,
                      int num_blocks, void* stream);
 
+/*
+ * Measurement aid, not part of the attention path: sustained rate of the
+ * bf16 matrix-core instruction the bf16 kernels are built from
+ * (v_mfma_f32_32x32x16_bf16, 32768 FLOPs per wave instruction).  The chip
+ * holds its clock only while power allows, and that depends on the operand
+ * data, so the rate reachable on real (random) data sits below the published
+ * peak that roofline fractions are quoted against; this call measures it.
+ *   fragments   : bf16 [n_fragments][8] device operand pool; n_fragments a
+ *                 power of two >= 16.  Lane t of the grid loads fragments
+ *                 (16 t + i) mod n_fragments, i < 16, and uses them as A and B
+ *                 operands, a different pair every instruction.
+ *   out         : fp32 [blocks * 256] device output (one value per lane, so
+ *                 the work is not optimised away).
+ *   blocks      : workgroups of 256 lanes (4 waves), 1 .. 65536.
+ *   iters       : MFMA instructions per wave, a multiple of 32, up to 2^24.
+ *   placement   : 0 .. 15, which of 16 placements of the loop in instruction
+ *                 memory (each 4 bytes further on) to run.  A loop of nothing
+ *                 but MFMAs issues at a placement-dependent rate on this GPU,
+ *                 so a measurement tries all 16 and keeps the fastest.
+ * FLOPs per call = blocks * 4 * iters * 32768.  Errors: ATTN_ERR_NULL,
+ * ATTN_ERR_ALIGN (pointers not 16-byte aligned), ATTN_ERR_SHAPE (sizes or
+ * placement out of range), ATTN_ERR_DEVICE, ATTN_ERR_LAUNCH.
+ */
+int attn_probe_mfma(const void* fragments, int n_fragments, float* out, int blocks, int iters, int placement,
+                    void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_strerror(int status);
 

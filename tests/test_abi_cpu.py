@@ -247,3 +247,22 @@ def test_bwd_workspace_bytes():
     assert attn.attn_prefill_bwd_workspace_bytes(16, 32, 8192) == 16 * 32 * 8192 * 8
     for bad in ((0, 8, 100), (2, 0, 100), (2, 8, 0), (-1, 8, 100)):
         assert attn.attn_prefill_bwd_workspace_bytes(*bad) == 0
+
+
+def probe(**kw):
+    a = dict(fragments=P, n_fragments=65536, out=P2, blocks=2048, iters=163840, placement=0, stream=NULL)
+    a.update(kw)
+    return attn.attn_probe_mfma(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fragments=NULL), E_NULL), (dict(out=NULL), E_NULL),
+    (dict(fragments=ctypes.c_void_p((1 << 20) + 8)), E_AL), (dict(out=ctypes.c_void_p((2 << 20) + 4)), E_AL),
+    (dict(n_fragments=8), E_SHAPE), (dict(n_fragments=48), E_SHAPE), (dict(n_fragments=0), E_SHAPE),
+    (dict(blocks=0), E_SHAPE), (dict(blocks=(1 << 16) + 1), E_SHAPE),
+    (dict(iters=0), E_SHAPE), (dict(iters=48), E_SHAPE), (dict(iters=(1 << 24) + 32), E_SHAPE),
+    (dict(placement=-1), E_SHAPE), (dict(placement=16), E_SHAPE),
+    (dict(), E_DEV), (dict(n_fragments=16, blocks=1, iters=32, placement=15), E_DEV),
+])
+def test_probe_rejects(kw, code):
+    assert probe(**kw) == code

@@ -15,8 +15,8 @@ __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
     "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
-    "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "attn_strerror",
-    "attn_version", "prefill", "prefill_bwd", "paged_attention",
+    "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "attn_probe_mfma",
+    "attn_strerror", "attn_version", "prefill", "prefill_bwd", "paged_attention", "probe_mfma",
     "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
     "APPEND_INVALID",
 ]
@@ -43,6 +43,7 @@ exported_symbols = (
     "paged_attn_gqa_workspace_bytes",
     "attn_prefill_bwd",
     "attn_prefill_bwd_workspace_bytes",
+    "attn_probe_mfma",
     "attn_strerror",
     "attn_version",
 )
@@ -92,6 +93,8 @@ def library():
     lib.attn_prefill_bwd.restype = I
     lib.attn_prefill_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_prefill_bwd_workspace_bytes.restype = SZ
+    lib.attn_probe_mfma.argtypes = [P, I, P, I, I, I, P]
+    lib.attn_probe_mfma.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -177,6 +180,10 @@ def attn_prefill_bwd_workspace_bytes(B, H, N) -> int:
 
 
 # ---- torch-tensor conveniences (marshalling only) -----------------------------
+
+def attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream):
+    return library().attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream)
+
 
 def _dtype_code(t):
     import torch
@@ -381,3 +388,24 @@ def kv_release(blocks, free_blocks, free_count, num_blocks: int, status=None, ch
         if code != APPEND_OK:
             raise _status_error(code, "paged_kv_release")
     return status
+
+
+PROBE_PLACEMENTS = 16
+
+
+def probe_mfma(fragments, iters: int, blocks: int = 2048, placement: int = 0, out=None, stream=None):
+    """Launch the matrix-core rate probe (attn_probe_mfma) on `fragments`, a
+    contiguous bf16 device tensor of n x 8 elements (n a power of two >= 16),
+    with its loop at `placement` (0 .. PROBE_PLACEMENTS - 1).  Returns (out,
+    flops): the per-lane output tensor and the FLOPs the launch performs
+    (blocks * 4 waves * iters * 32768)."""
+    import torch
+    if fragments.dtype != torch.bfloat16 or not fragments.is_contiguous() or fragments.numel() % 8:
+        raise ValueError("fragments must be a contiguous bf16 tensor of n x 8 elements")
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.float32, device=fragments.device)
+    rc = attn_probe_mfma(_ptr(fragments), fragments.numel() // 8, _ptr(out), blocks, iters, placement,
+                         _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "attn_probe_mfma")
+    return out, blocks * 4 * iters * 32768

@@ -10,6 +10,7 @@
 #include "append_internal.h"
 #include "bwd_internal.h"
 #include "attn_internal.h"
+#include "probe_internal.h"
 
 namespace {
 
@@ -291,6 +292,22 @@ int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t
     a.num_blocks = num_blocks;
     rc = attn::launch_release(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int attn_probe_mfma(const void* fragments, int n_fragments, float* out, int blocks, int iters, int placement,
+                    void* stream)
+{
+    if (!fragments || !out) return ATTN_ERR_NULL;
+    if (!aligned16(fragments) || !aligned16(out)) return ATTN_ERR_ALIGN;
+    if (n_fragments < 16 || (n_fragments & (n_fragments - 1)) != 0) return ATTN_ERR_SHAPE;
+    if (blocks < 1 || blocks > (1 << 16) || iters < 32 || (iters % 32) != 0 || iters > (1 << 24))
+        return ATTN_ERR_SHAPE;
+    if (placement < 0 || placement >= attn::kProbePlacements) return ATTN_ERR_SHAPE;
+    int rc = check_device();
+    if (rc) return rc;
+    return attn::launch_mfma_probe(fragments, n_fragments, out, blocks, iters, placement, (hipStream_t)stream) == 0
+               ? ATTN_OK
+               : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"
