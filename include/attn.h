@@ -55,7 +55,9 @@ enum {
     ATTN_ERR_WORKSPACE = -7,   /* workspace missing or smaller than required */
     ATTN_ERR_LAUNCH = -8,      /* the HIP runtime rejected a launch */
     ATTN_ERR_SCALE = -9,       /* scale is negative, NaN or infinite */
-    ATTN_ERR_DEVICE = -10      /* the current device is not a gfx950 GPU */
+    ATTN_ERR_DEVICE = -10,     /* the current device is not a gfx950 GPU */
+    ATTN_ERR_BAD_TABLE = -11   /* ATTN_DEBUG=1 only: a length or block-table entry breaks the
+                                  paged-attention contract (see paged_attn_check) */
 };
 
 /*
@@ -108,10 +110,14 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
  *                 bytes (partial results of split contexts); contents on entry
  *                 are ignored.  May be NULL when that function returns 0.
  *
- * Device-side contract (not checked on the device): 1 <= q_lens[r] <=
- * ctx_lens[r] <= max_ctx_len, q_lens[r] <= max_q_len, every block-table entry
- * needed lies in [0, num_blocks), and ceil(max_ctx_len / block_size) <=
- * max_blocks_per_seq.  Slots of a request's last block past its context may
+ * Device-side contract: 1 <= q_lens[r] <= ctx_lens[r] <= max_ctx_len,
+ * q_lens[r] <= max_q_len, every block-table entry needed lies in
+ * [0, num_blocks), and ceil(max_ctx_len / block_size) <= max_blocks_per_seq.
+ * The kernels do not check it (a bad entry reads outside the pool);
+ * paged_attn_check does, and with the environment variable ATTN_DEBUG=1 every
+ * paged call runs that check first, waits for it (the call then synchronises
+ * `stream`) and returns ATTN_ERR_BAD_TABLE, launching nothing else, when the
+ * contract is broken.  Slots of a request's last block past its context may
  * hold anything (NaN included); they are never used.  Several requests may
  * share (alias) physical blocks.
  *
@@ -284,6 +290,26 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* ctx_len
  */
 int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t* free_count, int32_t* status,
                      int num_blocks, void* stream);
+
+/*
+ * Check of the paged-attention device-side contract (see paged_attn_fwd):
+ * lengths and every block-table entry a request uses, on the device.  *status
+ * (int32 device word) receives, asynchronously, ATTN_CHECK_OK (0) or an OR of
+ * ATTN_CHECK_LENGTHS (some q_lens[r] < 1, q_lens[r] > ctx_lens[r],
+ * ctx_lens[r] > max_ctx_len, q_lens[r] > max_q_len, or a context needing more
+ * than max_blocks_per_seq blocks) and ATTN_CHECK_TABLE (an entry among the
+ * first ceil(ctx_lens[r] / block_size) of a row, at most max_blocks_per_seq,
+ * outside [0, num_blocks)).  It reads only those entries and the length
+ * arrays, so it is safe on any inputs of the declared shapes, and it writes
+ * *status on every call (no clearing needed).  One workgroup: a debugging aid,
+ * not for the per-step path.  Host-side errors: ATTN_ERR_NULL, ATTN_ERR_SHAPE,
+ * ATTN_ERR_BLOCK_SIZE, ATTN_ERR_ALIGN (pointers not 4-byte aligned),
+ * ATTN_ERR_DEVICE, ATTN_ERR_LAUNCH.
+ */
+enum { ATTN_CHECK_OK = 0, ATTN_CHECK_LENGTHS = 1, ATTN_CHECK_TABLE = 2 };
+int paged_attn_check(const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens, int num_seqs,
+                     int block_size, int max_blocks_per_seq, int num_blocks, int max_q_len, int max_ctx_len,
+                     int32_t* status, void* stream);
 
 /*
  * Measurement aid, not part of the attention path: sustained rate of the

@@ -12,7 +12,8 @@ import tiled_online_softmax_attention_amd as attn
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "attn.h"
 
-OK, E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
+OK, E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11
 
 
 def header_functions():
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_version():
     assert attn.attn_strerror(0) == "ok"
-    for code in (E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV):
+    for code in (E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE):
         s = attn.attn_strerror(code)
         assert s and s != "unknown attn status"
     assert attn.attn_strerror(-1234) == "unknown attn status"
@@ -266,3 +267,31 @@ def probe(**kw):
 ])
 def test_probe_rejects(kw, code):
     assert probe(**kw) == code
+
+
+def check_call(**kw):
+    a = dict(block_table=P, ctx_lens=P2, q_lens=P3, num_seqs=4, block_size=16, max_blocks_per_seq=64, num_blocks=256,
+             max_q_len=1, max_ctx_len=1024, status=P4, stream=NULL)
+    a.update(kw)
+    return attn.paged_attn_check(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(block_table=NULL), E_NULL), (dict(ctx_lens=NULL), E_NULL), (dict(q_lens=NULL), E_NULL),
+    (dict(status=NULL), E_NULL),
+    (dict(num_seqs=0), E_SHAPE), (dict(max_blocks_per_seq=0), E_SHAPE), (dict(num_blocks=0), E_SHAPE),
+    (dict(max_q_len=0), E_SHAPE), (dict(max_ctx_len=0), E_SHAPE),
+    (dict(block_size=8), E_BS), (dict(block_size=64), E_BS),
+    (dict(status=ctypes.c_void_p((4 << 20) + 2)), E_AL), (dict(block_table=ctypes.c_void_p((1 << 20) + 1)), E_AL),
+    (dict(), E_DEV),
+])
+def test_paged_check_rejects(kw, code):
+    assert check_call(**kw) == code
+
+
+def test_debug_flag_does_not_change_host_checks(monkeypatch):
+    """ATTN_DEBUG=1 adds a device check after the host checks; host errors
+    come first, unchanged."""
+    monkeypatch.setenv("ATTN_DEBUG", "1")
+    assert paged(q=NULL) == E_NULL
+    assert paged(block_size=8) == E_BS

@@ -15,8 +15,9 @@ __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
     "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
-    "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "attn_probe_mfma",
-    "attn_strerror", "attn_version", "prefill", "prefill_bwd", "paged_attention", "probe_mfma",
+    "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "paged_attn_check",
+    "attn_probe_mfma", "attn_strerror", "attn_version", "prefill", "prefill_bwd", "paged_attention", "paged_check",
+    "probe_mfma", "CHECK_OK", "CHECK_LENGTHS", "CHECK_TABLE", "ERR_BAD_TABLE",
     "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
     "APPEND_INVALID",
 ]
@@ -29,6 +30,10 @@ ATTN_F32 = 1
 
 # device status words of paged_kv_append / paged_kv_release
 APPEND_OK, APPEND_EXHAUSTED, APPEND_TABLE_FULL, APPEND_INVALID = 0, 1, 2, 3
+# flag bits of paged_attn_check's status word, and the status the paged calls
+# return under ATTN_DEBUG=1 when the check fails
+CHECK_OK, CHECK_LENGTHS, CHECK_TABLE = 0, 1, 2
+ERR_BAD_TABLE = -11
 
 # every symbol include/attn.h declares
 exported_symbols = (
@@ -43,6 +48,7 @@ exported_symbols = (
     "paged_attn_gqa_workspace_bytes",
     "attn_prefill_bwd",
     "attn_prefill_bwd_workspace_bytes",
+    "paged_attn_check",
     "attn_probe_mfma",
     "attn_strerror",
     "attn_version",
@@ -93,6 +99,8 @@ def library():
     lib.attn_prefill_bwd.restype = I
     lib.attn_prefill_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_prefill_bwd_workspace_bytes.restype = SZ
+    lib.paged_attn_check.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
+    lib.paged_attn_check.restype = I
     lib.attn_probe_mfma.argtypes = [P, I, P, I, I, I, P]
     lib.attn_probe_mfma.restype = I
     lib.attn_strerror.argtypes = [I]
@@ -180,6 +188,12 @@ def attn_prefill_bwd_workspace_bytes(B, H, N) -> int:
 
 
 # ---- torch-tensor conveniences (marshalling only) -----------------------------
+
+def paged_attn_check(block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq, num_blocks, max_q_len,
+                     max_ctx_len, status, stream):
+    return library().paged_attn_check(block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq,
+                                      num_blocks, max_q_len, max_ctx_len, status, stream)
+
 
 def attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream):
     return library().attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream)
@@ -312,6 +326,22 @@ def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, sca
     if rc != 0:
         raise AttnError(rc, "paged_attn_fwd")
     return out, lse
+
+
+def paged_check(block_table, ctx_lens, q_lens, block_size: int, num_blocks: int, max_q_len: int, max_ctx_len: int,
+                status=None, stream=None):
+    """Run paged_attn_check on the device; returns the int32 status tensor
+    (one element: CHECK_OK, or an OR of CHECK_LENGTHS and CHECK_TABLE),
+    written asynchronously on the stream."""
+    import torch
+    num_seqs, maxb = block_table.shape
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=block_table.device)
+    rc = paged_attn_check(_ptr(block_table), _ptr(ctx_lens), _ptr(q_lens), num_seqs, block_size, maxb, num_blocks,
+                          max_q_len, max_ctx_len, _ptr(status), _stream(stream))
+    if rc != 0:
+        raise AttnError(rc, "paged_attn_check")
+    return status
 
 
 def gather(pool, block_table, ctx_lens, block_size: int, total_tokens: int | None = None,

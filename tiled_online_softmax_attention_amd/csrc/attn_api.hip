@@ -11,6 +11,7 @@
 #include "bwd_internal.h"
 #include "attn_internal.h"
 #include "probe_internal.h"
+#include "check_internal.h"
 
 namespace {
 
@@ -29,6 +30,16 @@ int check_device()
         cached[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
     }
     return cached[dev] == 1 ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+// ATTN_DEBUG=1 (read at every call): the paged entry points check lengths
+// and block-table entries on the device first, wait for the result and
+// return ATTN_ERR_BAD_TABLE without launching anything else if they break
+// the contract.
+bool debug_checks()
+{
+    const char* env = getenv("ATTN_DEBUG");
+    return env && *env && atoi(env) != 0;
 }
 
 int check_scale(float scale)
@@ -55,6 +66,8 @@ const char* attn_strerror(int status)
         case ATTN_ERR_LAUNCH: return "HIP kernel launch failed";
         case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
         case ATTN_ERR_DEVICE: return "current device is not a gfx950 GPU";
+        case ATTN_ERR_BAD_TABLE:
+            return "a length or block-table entry breaks the paged-attention contract (ATTN_DEBUG check)";
         default: return "unknown attn status";
     }
 }
@@ -175,7 +188,7 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
     if (d != 64 && d != 128) return ATTN_ERR_HEAD_DIM;
     if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
     if (dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
-    if ((int64_t)(max_ctx_len + block_size - 1) / block_size > max_blocks_per_seq) return ATTN_ERR_SHAPE;
+    if (((int64_t)max_ctx_len + block_size - 1) / block_size > max_blocks_per_seq) return ATTN_ERR_SHAPE;
     if (kv_block_stride < (int64_t)H_kv * block_size * d) return ATTN_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(o) ||
         ((kv_block_stride * 2) & 15) || ((uintptr_t)block_table & 3u) || ((uintptr_t)lse & 3u))
@@ -192,6 +205,13 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
     }
     rc = check_device();
     if (rc) return rc;
+    if (debug_checks()) {
+        attn::CheckArgs c{block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq, num_blocks,
+                          max_q_len, max_ctx_len, nullptr};
+        int32_t flags = 0;
+        if (attn::run_paged_debug_check(c, (hipStream_t)stream, &flags) != 0) return ATTN_ERR_LAUNCH;
+        if (flags) return ATTN_ERR_BAD_TABLE;
+    }
     attn::PagedArgs a{};
     a.q = q; a.k_pool = k_pool; a.v_pool = v_pool;
     a.block_table = block_table; a.ctx_lens = ctx_lens; a.q_lens = q_lens;
@@ -292,6 +312,24 @@ int paged_kv_release(const int32_t* blocks, int n, int32_t* free_blocks, int32_t
     a.num_blocks = num_blocks;
     rc = attn::launch_release(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+int paged_attn_check(const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens, int num_seqs,
+                     int block_size, int max_blocks_per_seq, int num_blocks, int max_q_len, int max_ctx_len,
+                     int32_t* status, void* stream)
+{
+    if (!block_table || !ctx_lens || !q_lens || !status) return ATTN_ERR_NULL;
+    if (num_seqs < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 1 || max_ctx_len < 1)
+        return ATTN_ERR_SHAPE;
+    if (block_size != 16 && block_size != 32) return ATTN_ERR_BLOCK_SIZE;
+    if (((uintptr_t)block_table & 3u) || ((uintptr_t)ctx_lens & 3u) || ((uintptr_t)q_lens & 3u) ||
+        ((uintptr_t)status & 3u))
+        return ATTN_ERR_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    attn::CheckArgs c{block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq, num_blocks,
+                      max_q_len, max_ctx_len, status};
+    return attn::launch_paged_check(c, (hipStream_t)stream) == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 int attn_probe_mfma(const void* fragments, int n_fragments, float* out, int blocks, int iters, int placement,
