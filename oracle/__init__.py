@@ -51,14 +51,15 @@ BF16, F32, F64 = 0, 1, 2
 _lib = None
 
 
-def build(force: bool = True, src: Path | None = None, out: Path | None = None) -> Path:
-    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP)."""
+def build(force: bool = True, src: Path | None = None, out: Path | None = None, extra_flags=()) -> Path:
+    """Compile the oracle with gcc (-O2, IEEE semantics, OpenMP); extra_flags
+    are appended (the sanitizer test builds an instrumented copy this way)."""
     src = Path(src) if src else _SRC
     out = Path(out) if out else _LIB
     if not force and out.exists() and out.stat().st_mtime >= src.stat().st_mtime:
         return out
     tmp = out.with_suffix(".so.tmp%d" % os.getpid())
-    cmd = ["gcc", "-O2", "-fno-fast-math", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-fPIC", "-shared", "-fopenmp", "-std=c11", *extra_flags,
            str(src), "-o", str(tmp), "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
