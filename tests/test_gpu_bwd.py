@@ -164,3 +164,35 @@ def test_c3_gqa8_bwd_full_size_sampled_rows():
     check_grad("c3 gqa8 dq rows", gq, rq)
     check_grad("c3 gqa8 dk rows", gk, rk)
     check_grad("c3 gqa8 dv rows", gv, rv)
+
+
+@pytest.mark.parametrize("H,H_kv,N,d", [(4, 2, 300, 128), (3, 3, 77, 64)])
+def test_bwd_outputs_and_workspace_in_bounds(H, H_kv, N, d):
+    """Guard words around dQ, dK, dV and the workspace survive: the backward
+    writes only inside the buffers it is given (the workspace exactly
+    attn_prefill_bwd_workspace_bytes long)."""
+    cfg = inputs.PrefillConfig("bwd_guard", 1, H, N, d, torch.bfloat16, True, 31 + N, H_kv=H_kv)
+    q, k, v = inputs.prefill_inputs(cfg, DEV)
+    do = inputs.grad_output(cfg, DEV)
+    o, lse = attn.prefill(q, k, v, True, cfg.scale)
+    G = 4096
+
+    def guarded(like, fill):
+        buf = torch.full((2 * G + like.numel(),), fill, dtype=like.dtype, device=DEV)
+        return buf, buf[G:G + like.numel()].view(like.shape)
+
+    bq, dq = guarded(q, 7.0)
+    bk, dk = guarded(k, 5.0)
+    bv, dv = guarded(v, 3.0)
+    ws_bytes = attn.attn_prefill_bwd_workspace_bytes(1, H, N)
+    wbuf = torch.full((ws_bytes // 4 + 2 * G,), -9.0, dtype=torch.float32, device=DEV)
+    ws = wbuf[G:G + ws_bytes // 4]
+    log("bwd canaries H=%d H_kv=%d N=%d d=%d" % (H, H_kv, N, d))
+    attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    for buf, fill in ((bq, 7.0), (bk, 5.0), (bv, 3.0), (wbuf, -9.0)):
+        assert bool((buf[:G] == fill).all()) and bool((buf[-G:] == fill).all())
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, cfg.scale, True)
+    check_grad("dq", dq, rq)
+    check_grad("dk", dk, rk)
+    check_grad("dv", dv, rv)

@@ -228,3 +228,32 @@ def test_c5_sampled():
     og = torch.stack([o[rw, h] for rw, h in zip(rows, h_idx)])
     lg = torch.stack([lse[rw, h] for rw, h in zip(rows, h_idx)])
     check_close("c5 sampled", og, o_ref, lg, l_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("ql,split", [(1, None), (1, 64), (200, 128), (3, None)])
+def test_outputs_and_workspace_in_bounds(ql, split):
+    """Guard words around O, LSE and the workspace survive a call: the
+    decode and tile paths, with and without context splits, write only
+    inside the buffers they are given (the workspace exactly as large as
+    paged_attn_workspace_bytes asks)."""
+    ctx = [900, 64, 1, 300, 2000]
+    pi = make(ctx, [min(ql, c) for c in ctx], H=4, d=128, bs=16, seed=50 + ql)
+    G = 4096
+    rows, H, d = pi.q.shape
+    obuf = torch.full((2 * G + rows * H * d,), 7.0, dtype=torch.bfloat16, device=DEV)
+    lbuf = torch.full((2 * G + rows * H,), 3.0, dtype=torch.float32, device=DEV)
+    o = obuf[G:G + rows * H * d].view(rows, H, d)
+    lse = lbuf[G:G + rows * H].view(rows, H)
+    with env_split(split):
+        max_q, max_ctx = int(pi.q_lens.max()), int(pi.ctx_lens.max())
+        ws_bytes = attn.paged_attn_workspace_bytes(pi.num_seqs, H, d, pi.block_size, max_q, max_ctx)
+        wbuf = torch.full((ws_bytes + 2 * G,), 0x5A, dtype=torch.uint8, device=DEV)
+        ws = wbuf[G:G + ws_bytes] if ws_bytes else None   # offset G keeps the 256-byte alignment
+        log("canaries ql=%d split=%s ws=%d" % (ql, split, ws_bytes))
+        attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
+                             max_q_len=max_q, max_ctx_len=max_ctx, out=o, lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+    assert bool((obuf[:G] == 7.0).all()) and bool((obuf[-G:] == 7.0).all())
+    assert bool((lbuf[:G] == 3.0).all()) and bool((lbuf[-G:] == 3.0).all())
+    assert bool((wbuf[:G] == 0x5A).all()) and bool((wbuf[-G:] == 0x5A).all())
+    assert bool(torch.isfinite(o.float()).all())
