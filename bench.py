@@ -200,51 +200,96 @@ def mfma_ceiling(torch, attn, dev, launches=10, warm=2, iters=163840, blocks=204
     return res
 
 
-def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle):
+class ParityStats:
+    """Max / mean |GPU - oracle| over the rows the CPU baseline evaluated
+    (outside its timed region), reported beside the parity bounds of the bf16
+    path: O max 2e-2 and mean 2e-3; LSE max 2.5e-3 (every probability is
+    rounded to bf16 before it enters the running sum, a relative error of at
+    most 2^-9 in exp(LSE), i.e. 1.95e-3 in LSE, plus fp32 rounding)."""
+
+    def __init__(self):
+        self.n, self.max_o, self.sum_o, self.cnt_o, self.max_lse = 0, 0.0, 0.0, 0, 0.0
+
+    def add(self, o_gpu, o_ref, lse_gpu, lse_ref):
+        import numpy as np
+        e = np.abs(np.asarray(o_gpu, dtype=np.float64) - np.asarray(o_ref, dtype=np.float64))
+        self.n += e.shape[0]
+        self.max_o = max(self.max_o, float(e.max()))
+        self.sum_o += float(e.sum())
+        self.cnt_o += e.size
+        el = np.abs(np.asarray(lse_gpu, dtype=np.float64) - np.asarray(lse_ref, dtype=np.float64))
+        self.max_lse = max(self.max_lse, float(el.max()))
+
+    def report(self):
+        return {"rows": self.n, "o_max_abs": self.max_o, "o_mean_abs": self.sum_o / max(1, self.cnt_o),
+                "lse_max_abs": self.max_lse, "bounds": {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 2.5e-3},
+                "within": bool(self.max_o <= 2e-2 and self.sum_o / max(1, self.cnt_o) <= 2e-3
+                               and self.max_lse <= 2.5e-3)}
+
+
+def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle, o=None, lse=None):
     """Oracle on sampled rows of the causal prefill until ~budget_s of CPU
     work: seeded (b, h) heads, 256 seeded rows of each (full-length fp64
-    rows); TFLOP/s on the algorithmic FLOPs of the rows evaluated."""
+    rows); TFLOP/s on the algorithmic FLOPs of the rows evaluated.  With the
+    GPU's o and lse of the same inputs, the oracle rows also give the parity
+    errors of those rows."""
     import torch
     from tiled_online_softmax_attention_amd import inputs
     heads = inputs.sample_triples(cfg.seed + 1000, 4096, (cfg.B, cfg.H))
     done_rows, done_heads, flops, t_total = 0, 0, 0.0, 0.0
+    par = ParityStats()
     for hi, (b, h) in enumerate(heads):
         rows = inputs.sample_triples(cfg.seed + 2000 + hi, 256, (cfg.N,))
         rows = [r for (r,) in rows]
         qs, ks, vs = (x[b, h].unsqueeze(0).unsqueeze(0).cpu() for x in (q, k, v))
         t0 = time.perf_counter()
-        oracle.attention_rows(qs, ks, vs, cfg.scale, True, [0] * len(rows), [0] * len(rows), rows)
+        o_ref, l_ref = oracle.attention_rows(qs, ks, vs, cfg.scale, True, [0] * len(rows), [0] * len(rows), rows)
         t_total += time.perf_counter() - t0
+        if o is not None:
+            idx = torch.tensor(rows, device=o.device)
+            par.add(o[b, h].index_select(0, idx).float().cpu().numpy(), o_ref,
+                    lse[b, h].index_select(0, idx).cpu().numpy(), l_ref)
         done_rows += len(rows)
         done_heads += 1
         flops += sum(4.0 * cfg.d * (r + 1) for r in rows)
         if t_total >= budget_s:
             break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d seeded rows (256 per head, %d seeded heads) of the 16x32x8192x128 causal prefill, "
-                      "full-length fp64 rows, %.1f s of oracle time" % (done_rows, done_heads, t_total)}
+    res = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": "%d seeded rows (256 per head, %d seeded heads) of the 16x32x8192x128 causal prefill, "
+                     "full-length fp64 rows, %.1f s of oracle time" % (done_rows, done_heads, t_total)}
+    if o is not None:
+        res["parity"] = par.report()
+    return res
 
 
-def cpu_baseline_decode(pi, budget_s, oracle):
-    """Oracle on the first requests of the C4 batch until ~budget_s; KV GB/s."""
+def cpu_baseline_decode(pi, budget_s, oracle, o=None, lse=None):
+    """Oracle on the first requests of the C4 batch until ~budget_s; KV GB/s.
+    With the GPU's o and lse, also the parity errors of those rows."""
     import torch
     ctx = pi.ctx_lens.cpu().tolist()
     t_total, nbytes, nreq = 0.0, 0.0, 0
     pool_cpu = None
+    par = ParityStats()
+    q_cpu, bt_cpu, ctx_cpu, ql_cpu = pi.q.cpu(), pi.block_table.cpu(), pi.ctx_lens.cpu(), pi.q_lens.cpu()
     for r in range(len(ctx)):
         if pool_cpu is None:
             pool_cpu = pi.pool.cpu()
         rows = list(range(pi.H))
         t0 = time.perf_counter()
-        oracle.paged_attention_rows(pi.q.cpu(), pool_cpu, pi.block_table.cpu(), pi.ctx_lens.cpu(), pi.q_lens.cpu(),
-                                    pi.block_size, pi.scale, [r] * pi.H, rows, [0] * pi.H)
+        o_ref, l_ref = oracle.paged_attention_rows(q_cpu, pool_cpu, bt_cpu, ctx_cpu, ql_cpu, pi.block_size, pi.scale,
+                                                   [r] * pi.H, rows, [0] * pi.H)
         t_total += time.perf_counter() - t0
+        if o is not None:   # one query row per request: packed row r
+            par.add(o[r].float().cpu().numpy(), o_ref, lse[r].cpu().numpy(), l_ref)
         nbytes += paged_bytes([ctx[r]], [1], pi.H, pi.d, pi.block_size)
         nreq += 1
         if t_total >= budget_s:
             break
-    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
+    res = {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
+    if o is not None:
+        res["parity"] = par.report()
+    return res
 
 
 def cpu_baseline_bwd(q, k, v, do, cfg, budget_s, oracle):
@@ -689,9 +734,9 @@ def main():
         import oracle
         print("timing the fp64 oracle on the host", file=sys.stderr, flush=True)
         if do_prefill:
-            res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, c3, args.cpu_seconds, oracle)
+            res["cpu_baseline"] = cpu_baseline_prefill(q, k, v, c3, args.cpu_seconds, oracle, o=o, lse=lse)
         if do_decode:
-            cb = cpu_baseline_decode(pi, args.cpu_seconds * 0.5, oracle)
+            cb = cpu_baseline_decode(pi, args.cpu_seconds * 0.5, oracle, o=od, lse=lsed)
             if do_prefill:
                 res["cpu_baseline"]["decode"] = cb
             else:
