@@ -543,7 +543,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the sustained matrix-core rate measurement (attn_probe_mfma)")
@@ -658,18 +658,21 @@ def main():
             if record:
                 t_aux.stop(e)
 
+    # C2 launches last ~0.06 ms: time at least 2000 of them (>= 100 ms of
+    # kernel time) so that the median is stable
+    n_steps = max(args.steps, 2000) if args.only == "c2" else args.steps
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    print("timing %d steps" % n_steps, file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(n_steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / n_steps
 
-    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "causal prefill bf16 16x32x8192x128 + paged decode bf16 64 req x 1 query, "
@@ -700,12 +703,14 @@ def main():
                                       "kernels": "paged_decode_kernel<128,16> + paged_combine_kernel<128>"}}
         if not do_prefill:
             res["value"], res["unit"] = round(gbs, 1), "GB/s"
+            res["config"].update(workload="paged decode bf16 64 req x 1 query, ctx U[512,16384], 16-token pages, "
+                                          "H=32, d=128", global_batch=len(ctx_list), seq_len=1)
     if args.only == "c2":
         ms = t_aux.mean_ms()
         c2 = inputs.C2
         fl = prefill_flops(c2.B, c2.H, c2.N, c2.d, True)
         res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
-        res["config"]["workload"] = "causal prefill bf16 1x32x2048x128"
+        res["config"].update(workload="causal prefill bf16 1x32x2048x128", global_batch=c2.B, seq_len=c2.N)
         res["launch_ms"] = round(ms, 4)
         res["launch_ms_median"] = round(t_aux.median_ms(), 4)
         res["launch_ms_min"] = round(t_aux.min_ms(), 4)
@@ -718,7 +723,8 @@ def main():
         fl = paged_flops(ctx5, ql5, p5.d, p5.H)
         nb = paged_bytes(ctx5, ql5, p5.H, p5.d, p5.block_size)
         res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
-        res["config"]["workload"] = "paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], 32-token pages"
+        res["config"].update(workload="paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], "
+                                      "32-token pages", global_batch=len(ql5), seq_len=max(ql5))
         res["launch_ms"] = round(ms, 4)
         res["kv_gbps"] = round(nb / (ms * 1e-3) / 1e9, 1)
         res["launch_ms_median"] = round(t_aux.median_ms(), 4)
