@@ -226,7 +226,7 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
     a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
     a.ws_lse = plan.ws_bytes ? (float*)((char*)workspace + plan.ws_o_bytes) : nullptr;
     rc = attn::launch_paged(a, plan, (hipStream_t)stream);
-    return rc == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
 
 int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,

@@ -314,8 +314,16 @@ struct PagedKV {
     __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
 };
 
+// Work mapping.  An item is (request r, K/V head hk, context split, query
+// tile); the items of one (r, hk) pair read the same K/V, so they all go to
+// one XCD (workgroups are dealt to the 8 XCDs round-robin by block id) and
+// share its L2.  Pairs are dealt to the XCDs round-robin too: pair
+// 8 m + x runs on XCD x.  (Giving each XCD a contiguous range of pairs
+// instead hands it whole requests -- one request per XCD for a batch of 8 --
+// and requests of unequal context then leave most XCDs idle while the one
+// with the longest finishes.)
 template <int D, int BS>
-__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work)
+__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work, int pair_rr)
 {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
@@ -326,16 +334,29 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     // group), so each K/V tile staged in LDS serves the whole group.
     const int G = a.H / a.H_kv;
     const int ppt = kTileRows / G;                     // positions per tile
-    const int per = gridDim.x >> 3;
-    int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    if (L >= n_work) return;
     const int nqt = (a.max_q_len + ppt - 1) / ppt;
-    const int qt = L % nqt;
-    L /= nqt;
-    const int split = L % a.max_splits;
-    L /= a.max_splits;
-    const int hk = L % a.H_kv;
-    const int r = L / a.H_kv;
+    int qt, split, hk, r;
+    if (pair_rr) {
+        const int per_pair = nqt * a.max_splits;       // items of one (r, hk) pair
+        const int j = blockIdx.x >> 3;                 // position on this XCD
+        const int pair = (blockIdx.x & 7) + 8 * (j / per_pair);
+        if (pair >= a.num_seqs * a.H_kv) return;
+        const int w = j % per_pair;
+        qt = w % nqt;
+        split = w / nqt;
+        hk = pair % a.H_kv;
+        r = pair / a.H_kv;
+    } else {
+        const int per = gridDim.x >> 3;
+        int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+        if (L >= n_work) return;
+        qt = L % nqt;
+        L /= nqt;
+        split = L % a.max_splits;
+        L /= a.max_splits;
+        hk = L % a.H_kv;
+        r = L / a.H_kv;
+    }
     const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
     if (qt * ppt >= ql) return;
     const int S = a.split_tokens;
@@ -543,7 +564,7 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
 }
 
 template <int D, int BS>
-static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
+static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
 {
     if (plan.path == 0) {
         const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H_kv * plan.n_chunks * a.max_splits;
@@ -554,24 +575,31 @@ static void launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_
         else hipLaunchKernelGGL((paged_decode_kernel<D, BS, 1>), g, b, 0, stream, a);
     } else {
         const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H_kv * a.max_splits;
-        const int64_t grid = (n_work + 7) / 8 * 8;
-        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a, (int)n_work);
+        const int pair_rr = env_int("ATTN_CHUNK_MAP", 1) != 0;
+        const int64_t pairs = (int64_t)a.num_seqs * a.H_kv;
+        const int64_t grid = pair_rr ? (pairs + 7) / 8 * 8 * ((int64_t)plan.nqt * a.max_splits) : (n_work + 7) / 8 * 8;
+        if (grid > (int64_t)INT32_MAX) return -2;
+        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a,
+                           (int)n_work, pair_rr);
     }
     if (a.max_splits > 1) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;
         hipLaunchKernelGGL((paged_combine_kernel<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, a);
     }
+    return 0;
 }
 
 int launch_paged(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
 {
+    int rc;
     if (a.d == 128) {
-        if (a.block_size == 16) launch_paged_t<128, 16>(a, plan, stream);
-        else launch_paged_t<128, 32>(a, plan, stream);
+        if (a.block_size == 16) rc = launch_paged_t<128, 16>(a, plan, stream);
+        else rc = launch_paged_t<128, 32>(a, plan, stream);
     } else {
-        if (a.block_size == 16) launch_paged_t<64, 16>(a, plan, stream);
-        else launch_paged_t<64, 32>(a, plan, stream);
+        if (a.block_size == 16) rc = launch_paged_t<64, 16>(a, plan, stream);
+        else rc = launch_paged_t<64, 32>(a, plan, stream);
     }
+    if (rc) return rc;
     return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 
