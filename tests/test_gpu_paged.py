@@ -257,3 +257,31 @@ def test_outputs_and_workspace_in_bounds(ql, split):
     assert bool((lbuf[:G] == 3.0).all()) and bool((lbuf[-G:] == 3.0).all())
     assert bool((wbuf[:G] == 0x5A).all()) and bool((wbuf[-G:] == 0x5A).all())
     assert bool(torch.isfinite(o.float()).all())
+
+
+@pytest.mark.parametrize("ctx,ql,H,H_kv", [
+    ([900, 64, 3000, 300, 1, 2100], 40, 32, 8),   # 48 (request, K/V head) pairs: pairs dealt to XCDs
+    ([900, 2000, 300], 130, 8, 1),                 # 3 pairs: items dealt one by one
+])
+def test_chunk_work_mappings_bit_identical(ctx, ql, H, H_kv):
+    """The tile kernel's three work mappings (XCD-contiguous ranges, pairs
+    dealt round-robin, items dealt round-robin) only move items between
+    workgroups: outputs are bit-identical, and they match the oracle."""
+    qls = [min(ql, c) for c in ctx]
+    pi = inputs.build_paged(ctx, qls, H_kv, 128, 16, 77, DEV, H_q=H)
+    outs = []
+    old = os.environ.get("ATTN_CHUNK_MAP")
+    try:
+        for m in ("0", "1", "2"):
+            os.environ["ATTN_CHUNK_MAP"] = m
+            outs.append(run(pi, split=256, name="map %s" % m))
+    finally:
+        if old is None:
+            os.environ.pop("ATTN_CHUNK_MAP", None)
+        else:
+            os.environ["ATTN_CHUNK_MAP"] = old
+    for o, l in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
+    o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                          pi.scale)
+    check_close("chunk mappings", outs[0][0], o_ref, outs[0][1], l_ref, torch.bfloat16)

@@ -315,15 +315,22 @@ struct PagedKV {
 };
 
 // Work mapping.  An item is (request r, K/V head hk, context split, query
-// tile); the items of one (r, hk) pair read the same K/V, so they all go to
+// tile); the items of one (r, hk) pair read that head's K/V, so they run on
 // one XCD (workgroups are dealt to the 8 XCDs round-robin by block id) and
-// share its L2.  Pairs are dealt to the XCDs round-robin too: pair
-// 8 m + x runs on XCD x.  (Giving each XCD a contiguous range of pairs
-// instead hands it whole requests -- one request per XCD for a batch of 8 --
-// and requests of unequal context then leave most XCDs idle while the one
-// with the longest finishes.)
+// share its L2, and the pairs are dealt to the XCDs round-robin (pair 8 m + x
+// on XCD x), so that every XCD gets a similar mix of long and short
+// requests.  (Contiguous per-XCD ranges hand an XCD whole requests -- one
+// request per XCD for a batch of 8 -- and unequal contexts then leave most
+// XCDs idle behind the longest; dealing (pair, split) units instead puts
+// split s on XCD s mod 8 whenever max_splits is a multiple of 8, and the
+// high splits exist only for the longest contexts.)  With fewer than
+// kChunkPairsPerXcd pairs per XCD, items are dealt round-robin one by one
+// instead, so that a small batch still spreads over all XCDs.
+constexpr int kChunkPairsPerXcd = 4;
+enum { kMapRanges = 0, kMapPairs = 1, kMapItems = 2 };
+
 template <int D, int BS>
-__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work, int pair_rr)
+__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work, int map)
 {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
@@ -335,28 +342,34 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     const int G = a.H / a.H_kv;
     const int ppt = kTileRows / G;                     // positions per tile
     const int nqt = (a.max_q_len + ppt - 1) / ppt;
-    int qt, split, hk, r;
-    if (pair_rr) {
-        const int per_pair = nqt * a.max_splits;       // items of one (r, hk) pair
+    int qt, split, pair;                               // pair = r * H_kv + hk
+    if (map == kMapPairs) {
+        const int per_pair = nqt * a.max_splits;       // items of one pair
         const int j = blockIdx.x >> 3;                 // position on this XCD
-        const int pair = (blockIdx.x & 7) + 8 * (j / per_pair);
+        pair = (blockIdx.x & 7) + 8 * (j / per_pair);
         if (pair >= a.num_seqs * a.H_kv) return;
-        const int w = j % per_pair;
-        qt = w % nqt;
-        split = w / nqt;
-        hk = pair % a.H_kv;
-        r = pair / a.H_kv;
+        qt = (j % per_pair) % nqt;
+        split = (j % per_pair) / nqt;
+    } else if (map == kMapItems) {
+        // item = block id, query tile fastest, then pair, then split (so that
+        // the XCD an item lands on does not follow its split)
+        int L = (int)blockIdx.x;
+        if (L >= n_work) return;
+        qt = L % nqt;
+        L /= nqt;
+        pair = L % (a.num_seqs * a.H_kv);
+        split = L / (a.num_seqs * a.H_kv);
     } else {
-        const int per = gridDim.x >> 3;
-        int L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+        // XCD-contiguous ranges of (pair, split, query tile)
+        int L = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
         if (L >= n_work) return;
         qt = L % nqt;
         L /= nqt;
         split = L % a.max_splits;
-        L /= a.max_splits;
-        hk = L % a.H_kv;
-        r = L / a.H_kv;
+        pair = L / a.max_splits;
     }
+    const int hk = pair % a.H_kv;
+    const int r = pair / a.H_kv;
     const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
     if (qt * ppt >= ql) return;
     const int S = a.split_tokens;
@@ -574,13 +587,17 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         else if (plan.gc == 2) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 2>), g, b, 0, stream, a);
         else hipLaunchKernelGGL((paged_decode_kernel<D, BS, 1>), g, b, 0, stream, a);
     } else {
-        const int64_t n_work = (int64_t)a.num_seqs * plan.nqt * a.H_kv * a.max_splits;
-        const int pair_rr = env_int("ATTN_CHUNK_MAP", 1) != 0;
         const int64_t pairs = (int64_t)a.num_seqs * a.H_kv;
-        const int64_t grid = pair_rr ? (pairs + 7) / 8 * 8 * ((int64_t)plan.nqt * a.max_splits) : (n_work + 7) / 8 * 8;
+        const int64_t per_pair = (int64_t)plan.nqt * a.max_splits;
+        const int64_t n_work = pairs * per_pair;
+        int map = (pairs >= 8 * kChunkPairsPerXcd) ? kMapPairs : kMapItems;
+        const int env_map = env_int("ATTN_CHUNK_MAP", -1);
+        if (env_map >= kMapRanges && env_map <= kMapItems) map = env_map;
+        const int64_t grid = (map == kMapPairs) ? (pairs + 7) / 8 * 8 * per_pair
+                           : (map == kMapRanges) ? (n_work + 7) / 8 * 8 : n_work;
         if (grid > (int64_t)INT32_MAX) return -2;
         hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a,
-                           (int)n_work, pair_rr);
+                           (int)n_work, map);
     }
     if (a.max_splits > 1) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;
