@@ -105,11 +105,15 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
         if (env && *env) pair = atoi(env) ? 1 : 0;
         if (!a.causal || N <= 128) pair = 0;
         a.pair = pair;
-        // tile order of small causal grids (see launch_prefill);
-        // ATTN_PREFILL_ORDER=0 / 1 forces heavy-first / complementary
+        // tile order of causal grids (chosen by size in launch_prefill); for
+        // comparison ATTN_PREFILL_ORDER=0 / 1 / 3 forces per-head ranges /
+        // complementary / tile-major
         a.order = -1;
         const char* oenv = getenv("ATTN_PREFILL_ORDER");
-        if (oenv && *oenv) a.order = atoi(oenv) ? 1 : 0;
+        if (oenv && *oenv) {
+            const int ov = atoi(oenv);
+            a.order = (ov == 0 || ov == 1 || ov == 3) ? ov : -1;
+        }
     }
     rc = attn::launch_prefill(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);

@@ -21,8 +21,9 @@ struct PrefillArgs {
     int causal;
     int dtype;      // 0 bf16, 1 fp32
     int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t
-    int order;      // bf16 causal: -1 automatic, 0 heaviest tile first per head, 1 complementary
-                    // order within each XCD's share (for grids of one dispatch round)
+    int order;      // bf16 causal: -1 automatic, 0 heaviest tile first per head in
+                    // XCD-contiguous ranges, 1 complementary order within each XCD's share,
+                    // 3 tile-major over the whole grid
     int n_work;     // filled by the launcher
 };
 

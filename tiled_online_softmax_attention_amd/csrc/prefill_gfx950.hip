@@ -6,18 +6,26 @@
 //  * fp32: a vector-ALU kernel with the same online softmax (fp32 storage has
 //    no dense matrix path worth using at these sizes).
 //
-// Work mapping (bf16).  Workgroups are dealt to the 8 XCDs round-robin, so the
-// linear id is remapped such that each XCD receives a contiguous range of
-// (batch*head, query tile) work: the query tiles of one head then share that
-// XCD's L2 for their K/V.  Within a head, tiles run heaviest (most keys) first.
-// For causal launches with few tiles ("pair" mode), a workgroup instead takes
-// tile t and tile n-1-t, so that every workgroup does the same number of key
-// tiles and the chip stays balanced.  A causal grid of about one dispatch
-// round (all its workgroups resident at once, two or three per CU) instead
-// deals each XCD's tiles in a complementary order -- the heavy half
-// descending, then the light half ascending -- so that the workgroups one CU
-// receives together add up to the same work (heavy-first per head pairs
-// heavy with heavy there, and the most loaded CU sets the time).
+// Work mapping (bf16).  Workgroups are dealt to the 8 XCDs round-robin by
+// block id; a causal launch picks one of three tile orders (launch_prefill):
+//  * order 0, per-head ranges: the linear id is remapped so that each XCD
+//    receives a contiguous range of (batch*head, query tile) work, heaviest
+//    tile (most keys) first within each head; the query tiles of a head then
+//    share that XCD's L2 for their K/V.  Non-causal launches, whose tiles
+//    all weigh the same, always use it.
+//  * order 3, tile-major: block id p takes head p % (B*H) and its
+//    (p / (B*H))-th heaviest tile -- the heaviest tile of every head first,
+//    then the next -- so the longest work starts first everywhere and every
+//    XCD gets the same mix of tile weights, whatever B*H is.  All heads are
+//    in flight at once, which pays while their K/V fits in the last-level
+//    cache: 1x12x16384 870 -> 1036 TFLOP/s, 1x28x8192 853 -> 969, 2x32x8192
+//    1000 -> 1045, but 16x32x8192 (2 GB of K/V) 1070 -> 722.
+//  * order 1, complementary: for a grid of about one dispatch round (all
+//    its workgroups resident, two or three per CU) each XCD's tiles go heavy
+//    half descending, then light half ascending, so that the workgroups one
+//    CU receives together add up to the same work.
+// In "pair" mode a workgroup instead takes tile t and tile n-1-t, so that
+// every workgroup does the same number of key tiles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,7 +65,7 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
     const TileBuffers buf{lds0, lds1};
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
-    if (L >= a.n_work) return;
+    if (L >= a.n_work && (PAIR || a.order != 3)) return;
     const int nqt = (a.N + BM - 1) / BM;
     const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
     int bh = L / per_bh, t = L % per_bh;
@@ -72,6 +80,13 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
         const int j = blockIdx.x >> 3, k = j / hpx, half = nqt / 2;
         bh = (blockIdx.x & 7) * hpx + j % hpx;
         t = (k < half) ? k : (nqt - 1) - (k - half);   // tiles[0] = nqt - 1 - t below
+    }
+    if (!PAIR && a.order == 3) {
+        // tile-major: head p % (B*H), (p / (B*H))-th heaviest tile
+        const int nbh = a.B * a.H;
+        if ((int)blockIdx.x >= a.n_work) return;
+        bh = (int)blockIdx.x % nbh;
+        t = (int)blockIdx.x / nbh;
     }
     const int64_t head_off = (int64_t)bh * a.N * D * 2;   // bytes, q and o
     const int64_t kv_off =                                 // bytes, k and v of this head's K/V head
@@ -113,9 +128,6 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
     }
 }
 
-// Causal grids of at most this many query tiles (about one dispatch round)
-// take the complementary tile order.
-constexpr int64_t kOrderMaxTiles = 1024;
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64 query rows per workgroup, 4 threads per row (each owns d/4
@@ -195,6 +207,13 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a)
     }
 }
 
+// Causal grids of at most this many query tiles (about one dispatch round)
+// take the complementary tile order; larger ones take the tile-major order
+// while the K/V of all heads fits in the last-level cache (256 MB), and
+// per-head ranges beyond that.
+constexpr int64_t kOrderMaxTiles = 1024;
+constexpr int64_t kTileMajorMaxKV = (int64_t)256 << 20;
+
 int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
@@ -209,7 +228,12 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         const int grid = (int)((n_work + 7) / 8 * 8);
         // complementary order needs whole heads per XCD share (grid = n_work, a multiple of 8 * nqt)
         const bool can_order = a.causal && !a.pair && n_work % 8 == 0 && (n_work / 8) % nqt == 0;
-        a.order = can_order ? (a.order < 0 ? (n_work <= kOrderMaxTiles ? 1 : 0) : a.order) : 0;
+        if (a.order == 1 && !can_order) a.order = 0;
+        if (a.order < 0) {
+            const int64_t kv_bytes = (int64_t)a.B * a.H_kv * a.N * a.d * 2 * 2;
+            a.order = (can_order && n_work <= kOrderMaxTiles) ? 1 : (kv_bytes <= kTileMajorMaxKV ? 3 : 0);
+        }
+        if (!a.causal || a.pair) a.order = 0;
 #define ATTN_LAUNCH_PREFILL(DD, PP) \
     hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
         if (a.d == 128) {
