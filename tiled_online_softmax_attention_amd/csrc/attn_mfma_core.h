@@ -178,8 +178,9 @@ __device__ __forceinline__ uint32_t v_dma_col(int lane)
 template <int D>
 struct WaveState {
     f32x16 o[TileCfg<D>::DBLK];
-    float m;  // offset of this lane's query, raw score units (-inf: none yet)
-    float l;  // running sum of this lane-half's rounded probabilities
+    float m;   // offset of this lane's query, raw score units (-inf: none yet)
+    float ms;  // the same offset in the exponent's base-2 units, m * c2 (0 while m = -inf)
+    float l;   // running sum of this lane-half's rounded probabilities
 };
 
 // Scores of one key tile: S^T blocks of 32 keys (accumulator register i of
@@ -267,11 +268,12 @@ __device__ __forceinline__ float tile_max(TileScores<D>& S, int lane, int key0, 
                 S.s[kb][i] = (off < lim_rel) ? S.s[kb][i] : -INFINITY;
             }
     }
-    float x = -INFINITY;
+    // one chain of three-operand maxima (v_max3_f32 takes two new scores each)
+    float x = fmaxf(S.s[0][0], S.s[0][1]);
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) x = fmaxf(x, fmaxf(S.s[kb][i], S.s[kb][i + 1]));
+        for (int i = (kb == 0) ? 2 : 0; i < 16; i += 2) x = fmaxf(fmaxf(x, S.s[kb][i]), S.s[kb][i + 1]);
     return half_max(x);
 }
 
@@ -287,6 +289,7 @@ __device__ __forceinline__ void update_offset(WaveState<D>& ws, float mt, float 
         const float m_new = fmaxf(ws.m, mt);
         const float alpha = (ws.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((ws.m - m_new) * c2);
         ws.m = m_new;
+        ws.ms = (m_new == -INFINITY) ? 0.f : m_new * c2;
         ws.l *= alpha;
 #pragma unroll
         for (int db = 0; db < C::DBLK; ++db) scale_in_place(ws.o[db], alpha);
@@ -294,17 +297,18 @@ __device__ __forceinline__ void update_offset(WaveState<D>& ws, float mt, float 
 }
 
 // p = exp2(s*c2 - m*c2) rounded to bf16 (packed in pairs, the P^T operand
-// layout); l += the sum of the rounded p.  (c2 > 0 always: a zero scale is
-// passed as a tiny positive c2, which gives the same p = 1 for every allowed
-// key and keeps exp2(-inf) = 0 for masked ones.)
+// layout); l += the sum of the rounded p, added pair by pair onto l in key
+// order.  (c2 > 0 always: a zero scale is passed as a tiny positive c2, which
+// gives the same p = 1 for every allowed key and keeps exp2(-inf) = 0 for
+// masked ones.)
 template <int D>
 __device__ __forceinline__ void exp_tile(bf16x2 (&pk)[TileCfg<D>::KBLK][8], const TileScores<D>& S, WaveState<D>& ws,
                                          float c2)
 {
     using C = TileCfg<D>;
     const bf16x2 ones = pack2(1.f, 1.f);
-    const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * c2;
-    float ps0 = 0.f, ps1 = 0.f;
+    const float ms = ws.ms;
+    float l = ws.l;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
@@ -313,10 +317,9 @@ __device__ __forceinline__ void exp_tile(bf16x2 (&pk)[TileCfg<D>::KBLK][8], cons
             const float t1 = __builtin_fmaf(S.s[kb][i + 1], c2, -ms);
             const bf16x2 w = pack2(__builtin_amdgcn_exp2f(t0), __builtin_amdgcn_exp2f(t1));
             pk[kb][i >> 1] = w;
-            if ((i >> 1) & 1) ps1 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps1, false);
-            else ps0 = __builtin_amdgcn_fdot2_f32_bf16(w, ones, ps0, false);
+            l = __builtin_amdgcn_fdot2_f32_bf16(w, ones, l, false);
         }
-    ws.l += ps0 + ps1;
+    ws.l = l;
 }
 
 // O^T += V^T P^T for one key tile.

@@ -246,6 +246,7 @@ __device__ __forceinline__ void clear_state(WaveState<D>& ws)
 #pragma unroll
     for (int db = 0; db < TileCfg<D>::DBLK; ++db) ws.o[db] = f32x16{};
     ws.m = -INFINITY;
+    ws.ms = 0.f;
     ws.l = 0.f;
 }
 
@@ -288,9 +289,8 @@ __device__ __forceinline__ void store_query_rows(const WaveState<D>& ws, const T
                 }
         }
         if (out.lse && g == 0) {
-            const float ms = (ws.m == -INFINITY) ? 0.f : ws.m * cx.c2;
             out.lse[qpos * out.lse_stride + qhead * out.lse_hstride] =
-                (l_tot > 0.f) ? (ms + __log2f(l_tot)) * kLn2 : -INFINITY;
+                (l_tot > 0.f) ? (ws.ms + __log2f(l_tot)) * kLn2 : -INFINITY;
         }
     }
 }

@@ -428,6 +428,9 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
 // ============================================================================
 // Combine: one wave per (request, query row, head) whose context was split.
 // M = max_s lse_s, L = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - L) O_s.
+// Lane s of the wave computes the weight of split s (64 splits at a time) and
+// the partial rows are read eight splits per batch, all eight loads in flight
+// together; O is still summed split by split in ascending order.
 // ============================================================================
 template <int D>
 __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a)
@@ -453,14 +456,34 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a)
     const float Lse = M + logf(sum);
     const int64_t row = prefix_len(a.q_lens, r, lane) + i;
     __bf16* orow = (__bf16*)a.o + (row * a.H + h) * D;
-    float acc[D / 64];
+    constexpr int CPL = D / 64;      // channels per lane: lane and lane + 64
+    constexpr int BATCH = 8;         // splits whose partial rows are loaded together
+    float acc[CPL];
 #pragma unroll
-    for (int c = 0; c < D / 64; ++c) acc[c] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const float wgt = expf(a.ws_lse[slot0 + s] - Lse);
-        const float* os = a.ws_o + (slot0 + s) * D;
+    for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+        const int n = min(64, nsplit - s0);
+        const float wl = (lane < n) ? expf(a.ws_lse[slot0 + s0 + lane] - Lse) : 0.f;
+        const float* os = a.ws_o + (slot0 + s0) * D + lane;
+        int s = 0;
+        for (; s + BATCH <= n; s += BATCH) {
+            float x[BATCH][CPL];
 #pragma unroll
-        for (int c = 0; c < D / 64; ++c) acc[c] = __builtin_fmaf(wgt, os[lane + 64 * c], acc[c]);
+            for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) x[u][c] = os[(s + u) * D + 64 * c];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const float wgt = __shfl(wl, s + u, 64);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(wgt, x[u][c], acc[c]);
+            }
+        }
+        for (; s < n; ++s) {
+            const float wgt = __shfl(wl, s, 64);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) acc[c] = __builtin_fmaf(wgt, os[s * D + 64 * c], acc[c]);
+        }
     }
 #pragma unroll
     for (int c = 0; c < D / 64; ++c) orow[lane + 64 * c] = (__bf16)acc[c];
