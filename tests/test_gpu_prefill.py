@@ -34,11 +34,13 @@ class env_set:
                 os.environ[k] = v
 
 
-def run_case(B, H, N, d, dtype, causal, seed, pair=None):
+def run_case(B, H, N, d, dtype, causal, seed, pair=None, wide=None):
     cfg = inputs.PrefillConfig("case", B, H, N, d, dtype, causal, seed)
-    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s" % (B, H, N, d, dtype, causal, seed, pair))
+    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s wide=%s"
+        % (B, H, N, d, dtype, causal, seed, pair, wide))
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair)):
+    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair),
+                 ATTN_PREFILL_WIDE=None if wide is None else int(wide)):
         o, lse = attn.prefill(q, k, v, causal, cfg.scale)
         torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, cfg.scale, causal)
@@ -107,6 +109,29 @@ def test_key_tile_counts(N, d, causal):
     the boundary between unmasked and masked tiles of the double-buffered
     key loop."""
     run_case(1, 2, N, d, torch.bfloat16, causal, 400 + N + d)
+
+
+@pytest.mark.parametrize("N", [1, 31, 200, 256, 257, 640, 1100])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_kernel_matches_oracle(N, causal):
+    """The 64-rows-per-wave variant (ATTN_PREFILL_WIDE=1): no full tile, a
+    partial 256-row tile, pipelined key loops of 4 and more tiles followed by
+    masked tiles, and rows past N in the last tile."""
+    run_case(2, 3, N, 128, torch.bfloat16, causal, 700 + N, wide=1)
+
+
+def test_wide_kernel_grouped_heads_and_repeat():
+    """Grouped-query heads through the wide kernel, and two calls giving the
+    same bits."""
+    cfg = inputs.PrefillConfig("wide_gqa", 1, 8, 777, 128, torch.bfloat16, True, 31, H_kv=2)
+    q, k, v = inputs.prefill_inputs(cfg, DEV)
+    with env_set(ATTN_PREFILL_WIDE=1):
+        o1, l1 = attn.prefill(q, k, v, True, cfg.scale)
+        o2, l2 = attn.prefill(q, k, v, True, cfg.scale)
+        torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o_ref, l_ref = oracle.attention(q, k, v, cfg.scale, True)
+    check_close("wide_gqa", o1, o_ref, l1, l_ref, torch.bfloat16)
 
 
 def test_deterministic_and_pair_independent():

@@ -109,6 +109,12 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
         // comparison ATTN_PREFILL_ORDER=0 / 1 / 3 forces per-head ranges /
         // complementary / tile-major
         a.order = -1;
+        // the 64-rows-per-wave kernel (bf16, d = 128) runs only when asked
+        // for with ATTN_PREFILL_WIDE=1 (measured slower than the 32-row
+        // kernel on the long causal prefill; kept for comparison)
+        a.wide = -1;
+        const char* wenv = getenv("ATTN_PREFILL_WIDE");
+        if (wenv && *wenv) a.wide = atoi(wenv) ? 1 : 0;
         const char* oenv = getenv("ATTN_PREFILL_ORDER");
         if (oenv && *oenv) {
             const int ov = atoi(oenv);

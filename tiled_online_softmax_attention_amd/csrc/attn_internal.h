@@ -24,6 +24,8 @@ struct PrefillArgs {
     int order;      // bf16 causal: -1 automatic, 0 heaviest tile first per head in
                     // XCD-contiguous ranges, 1 complementary order within each XCD's share,
                     // 3 tile-major over the whole grid
+    int wide;       // bf16, d = 128: 1 takes the 64-rows-per-wave kernel (256-row query tiles,
+                    // one workgroup per CU); otherwise the 32-row kernel
     int n_work;     // filled by the launcher
 };
 

@@ -3,6 +3,8 @@
 //  * bf16: fused MFMA kernel (attn_mfma_kernel.h), one workgroup of 4 waves per
 //    128-row query tile (or per pair of tiles, see below), K/V streamed through
 //    LDS in 32-key tiles, causal key tiles above the diagonal never loaded.
+//  * bf16, d = 128, on request (PrefillArgs::wide): the 64-rows-per-wave
+//    variant of attn_mfma_wide.h, 256-row query tiles, one workgroup per CU.
 //  * fp32: a vector-ALU kernel with the same online softmax (fp32 storage has
 //    no dense matrix path worth using at these sizes).
 //
@@ -30,6 +32,7 @@
 #include <stdint.h>
 
 #include "attn_mfma_kernel.h"
+#include "attn_mfma_wide.h"
 #include "attn_internal.h"
 
 namespace attn {
@@ -128,6 +131,46 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
     }
 }
 
+// 64 query rows per wave (attn_mfma_wide.h): one workgroup of 4 waves per
+// 256-row query tile, one workgroup per CU; per-head ranges on each XCD,
+// heaviest tile first within a head.
+template <int D>
+__global__ __launch_bounds__(256, 1) void prefill_bf16_wide_kernel(PrefillArgs a)
+{
+    using C = TileCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
+    const WideBuffers buf{{lds0, lds1, lds2, lds3}};
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= a.n_work) return;
+    const int nqt = (a.N + kWideRows - 1) / kWideRows;
+    const int bh = L / nqt, qt = nqt - 1 - L % nqt;
+    const int64_t head_off = (int64_t)bh * a.N * D * 2;
+    const int64_t kv_off = ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * a.N * D * 2;
+    ContigKV<D> kv{(const char*)a.k + kv_off, (const char*)a.v + kv_off, (uint32_t)a.N * (uint32_t)(D * 2)};
+    const int q0 = qt * kWideRows;
+    TileProblem P;
+    P.q = (const char*)a.q + head_off + (int64_t)q0 * D * 2;
+    P.q_stride = D * 2;
+    P.q_hstride = 0;
+    P.rows_per_pos = 1;
+    P.n_rows = min(kWideRows, a.N - q0);
+    P.q_pos0 = q0;
+    P.causal = a.causal;
+    P.kv_begin = 0;
+    P.kv_end = a.N;
+    TileOut out;
+    out.o = (char*)a.o + head_off + (int64_t)q0 * D * 2;
+    out.o_stride = D * 2;
+    out.o_hstride = 0;
+    out.lse_hstride = 0;
+    out.lse = a.lse ? a.lse + (int64_t)bh * a.N + q0 : nullptr;
+    out.lse_stride = 1;
+    out.fp32_out = 0;
+    run_wide_tile<D>(P, kv, out, a.scale * kLog2e, buf);
+}
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64 query rows per workgroup, 4 threads per row (each owns d/4
@@ -217,7 +260,14 @@ constexpr int64_t kTileMajorMaxKV = (int64_t)256 << 20;
 int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
-    if (a.dtype == 0) {
+    if (a.dtype == 0 && a.d == 128 && !a.pair && a.wide == 1) {
+        const int nqt = (a.N + kWideRows - 1) / kWideRows;
+        const int64_t n_work = (int64_t)a.B * a.H * nqt;
+        if (n_work > (int64_t)INT32_MAX - 8) return -2;
+        a.n_work = (int)n_work;
+        const int grid = (int)((n_work + 7) / 8 * 8);
+        hipLaunchKernelGGL((prefill_bf16_wide_kernel<128>), dim3(grid), dim3(TileCfg<128>::kThreads), 0, stream, a);
+    } else if (a.dtype == 0) {
         const int BM = kTileRows;
         const int nqt = (a.N + BM - 1) / BM;
         const int64_t bh = (int64_t)a.B * a.H;
