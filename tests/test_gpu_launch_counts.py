@@ -36,7 +36,8 @@ def test_prefill_one_launch():
 
 
 @pytest.mark.parametrize("ctx,ql,split", [
-    ([900, 64, 1, 300], 1, True),        # decode, split contexts
+    ([900, 64, 1, 300], 1, True),        # decode, split contexts (at most 8 splits)
+    ([5000, 64, 1, 300], 1, True),       # decode, more than 8 splits of one context
     ([40, 64, 1, 17], 1, False),         # decode, every context in one split
     ([3000, 600, 1300], 200, True),      # chunked prefill (tile kernel), split
     ([900, 600, 300], 200, False),       # chunked prefill, one split (1024 keys at least)
@@ -51,7 +52,13 @@ def test_paged_launches(ctx, ql, split):
     log("paged ctx=%s ql=%d: %s" % (ctx, ql, got))
     assert len(got) == (2 if split else 1), got
     if split:
-        assert "paged_combine_kernel" in got[1], got
+        # the workspace holds (d + 1) fp32 per (row, head, split): at most 8
+        # splits per row take the lane-groups-per-head combine, more a wave per head
+        rows_heads = pi.num_seqs * max_q * pi.H
+        max_splits = ws // (rows_heads * (pi.d + 1) * 4)
+        kname = "paged_combine_kernel" if max_splits > 8 else "paged_combine_heads_kernel"
+        log("max_splits=%d -> %s" % (max_splits, kname))
+        assert kname in got[1], got
 
 
 def test_backward_two_launches():

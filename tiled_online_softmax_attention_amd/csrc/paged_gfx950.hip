@@ -426,7 +426,88 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
 }
 
 // ============================================================================
-// Combine: one wave per (request, query row, head) whose context was split.
+// Combine for few splits (at most kCombineHeadsMaxSplits, e.g. chunked
+// prefill): M = max_s lse_s, L = M + ln sum_s exp(lse_s - M),
+// O = sum_s exp(lse_s - L) O_s, for every (request, query row, head) whose
+// context was split.  One wave per (request, query row, group of 64 / (d/8)
+// heads): d/8 lanes per head, 8 channels (two 16-byte loads of the fp32
+// partial) per lane.  Each lane walks its head's log-sum-exps itself (a few
+// values, the same for the lanes of a head), so no cross-lane reduction sits
+// between the memory round trips, and the partial rows are read eight splits
+// per batch with all their loads in flight; O is summed split by split in
+// ascending order.
+// ============================================================================
+template <int D>
+__global__ __launch_bounds__(256) void paged_combine_heads_kernel(PagedArgs a)
+{
+    constexpr int LPH = D / 8;          // lanes per head
+    constexpr int HPW = 64 / LPH;       // heads per wave
+    constexpr int BATCH = 8;            // splits whose partial rows are loaded together
+    const int lane = threadIdx.x & 63;
+    const int sub = lane / LPH, c = lane % LPH;
+    const int hgroups = (a.H + HPW - 1) / HPW;
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)a.num_seqs * a.max_q_len * hgroups;
+    if (wid >= n_waves) return;
+    const int hg = (int)(wid % hgroups);
+    const int i = (int)((wid / hgroups) % a.max_q_len);
+    const int r = (int)(wid / ((int64_t)hgroups * a.max_q_len));
+    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    if (i >= ql) return;                                   // uniform over the wave
+    const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
+    if (nsplit <= 1) return;
+    const int64_t row = prefix_len(a.q_lens, r, lane) + i;  // whole wave, one request
+    const int h = hg * HPW + sub;
+    if (h >= a.H) return;
+    const int64_t slot0 = (((int64_t)r * a.max_q_len + i) * a.H + h) * a.max_splits;
+    const float* lse_s = a.ws_lse + slot0;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lse_s[s]);
+    float sum = 0.f;
+    for (int s = 0; s < nsplit; ++s) sum += expf(lse_s[s] - M);
+    const float Lse = M + logf(sum);
+    const float* os = a.ws_o + slot0 * D + c * 8;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + BATCH <= nsplit; s += BATCH) {
+        f32x4 x0[BATCH], x1[BATCH];
+        float wgt[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            x0[u] = *(const f32x4*)(os + (int64_t)(s + u) * D);
+            x1[u] = *(const f32x4*)(os + (int64_t)(s + u) * D + 4);
+            wgt[u] = expf(lse_s[s + u] - Lse);
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc0[e] = __builtin_fmaf(wgt[u], x0[u][e], acc0[e]);
+                acc1[e] = __builtin_fmaf(wgt[u], x1[u][e], acc1[e]);
+            }
+    }
+    for (; s < nsplit; ++s) {
+        const f32x4 x0 = *(const f32x4*)(os + (int64_t)s * D);
+        const f32x4 x1 = *(const f32x4*)(os + (int64_t)s * D + 4);
+        const float wgt = expf(lse_s[s] - Lse);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc0[e] = __builtin_fmaf(wgt, x0[e], acc0[e]);
+            acc1[e] = __builtin_fmaf(wgt, x1[e], acc1[e]);
+        }
+    }
+    u32x4 packed;
+    packed[0] = pack_bf16(acc0[0], acc0[1]);
+    packed[1] = pack_bf16(acc0[2], acc0[3]);
+    packed[2] = pack_bf16(acc1[0], acc1[1]);
+    packed[3] = pack_bf16(acc1[2], acc1[3]);
+    *(u32x4*)((__bf16*)a.o + (row * a.H + h) * D + c * 8) = packed;
+    if (a.lse && c == 0) a.lse[row * a.H + h] = Lse;
+}
+
+// ============================================================================
+// Combine for many splits (decode): one wave per (request, query row, head)
+// whose context was split.
 // M = max_s lse_s, L = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - L) O_s.
 // Lane s of the wave computes the weight of split s (64 splits at a time) and
 // the partial rows are read eight splits per batch, all eight loads in flight
@@ -523,6 +604,13 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(GatherArgs a)
 // ============================================================================
 // host side
 // ============================================================================
+// The combine of few splits per row (chunked prefill: C5 has at most 5) runs
+// lane groups per head, each lane walking its head's log-sum-exps itself;
+// with many splits (decode: up to 64) a wave per head reads them in parallel
+// (same-box A/B: heads kernel C5 call 920 -> 939 TFLOP/s, but 64-request
+// decode 5.75 -> 5.69 TB/s).
+constexpr int kCombineHeadsMaxSplits = 8;
+
 static int env_int(const char* name, int dflt)
 {
     const char* s = getenv(name);
@@ -622,9 +710,14 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a,
                            (int)n_work, map);
     }
-    if (a.max_splits > 1) {
+    if (a.max_splits > kCombineHeadsMaxSplits) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;
+        if ((items + 3) / 4 > (int64_t)UINT32_MAX) return -2;
         hipLaunchKernelGGL((paged_combine_kernel<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, a);
+    } else if (a.max_splits > 1) {
+        const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * ((a.H + 64 / (D / 8) - 1) / (64 / (D / 8)));
+        if ((waves + 3) / 4 > (int64_t)UINT32_MAX) return -2;
+        hipLaunchKernelGGL((paged_combine_heads_kernel<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
     }
     return 0;
 }
