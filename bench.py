@@ -227,6 +227,20 @@ class ParityStats:
                                and self.max_lse <= 2.5e-3)}
 
 
+def host_cpu():
+    """CPU model and logical CPU count of the host the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle, o=None, lse=None):
     """Oracle on sampled rows of the causal prefill until ~budget_s of CPU
     work: seeded (b, h) heads, 256 seeded rows of each (full-length fp64
@@ -254,7 +268,7 @@ def cpu_baseline_prefill(q, k, v, cfg, budget_s, oracle, o=None, lse=None):
         flops += sum(4.0 * cfg.d * (r + 1) for r in rows)
         if t_total >= budget_s:
             break
-    res = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    res = {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), **host_cpu(), "kind": "oracle",
            "sample": "%d seeded rows (256 per head, %d seeded heads) of the 16x32x8192x128 causal prefill, "
                      "full-length fp64 rows, %.1f s of oracle time" % (done_rows, done_heads, t_total)}
     if o is not None:
@@ -285,7 +299,7 @@ def cpu_baseline_decode(pi, budget_s, oracle, o=None, lse=None):
         nreq += 1
         if t_total >= budget_s:
             break
-    res = {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+    res = {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), **host_cpu(), "kind": "oracle",
            "sample": "%d of 64 decode requests (all 32 heads each), %.1f s" % (nreq, t_total)}
     if o is not None:
         res["parity"] = par.report()
@@ -313,7 +327,7 @@ def cpu_baseline_bwd(q, k, v, do, cfg, budget_s, oracle):
         flops += sum(6.0 * cfg.d * (r + 1) for r in rows)
         if t_total >= budget_s:
             break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), **host_cpu(), "kind": "oracle",
             "sample": "%d seeded dQ rows (64 per head, %d seeded heads) of the 16x32x8192x128 causal backward, "
                       "full-length fp64 rows (S, dP, dQ products; 6*d FLOPs per allowed key), %.1f s of oracle "
                       "time" % (done_rows, done_heads, t_total)}
