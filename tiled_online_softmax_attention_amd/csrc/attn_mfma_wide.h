@@ -251,9 +251,14 @@ template <int D>
 __device__ __forceinline__ void publish_tile()
 {
     static_assert(TileCfg<D>::COPIES_PER_GROUP < 16, "vmcnt field");
+    // The empty asm statements keep the compiler from moving memory accesses
+    // across the barrier (s_barrier alone is not a memory operation to it);
+    // unlike a workgroup fence they add no wait for the copies in flight.
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x3f70 | TileCfg<D>::COPIES_PER_GROUP);   // vmcnt(one tile's copies)
     __builtin_amdgcn_s_waitcnt(0xc07f);                                  // lgkmcnt(0): this wave's LDS reads done
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 // Pipelined step for tile j (in buffer I), whose scores S[cur] and offset
