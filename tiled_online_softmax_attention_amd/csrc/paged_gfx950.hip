@@ -644,14 +644,17 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     p.n_chunks = G / p.gc;
     int S;
     if (p.path == 0) {
-        // decode: 4 waves x 4 pages per split by default (measured best on the
-        // 64-request, 16-token-page decode batch), halved while the batch
-        // would leave the chip short of workgroups; a workgroup serving
-        // several query heads keeps at least 2 pages per wave
+        // decode: 4 waves x 6 pages of 16 tokens per split (measured on the
+        // 64-request, 16-token-page decode batch: 384-token splits 5.90 TB/s,
+        // 352 5.90, 256 5.77, 448 5.86, 512 5.35), 4 pages of 32 tokens;
+        // halved while the batch would leave the chip short of workgroups,
+        // down to 1 page per wave (2 for a workgroup serving several query
+        // heads)
         const int64_t items = rows * H_kv * p.n_chunks;
-        S = 4 * block_size * 4;
+        S = 4 * block_size * (block_size == 16 ? 6 : 4);
         const int s_min = (p.gc > 1 ? 2 : 1) * 4 * block_size;
         while (S > s_min && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
+        if (S < s_min) S = s_min;
         p.nqt = 1;
     } else {
         const int ppt = kTileRows / G;                 // query positions per tile
