@@ -662,12 +662,17 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         const int64_t items = (int64_t)num_seqs * p.nqt * H_kv;
         // Decode-length queries (grouped heads on this path) leave one wave of
         // the tile with rows, so a workgroup is latency-bound and more, shorter
-        // splits keep more of them in flight (64 requests x 4 K/V heads, 16-token
-        // pages: 1024-key splits 4.27 TB/s, 2048-key 3.50); longer queries
-        // have full tiles and want fewer partials to combine.
-        const int64_t target = (max_q_len <= kDecodeMaxQ) ? 4096 : 2048;
-        S = 8192;
-        while (S > 1024 && items * ((max_ctx_len + S - 1) / S) < target) S /= 2;
+        // splits keep more of them in flight; longer queries have full tiles
+        // and want fewer partials to combine.  The split count per (request,
+        // K/V head, query tile) brings the grid to about `target` items, in
+        // whole 64-key units between 1024 and 8192 keys (64 requests x 4 K/V
+        // heads, 16-token pages, one query: 1280-key splits 4.84 TB/s, 1024
+        // 4.75, 1536 4.54, 2048 3.50; 8 requests x 512 rows: 8192).
+        const int64_t target = (max_q_len <= kDecodeMaxQ) ? 3200 : 2048;
+        const int64_t per = (target + items - 1) / items;              // splits per item
+        int64_t s = (max_ctx_len + per - 1) / per;
+        s = (s + 63) / 64 * 64;
+        S = (int)(s < 1024 ? 1024 : (s > 8192 ? 8192 : s));
     }
     const int env = env_int("ATTN_SPLIT_TOKENS", 0);
     if (env > 0) S = env;
