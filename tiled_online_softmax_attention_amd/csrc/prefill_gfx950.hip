@@ -21,7 +21,9 @@
 //    XCD gets the same mix of tile weights, whatever B*H is.  All heads are
 //    in flight at once, which pays while their K/V fits in the last-level
 //    cache: 1x12x16384 870 -> 1036 TFLOP/s, 1x28x8192 853 -> 969, 2x32x8192
-//    1000 -> 1045, but 16x32x8192 (2 GB of K/V) 1070 -> 722.
+//    1000 -> 1045, but 16x32x8192 (2 GB of K/V) 1070 -> 722, and with grouped
+//    heads per-head ranges win (their L2 serves a K/V head to all its query
+//    heads): 16x32x8192 on 4 K/V heads 1075-1081 against 905-937.
 //  * order 1, complementary: for a grid of about one dispatch round (all
 //    its workgroups resident, two or three per CU) each XCD's tiles go heavy
 //    half descending, then light half ascending, so that the workgroups one
@@ -252,8 +254,8 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a)
 
 // Causal grids of at most this many query tiles (about one dispatch round)
 // take the complementary tile order; larger ones take the tile-major order
-// while the K/V of all heads fits in the last-level cache (256 MB), and
-// per-head ranges beyond that.
+// while the K/V of all heads fits in the last-level cache (256 MB) and no
+// query heads share a K/V head, and per-head ranges otherwise.
 constexpr int64_t kOrderMaxTiles = 1024;
 constexpr int64_t kTileMajorMaxKV = (int64_t)256 << 20;
 
@@ -281,7 +283,12 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         if (a.order == 1 && !can_order) a.order = 0;
         if (a.order < 0) {
             const int64_t kv_bytes = (int64_t)a.B * a.H_kv * a.N * a.d * 2 * 2;
-            a.order = (can_order && n_work <= kOrderMaxTiles) ? 1 : (kv_bytes <= kTileMajorMaxKV ? 3 : 0);
+            // tile-major only without grouped heads: per-head ranges keep the
+            // query heads of one K/V head on one XCD, whose L2 then serves
+            // their K/V (16x32x8192x128 on 4 K/V heads, 256 MiB of K/V: per-head
+            // ranges 1075-1081 TFLOP/s, tile-major 905-937)
+            a.order = (can_order && n_work <= kOrderMaxTiles) ? 1
+                    : ((kv_bytes <= kTileMajorMaxKV && a.H_kv == a.H) ? 3 : 0);
         }
         if (!a.causal || a.pair) a.order = 0;
 #define ATTN_LAUNCH_PREFILL(DD, PP) \
