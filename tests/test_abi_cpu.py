@@ -125,6 +125,30 @@ def test_workspace_plan_is_pure_and_sane():
     assert attn.paged_attn_workspace_bytes(4, 32, 128, 8, 1, 100) == 0
 
 
+def _max_splits(num_seqs, H, H_kv, d, bs, max_q, max_ctx):
+    """Splits per (row, head) the plan chose, read back from the workspace
+    size: d + 1 fp32 per (row, head, split), the O part rounded up to 256 B."""
+    ws = attn.paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, bs, max_q, max_ctx)
+    return ws // (num_seqs * max_q * H * (d + 1) * 4) if ws else 1
+
+
+@pytest.mark.parametrize("args,splits", [
+    # 64-request decode on 16-token pages (vector kernel): 384-token splits
+    ((64, 32, 32, 128, 16, 1, 16384), 43),
+    # the same lengths on 4 K/V heads (tile kernel, decode-length rows): 1280-key splits
+    ((64, 32, 4, 128, 16, 1, 16384), 13),
+    # chunked prefill, 8 x 512 rows on 32-token pages (tile kernel): 8192-key splits
+    ((8, 32, 32, 128, 32, 512, 33280), 5),
+    # small decode batches: splits halved down to one 16-token page per wave, no further
+    ((4, 32, 32, 128, 16, 1, 900), 15),
+    ((4, 32, 32, 128, 16, 1, 64), 1),
+])
+def test_split_plans(args, splits):
+    """The split plans measured best on the benchmark shapes (host-side plan,
+    read back through the workspace size)."""
+    assert _max_splits(*args) == splits
+
+
 def gather(**kw):
     a = dict(k_pool=P, v_pool=P2, block_table=P3, ctx_lens=P4, block_size=16, num_seqs=2, H=4, d=64,
              max_blocks_per_seq=8, kv_block_stride=2 * 4 * 16 * 64, max_ctx_len=100, dtype=0, k_out=P,
