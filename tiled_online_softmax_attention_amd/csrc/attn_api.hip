@@ -97,10 +97,10 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
     // bf16 query tiles: 128 rows (32 queries per wave, three workgroups per CU).
-    // Pairing tiles t and n-1-t (equal work per workgroup) is opt-in for
-    // causal launches with ATTN_PREFILL_PAIR=1.
+    // Pairing tiles t and n-1-t (equal work per workgroup) is chosen by the
+    // launcher for causal grids (-1); ATTN_PREFILL_PAIR=0 / 1 forces it.
     {
-        int pair = 0;
+        int pair = -1;
         const char* env = getenv("ATTN_PREFILL_PAIR");
         if (env && *env) pair = atoi(env) ? 1 : 0;
         if (!a.causal || N <= 128) pair = 0;

@@ -20,7 +20,7 @@ struct PrefillArgs {
     float scale;
     int causal;
     int dtype;      // 0 bf16, 1 fp32
-    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t
+    int pair;       // bf16 causal: one workgroup takes tiles t and n-1-t (-1: launcher decides)
     int order;      // bf16 causal: -1 automatic, 0 heaviest tile first per head in
                     // XCD-contiguous ranges, 1 complementary order within each XCD's share,
                     // 3 tile-major over the whole grid

@@ -262,7 +262,7 @@ constexpr int64_t kTileMajorMaxKV = (int64_t)256 << 20;
 int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
-    if (a.dtype == 0 && a.d == 128 && !a.pair && a.wide == 1) {
+    if (a.dtype == 0 && a.d == 128 && a.pair != 1 && a.wide == 1) {
         const int nqt = (a.N + kWideRows - 1) / kWideRows;
         const int64_t n_work = (int64_t)a.B * a.H * nqt;
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
@@ -273,13 +273,11 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         const int BM = kTileRows;
         const int nqt = (a.N + BM - 1) / BM;
         const int64_t bh = (int64_t)a.B * a.H;
-        const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
-        const int64_t n_work = bh * per_bh;
-        if (n_work > (int64_t)INT32_MAX - 8) return -2;
-        a.n_work = (int)n_work;
-        const int grid = (int)((n_work + 7) / 8 * 8);
-        // complementary order needs whole heads per XCD share (grid = n_work, a multiple of 8 * nqt)
-        const bool can_order = a.causal && !a.pair && n_work % 8 == 0 && (n_work / 8) % nqt == 0;
+        // tile order, decided for one query tile per workgroup; the
+        // complementary order needs whole heads per XCD share (a multiple of
+        // 8 * nqt tiles)
+        const int64_t n_tiles = bh * nqt;
+        const bool can_order = a.causal && a.pair != 1 && n_tiles % 8 == 0 && (n_tiles / 8) % nqt == 0;
         if (a.order == 1 && !can_order) a.order = 0;
         if (a.order < 0) {
             const int64_t kv_bytes = (int64_t)a.B * a.H_kv * a.N * a.d * 2 * 2;
@@ -287,10 +285,22 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
             // query heads of one K/V head on one XCD, whose L2 then serves
             // their K/V (16x32x8192x128 on 4 K/V heads, 256 MiB of K/V: per-head
             // ranges 1075-1081 TFLOP/s, tile-major 905-937)
-            a.order = (can_order && n_work <= kOrderMaxTiles) ? 1
+            a.order = (can_order && n_tiles <= kOrderMaxTiles) ? 1
                     : ((kv_bytes <= kTileMajorMaxKV && a.H_kv == a.H) ? 3 : 0);
         }
-        if (!a.causal || a.pair) a.order = 0;
+        if (!a.causal) a.order = 0;
+        // Pairing (tiles t and nqt-1-t in one workgroup, equal work per
+        // workgroup) by default where a causal grid runs in per-head ranges:
+        // 16x32x8192x128 1057-1064 -> 1077-1084 TFLOP/s, on 4 K/V heads
+        // 1057-1067 -> 1079-1089; one-round grids keep the complementary
+        // order (1x32x2048x128 paired: -2.5 %)
+        if (a.pair < 0) a.pair = (a.causal && a.order == 0 && nqt > 1) ? 1 : 0;
+        if (a.pair) a.order = 0;
+        const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
+        const int64_t n_work = bh * per_bh;
+        if (n_work > (int64_t)INT32_MAX - 8) return -2;
+        a.n_work = (int)n_work;
+        const int grid = (int)((n_work + 7) / 8 * 8);
 #define ATTN_LAUNCH_PREFILL(DD, PP) \
     hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
         if (a.d == 128) {
