@@ -46,6 +46,7 @@
 // no registers), one tile ahead into two buffers, one barrier per tile.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "attn_mfma_core.h"
 #include "bwd_internal.h"
@@ -285,18 +286,13 @@ __device__ __forceinline__ void dq_tile(f32x16 (&dq)[BwdCfg<D>::DBLK], const bf1
     }
 }
 
+// dQ of one 128-query tile starting at q0 of head bh (the body of
+// bwd_dq_kernel; a paired workgroup runs it for two tiles).
 template <int D>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
+__device__ __forceinline__ void dq_query_tile(const BwdArgs& a, int bh, int q0, char* lds0, char* lds1)
 {
     using C = BwdCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
-    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
-    if (L >= n_work) return;
     const int N = a.N;
-    const int nqt = (N + C::BLK - 1) / C::BLK;
-    const int bh = L / nqt;
-    const int q0 = (nqt - 1 - L % nqt) * C::BLK;            // heaviest (most keys) first within a head
     const int G = a.H / a.H_kv;
     const int64_t head_off = (int64_t)bh * N * C::ROW_BYTES;
     const int64_t kv_off = ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / G) * N * C::ROW_BYTES;
@@ -396,6 +392,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
                 w2[1] = pack_bf16(dq[db][r * 4 + 2] * a.scale, dq[db][r * 4 + 3] * a.scale);
                 *(u32x2*)(orow + (db * 32 + r * 8 + g * 4) * 2) = w2;
             }
+    }
+}
+
+// One workgroup per (b, h, 128-query tile), heaviest tile first within a
+// head, or (PAIR, causal launches) per pair of tiles t and nqt-1-t, so that
+// every workgroup does the same number of key tiles.
+template <int D, bool PAIR>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
+{
+    using C = BwdCfg<D>;
+    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= n_work) return;
+    const int nqt = (a.N + C::BLK - 1) / C::BLK;
+    const int per_bh = PAIR ? (nqt + 1) / 2 : nqt;
+    const int bh = L / per_bh, t = L % per_bh;
+    dq_query_tile<D>(a, bh, (nqt - 1 - t) * C::BLK, lds0, lds1);   // heaviest (most keys) first
+    if (PAIR && t != nqt - 1 - t) {
+        __syncthreads();   // LDS reuse across the two tiles
+        dq_query_tile<D>(a, bh, t * C::BLK, lds0, lds1);
     }
 }
 
@@ -661,16 +678,31 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
 {
     constexpr int BLK = 128;
     const int64_t nblk = (a.N + BLK - 1) / BLK;
-    const int64_t n_dq = (int64_t)a.B * a.H * nblk;
+    // causal launches pair the dQ kernel's query tiles (t, nqt-1-t);
+    // ATTN_BWD_PAIR=0 / 1 forces one tile / pairs per workgroup
+    bool pair = a.causal && nblk > 1;
+    const char* env = getenv("ATTN_BWD_PAIR");
+    if (env && *env) pair = atoi(env) != 0 && nblk > 1;
+    const int64_t n_dq = (int64_t)a.B * a.H * (pair ? (nblk + 1) / 2 : nblk);
     const int64_t n_kv = (int64_t)a.B * a.H_kv * ((a.N + 32 * kRoleKB - 1) / (32 * kRoleKB));
     if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
     const int grid_dq = (int)((n_dq + 7) / 8 * 8);
     const int grid_kv = (int)((n_kv + 7) / 8 * 8);
     if (a.d == 128) {
-        hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a, (int)n_dq);
+        if (pair)
+            hipLaunchKernelGGL((bwd_dq_kernel<128, true>), dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a,
+                               (int)n_dq);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a,
+                               (int)n_dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
     } else {
-        hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a, (int)n_dq);
+        if (pair)
+            hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a,
+                               (int)n_dq);
+        else
+            hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a,
+                               (int)n_dq);
         hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
