@@ -568,21 +568,16 @@ __device__ __forceinline__ void role_ds_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], cons
     }
 }
 
+// dK, dV of one key block of BLK keys starting at k0 of K/V head bhk (the
+// body of bwd_dkdv_kernel; a paired workgroup runs it for two blocks).
 template <int D>
-__global__ __launch_bounds__(64 * kRoleWaves, 1) void bwd_dkdv_kernel(BwdArgs a, int n_work)
+__device__ __forceinline__ void dkdv_key_block(const BwdArgs& a, int bhk, int k0, char* lds0, char* lds1,
+                                               char* xch_all)
 {
     using C = BwdCfg<D>;
     using R = RoleCfg<D>;
     constexpr int KB = kRoleKB, BLK = 32 * KB;
-    __shared__ __attribute__((aligned(16))) char lds0[R::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[R::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char xch_all[KB * R::XCH_BYTES];
-    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
-    if (L >= n_work) return;
     const int N = a.N;
-    const int nkb = (N + BLK - 1) / BLK;
-    const int bhk = L / nkb;
-    const int k0 = (L % nkb) * BLK;                         // heaviest (most query tiles) first
     const int b = bhk / a.H_kv, hk = bhk % a.H_kv;
     const int G = a.H / a.H_kv;
     const int64_t kv_off = (int64_t)bhk * N * C::ROW_BYTES;
@@ -672,6 +667,29 @@ __global__ __launch_bounds__(64 * kRoleWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
     }
 }
 
+// One workgroup per (b, K/V head, key block of BLK keys), the block with the
+// most query tiles first, or (PAIR, causal launches) per pair of blocks kb
+// and nkb-1-kb, so that every workgroup sees the same number of query tiles.
+template <int D, bool PAIR>
+__global__ __launch_bounds__(64 * kRoleWaves, 1) void bwd_dkdv_kernel(BwdArgs a, int n_work)
+{
+    using R = RoleCfg<D>;
+    constexpr int KB = kRoleKB, BLK = 32 * KB;
+    __shared__ __attribute__((aligned(16))) char lds0[R::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds1[R::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char xch_all[KB * R::XCH_BYTES];
+    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
+    if (L >= n_work) return;
+    const int nkb = (a.N + BLK - 1) / BLK;
+    const int per = PAIR ? (nkb + 1) / 2 : nkb;
+    const int bhk = L / per, t = L % per;
+    dkdv_key_block<D>(a, bhk, t * BLK, lds0, lds1, xch_all);
+    if (PAIR && t != nkb - 1 - t) {
+        __syncthreads();   // LDS reuse across the two blocks
+        dkdv_key_block<D>(a, bhk, (nkb - 1 - t) * BLK, lds0, lds1, xch_all);
+    }
+}
+
 }  // namespace
 
 int launch_bwd(const BwdArgs& a, hipStream_t stream)
@@ -684,7 +702,11 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
     const char* env = getenv("ATTN_BWD_PAIR");
     if (env && *env) pair = atoi(env) != 0 && nblk > 1;
     const int64_t n_dq = (int64_t)a.B * a.H * (pair ? (nblk + 1) / 2 : nblk);
-    const int64_t n_kv = (int64_t)a.B * a.H_kv * ((a.N + 32 * kRoleKB - 1) / (32 * kRoleKB));
+    const int64_t nkb = (a.N + 32 * kRoleKB - 1) / (32 * kRoleKB);
+    bool pair_kv = a.causal && nkb > 1;
+    const char* env_kv = getenv("ATTN_BWD_PAIR_KV");
+    if (env_kv && *env_kv) pair_kv = atoi(env_kv) != 0 && nkb > 1;
+    const int64_t n_kv = (int64_t)a.B * a.H_kv * (pair_kv ? (nkb + 1) / 2 : nkb);
     if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
     const int grid_dq = (int)((n_dq + 7) / 8 * 8);
     const int grid_kv = (int)((n_kv + 7) / 8 * 8);
@@ -695,7 +717,12 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
         else
             hipLaunchKernelGGL((bwd_dq_kernel<128, false>), dim3(grid_dq), dim3(BwdCfg<128>::kThreads), 0, stream, a,
                                (int)n_dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
+        if (pair_kv)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a,
+                               (int)n_kv);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a,
+                               (int)n_kv);
     } else {
         if (pair)
             hipLaunchKernelGGL((bwd_dq_kernel<64, true>), dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a,
@@ -703,7 +730,12 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
         else
             hipLaunchKernelGGL((bwd_dq_kernel<64, false>), dim3(grid_dq), dim3(BwdCfg<64>::kThreads), 0, stream, a,
                                (int)n_dq);
-        hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a, (int)n_kv);
+        if (pair_kv)
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a,
+                               (int)n_kv);
+        else
+            hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), dim3(grid_kv), dim3(64 * kRoleWaves), 0, stream, a,
+                               (int)n_kv);
     }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
