@@ -5,20 +5,22 @@ One step = one pass of the whole hot path over one batch of synthetic input:
   * causal prefill, bf16, B=16 H=32 N=8192 d=128 (attn_prefill_fwd, one launch)
   * paged decode, bf16, 64 requests x 1 query, ctx ~ U[512, 16384], 16-token
     pages scattered in the pool (paged_attn_fwd: split kernel + combine kernel)
+  * paged chunked prefill, bf16, 8 requests x 512 query rows on prior contexts
+    ~ U[4096, 32768], 32-token pages (paged_attn_fwd: tile kernel + combine)
 Inputs are generated on the GPU before timing (resident in HBM).  The line
 printed reports prefill TFLOP/s as `value` (algorithmic FLOPs = 4*d per
 allowed (query, key) pair, per launch, over the launch's average duration
-measured with HIP events on the launch stream) and the decode KV GB/s
+measured with HIP events on the launch stream), the decode KV GB/s
 (algorithmic bytes: K and V of every context token read once, plus q, o and
-the block table) under "decode".  The oracle (fp64, CPU) is timed on a
-bounded sample of the same prefill workload as `cpu_baseline`.
+the block table) under "decode", the chunked prefill under "c5", and, timed
+after the steps, the small causal prefill B=1 H=32 N=2048 under "c2" (warm,
+and cold: 1 GiB written between launches).  The oracle (fp64, CPU) is timed
+on a bounded sample of the same prefill and decode workloads as
+`cpu_baseline`.
 
 Other modes (--only): prefill, decode, c2, c5 (single workloads), append (KV
 append), gqa (grouped-query prefill and decode), bwd (the backward of the
-causal prefill, MHA and GQA-8), ceiling (the sustained bf16 matrix-core rate
-alone).  With the prefill, the line also carries roofline.mfma_sustained: the
-rate the matrix cores hold on random and on constant operands
-(attn_probe_mfma), i.e. how much of the published peak real data can reach.
+causal prefill, MHA and GQA-8).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -42,8 +44,10 @@ METRIC = "causal prefill TFLOP/s + paged-decode KV GB/s (and % roofline), 1 MI35
 # Sources each measured kernel is built from (csrc/): a PMC summary in
 # profiles/ is used only while these files are unchanged.
 KERNEL_SOURCES = {
-    "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "prefill_gfx950.hip", "attn_internal.h"],
+    "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "prefill_gfx950.hip",
+                   "attn_internal.h"],
     "decode_c4": ["paged_gfx950.hip", "attn_internal.h"],
+    "chunk_c5": ["attn_mfma_core.h", "attn_mfma_kernel.h", "paged_gfx950.hip", "attn_internal.h"],
     "bwd_c3": ["attn_mfma_core.h", "bwd_gfx950.hip", "bwd_internal.h"],
 }
 
@@ -160,52 +164,10 @@ class EventTimer:
         return self.times_ms()[0]
 
 
-def mfma_ceiling(torch, attn, dev, launches=10, warm=2, iters=163840, blocks=2048):
-    """Sustained rate of the bf16 matrix-core instruction the kernels use
-    (attn_probe_mfma) on random operands (seeded N(0,1) rounded to bf16, the
-    kind of data attention multiplies) and on constant operands.  The chip
-    lowers its clock to stay within its power limit, and random operands draw
-    more power, so the random-operand rate is the ceiling a bf16 contraction
-    can reach on real data.  A loop of nothing but MFMAs issues at a rate that
-    depends on where it lands in instruction memory, so each of the probe's
-    16 loop placements is tried (one untimed and two timed launches of about
-    20 ms) and the fastest is then timed over `launches` launches after `warm`
-    untimed ones (median)."""
-    g = torch.Generator(device=dev)
-    g.manual_seed(4242)
-    frags = {"random_operands": torch.randn(65536 * 8, generator=g, device=dev).to(torch.bfloat16),
-             "constant_operands": torch.full((65536 * 8,), 0.5, dtype=torch.bfloat16, device=dev)}
-    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
-
-    def rate(f, placement, n_warm, n_timed):
-        t = EventTimer(torch)
-        flops = 0
-        for i in range(n_warm + n_timed):
-            e = t.start() if i >= n_warm else None
-            _, flops = attn.probe_mfma(f, iters, blocks, placement=placement, out=out)
-            if e is not None:
-                t.stop(e)
-        torch.cuda.synchronize()
-        return flops / (t.median_ms() * 1e-3) / 1e12
-
-    res = {}
-    for name, f in frags.items():
-        sweep = [rate(f, pl, 1, 2) for pl in range(attn.PROBE_PLACEMENTS)]
-        best = max(range(len(sweep)), key=lambda pl: sweep[pl])
-        res[name] = round(rate(f, best, warm, launches), 1)
-        res[name + "_placements"] = [round(x, 1) for x in sweep]
-    res["unit"] = "TFLOP/s"
-    res["kind"] = ("sustained v_mfma_f32_32x32x16_bf16 (attn_probe_mfma): 2048 x 4 waves, 4 accumulation chains "
-                   "per wave, ~20 ms launches, fastest of 16 loop placements")
-    return res
-
-
 class ParityStats:
     """Max / mean |GPU - oracle| over the rows the CPU baseline evaluated
     (outside its timed region), reported beside the parity bounds of the bf16
-    path: O max 2e-2 and mean 2e-3; LSE max 2.5e-3 (every probability is
-    rounded to bf16 before it enters the running sum, a relative error of at
-    most 2^-9 in exp(LSE), i.e. 1.95e-3 in LSE, plus fp32 rounding)."""
+    path (tests/parity.py): O max 2e-2 and mean 2e-3; LSE max 2.5e-3."""
 
     def __init__(self):
         self.n, self.max_o, self.sum_o, self.cnt_o, self.max_lse = 0, 0.0, 0.0, 0, 0.0
@@ -532,25 +494,66 @@ def bench_gqa(args):
     print(json.dumps(res), flush=True)
 
 
-def bench_ceiling(args):
-    """--only ceiling: the sustained matrix-core rate alone (one JSON line)."""
-    import torch
-    import tiled_online_softmax_attention_amd as attn
-    if args.gpus != 1:
-        print("bench.py runs on one GPU only; run with --gpus 1", file=sys.stderr)
+# Kernels behind each measured workload, as the launchers pick them for these
+# shapes (prefill: paired 128-row tiles in per-head ranges take the plain key
+# loop; one-round causal grids take the complementary order and the
+# pipelined key loop).
+KERNELS = {
+    "c3": "prefill_bf16_kernel<128, true, 0>",
+    "c2": "prefill_bf16_kernel<128, false, 1>",
+    "c4": "paged_decode_kernel<128, 16, 1> + paged_combine_kernel<128>",
+    "c5": "paged_chunk_kernel<128, 32> + paged_combine_heads_kernel<128>",
+}
+
+
+def single_gpu_or_exit(args):
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    attn.library()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    c = mfma_ceiling(torch, attn, dev, launches=args.steps, warm=args.warmup)
-    res = {"metric": "sustained bf16 MFMA TFLOP/s, 1 MI355X", "value": c["random_operands"], "unit": "TFLOP/s",
-           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "bf16",
-           "data": "synthetic", "config": {"workload": "attn_probe_mfma, 2048 x 256 lanes, 163840 MFMAs per wave"},
-           "peak": PEAK_BF16_TFLOPS, "frac": round(c["random_operands"] / PEAK_BF16_TFLOPS, 4), "ceiling": c}
-    print(json.dumps(res), flush=True)
+
+
+def time_c2(torch, attn, inputs, dev, warm_launches, cold_launches):
+    """The small causal prefill (1x32x2048x128): warm (inputs in the 256 MB
+    last-level cache, >= warm_launches back to back) and cold (1 GiB written
+    between launches, outside the timed events, so each launch starts from
+    HBM)."""
+    c2 = inputs.C2
+    q2, k2, v2 = inputs.prefill_inputs(c2, dev)
+    o2 = torch.empty_like(q2)
+    l2 = torch.empty((c2.B, c2.H, c2.N), dtype=torch.float32, device=dev)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    fl = prefill_flops(c2.B, c2.H, c2.N, c2.d, True)
+    for _ in range(20):
+        attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
+    torch.cuda.synchronize()
+    warm, cold = EventTimer(torch), EventTimer(torch)
+    for _ in range(warm_launches):
+        e = warm.start()
+        attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
+        warm.stop(e)
+    for _ in range(cold_launches):
+        flush.fill_(1.0)
+        e = cold.start()
+        attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
+        cold.stop(e)
+    torch.cuda.synchronize()
+
+    def entry(t, note):
+        ms = t.mean_ms()
+        tf = fl / (ms * 1e-3) / 1e12
+        return {"value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 5),
+                "launch_ms_median": round(t.median_ms(), 5), "launch_ms_min": round(t.min_ms(), 5),
+                "launches": len(t.pairs), "frac": round(tf / PEAK_BF16_TFLOPS, 4), "note": note}
+
+    res = {"metric": "causal prefill TFLOP/s", "workload": "causal prefill bf16 1x32x2048x128",
+           "kernel": KERNELS["c2"], "flops_per_launch": fl,
+           "algorithmic_bytes_per_launch": prefill_bytes(c2.B, c2.H, c2.N, c2.d)}
+    res["warm"] = entry(warm, "inputs resident in the last-level cache")
+    res["cold"] = entry(cold, "1 GiB written between launches, outside the timed events")
+    res["value"], res["unit"], res["frac"] = res["warm"]["value"], "TFLOP/s", res["warm"]["frac"]
+    del q2, k2, v2, o2, l2, flush
+    return res
 
 
 def main():
@@ -559,12 +562,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the sustained matrix-core rate measurement (attn_probe_mfma)")
+    ap.add_argument("--no-c2", action="store_true", help="skip the small-prefill timing after the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa", "bwd", "ceiling"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "c2", "c5", "append", "gqa", "bwd"],
                     default="all")
     ap.add_argument("--bwd-mha-only", action="store_true",
                     help="--only bwd: skip the grouped-query variant (profiling runs)")
@@ -576,14 +578,7 @@ def main():
         return bench_gqa(args)
     if args.only == "bwd":
         return bench_bwd(args)
-    if args.only == "ceiling":
-        return bench_ceiling(args)
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: the library has no multi-GPU path; run with --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
+    single_gpu_or_exit(args)
 
     import torch
     import tiled_online_softmax_attention_amd as attn
@@ -596,9 +591,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    c3, c4 = inputs.C3, inputs.C4
+    c3, c4, c5 = inputs.C3, inputs.C4, inputs.C5
     do_prefill = args.only in ("all", "prefill")
     do_decode = args.only in ("all", "decode")
+    do_c5 = args.only in ("all", "c5")
 
     if args.probe_copy:
         probe_copy(torch, dev)
@@ -617,17 +613,7 @@ def main():
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         od = torch.empty_like(pi.q)
         lsed = torch.empty(pi.q.shape[:2], dtype=torch.float32, device=dev)
-    if args.only == "c2":
-        c2 = inputs.C2
-        q2, k2, v2 = inputs.prefill_inputs(c2, dev)
-        o2 = torch.empty_like(q2)
-        l2 = torch.empty((c2.B, c2.H, c2.N), dtype=torch.float32, device=dev)
-        # C2's 67 MB of inputs and outputs fit in the 256 MB last-level cache:
-        # the cold variant overwrites 1 GiB between launches (outside the
-        # timed events) so that each launch starts from HBM.
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    if args.only == "c5":
-        c5 = inputs.C5
+    if do_c5:
         p5 = inputs.paged_inputs(c5, dev)
         ctx5 = p5.ctx_lens.cpu().tolist()
         ql5 = p5.q_lens.cpu().tolist()
@@ -640,8 +626,7 @@ def main():
 
     t_pre = EventTimer(torch)
     t_dec = EventTimer(torch)
-    t_aux = EventTimer(torch)
-    t_cold = EventTimer(torch)
+    t_c5 = EventTimer(torch)
 
     def step(record):
         if do_prefill:
@@ -655,52 +640,48 @@ def main():
                                  max_q_len=1, max_ctx_len=max_ctx, out=od, lse=lsed, workspace=ws)
             if record:
                 t_dec.stop(e)
-        if args.only == "c2":
-            e = t_aux.start() if record else None
-            attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
-            if record:
-                t_aux.stop(e)
-            flush.fill_(1.0)
-            e = t_cold.start() if record else None
-            attn.prefill(q2, k2, v2, True, c2.scale, out=o2, lse=l2)
-            if record:
-                t_cold.stop(e)
-        if args.only == "c5":
-            e = t_aux.start() if record else None
+        if do_c5:
+            e = t_c5.start() if record else None
             attn.paged_attention(p5.q, p5.pool, p5.block_table, p5.ctx_lens, p5.q_lens, p5.block_size, p5.scale,
                                  max_q_len=max(ql5), max_ctx_len=max(ctx5), out=o5, lse=l5, workspace=ws5)
             if record:
-                t_aux.stop(e)
+                t_c5.stop(e)
 
-    # C2 launches last ~0.06 ms: time at least 2000 of them (>= 100 ms of
-    # kernel time) so that the median is stable
-    n_steps = max(args.steps, 2000) if args.only == "c2" else args.steps
+    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "causal prefill bf16 16x32x8192x128 + paged decode bf16 64 req x 1 query, "
+                                  "ctx U[512,16384], 16-token pages + paged chunked prefill bf16 8 x 512 rows, "
+                                  "prev ctx U[4096,32768], 32-token pages; H=32, d=128",
+                      "global_batch": c3.B, "seq_len": c3.N, "parallelism": "none (1 GPU)"}}
+    if args.only == "c2":
+        c2res = time_c2(torch, attn, inputs, dev, max(args.steps, 2000), max(args.steps, 200))
+        res.update(value=c2res["value"], unit="TFLOP/s", steps=c2res["warm"]["launches"],
+                   ms_per_step=c2res["warm"]["launch_ms"])
+        res["config"].update(workload="causal prefill bf16 1x32x2048x128", global_batch=1, seq_len=2048)
+        res["c2"] = c2res
+        print(json.dumps(res), flush=True)
+        return
+
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
-    print("timing %d steps" % n_steps, file=sys.stderr, flush=True)
+    print("timing %d steps" % args.steps, file=sys.stderr, flush=True)
     t0 = time.perf_counter()
-    for _ in range(n_steps):
+    for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / n_steps
+    res["ms_per_step"] = round(wall * 1e3 / args.steps, 4)
 
-    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": n_steps,
-           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "causal prefill bf16 16x32x8192x128 + paged decode bf16 64 req x 1 query, "
-                                  "ctx U[512,16384], 16-token pages, H=32, d=128",
-                      "global_batch": c3.B, "seq_len": c3.N, "parallelism": "none (1 GPU)"}}
     if do_prefill:
         ms = t_pre.mean_ms()
         fl = prefill_flops(c3.B, c3.H, c3.N, c3.d, True)
         tf = fl / (ms * 1e-3) / 1e12
         res["value"] = round(tf, 2)
-        traffic = read_traffic("prefill_c3")
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                           "kernel": "prefill_bf16_kernel<128>", "launch_ms": round(ms, 4),
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": read_traffic("prefill_c3"),
+                           "kernel": KERNELS["c3"], "launch_ms": round(ms, 4),
                            "launch_ms_median": round(t_pre.median_ms(), 4), "launch_ms_min": round(t_pre.min_ms(), 4),
                            "flops_per_launch": fl, "algorithmic_bytes_per_launch":
                                prefill_bytes(c3.B, c3.H, c3.N, c3.d)}
@@ -713,42 +694,30 @@ def main():
                          "launch_ms_min": round(t_dec.min_ms(), 4), "bytes_per_call": nb, "sum_ctx": sum(ctx_list),
                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBPS, 4),
-                                      "traffic": read_traffic("decode_c4"),
-                                      "kernels": "paged_decode_kernel<128,16> + paged_combine_kernel<128>"}}
+                                      "traffic": read_traffic("decode_c4"), "kernels": KERNELS["c4"]}}
         if not do_prefill:
             res["value"], res["unit"] = round(gbs, 1), "GB/s"
             res["config"].update(workload="paged decode bf16 64 req x 1 query, ctx U[512,16384], 16-token pages, "
                                           "H=32, d=128", global_batch=len(ctx_list), seq_len=1)
-    if args.only == "c2":
-        ms = t_aux.mean_ms()
-        c2 = inputs.C2
-        fl = prefill_flops(c2.B, c2.H, c2.N, c2.d, True)
-        res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
-        res["config"].update(workload="causal prefill bf16 1x32x2048x128", global_batch=c2.B, seq_len=c2.N)
-        res["launch_ms"] = round(ms, 4)
-        res["launch_ms_median"] = round(t_aux.median_ms(), 4)
-        res["launch_ms_min"] = round(t_aux.min_ms(), 4)
-        ms_c = t_cold.mean_ms()
-        res["cold"] = {"value": round(fl / (ms_c * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "launch_ms": round(ms_c, 4),
-                       "launch_ms_median": round(t_cold.median_ms(), 4), "launch_ms_min": round(t_cold.min_ms(), 4),
-                       "note": "1 GiB written between launches, outside the timed events"}
-    if args.only == "c5":
-        ms = t_aux.mean_ms()
+    if do_c5:
+        ms = t_c5.mean_ms()
         fl = paged_flops(ctx5, ql5, p5.d, p5.H)
         nb = paged_bytes(ctx5, ql5, p5.H, p5.d, p5.block_size)
-        res["value"], res["unit"] = round(fl / (ms * 1e-3) / 1e12, 2), "TFLOP/s"
-        res["config"].update(workload="paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], "
-                                      "32-token pages", global_batch=len(ql5), seq_len=max(ql5))
-        res["launch_ms"] = round(ms, 4)
-        res["kv_gbps"] = round(nb / (ms * 1e-3) / 1e9, 1)
-        res["launch_ms_median"] = round(t_aux.median_ms(), 4)
-        res["launch_ms_min"] = round(t_aux.min_ms(), 4)
-
-    if do_prefill and not args.no_ceiling:
-        print("measuring the sustained matrix-core rate", file=sys.stderr, flush=True)
-        ceil = mfma_ceiling(torch, attn, dev)
-        ceil["prefill_frac_of_random"] = round(res["roofline"]["achieved"] / ceil["random_operands"], 4)
-        res["roofline"]["mfma_sustained"] = ceil
+        tf = fl / (ms * 1e-3) / 1e12
+        res["c5"] = {"metric": "paged chunked-prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+                     "kv_gbps": round(nb / (ms * 1e-3) / 1e9, 1), "launch_ms": round(ms, 4),
+                     "launch_ms_median": round(t_c5.median_ms(), 4), "launch_ms_min": round(t_c5.min_ms(), 4),
+                     "flops_per_call": fl, "bytes_per_call": nb,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                  "traffic": read_traffic("chunk_c5"), "kernels": KERNELS["c5"]}}
+        if args.only == "c5":
+            res["value"], res["unit"] = res["c5"]["value"], "TFLOP/s"
+            res["config"].update(workload="paged chunked prefill bf16 8 x 512 rows, prev ctx U[4096,32768], "
+                                          "32-token pages", global_batch=len(ql5), seq_len=max(ql5))
+    if args.only == "all" and not args.no_c2:
+        print("timing the 1x32x2048x128 prefill", file=sys.stderr, flush=True)
+        res["c2"] = time_c2(torch, attn, inputs, dev, 2000, 200)
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill", "decode"):
         import oracle

@@ -56,9 +56,59 @@ enum {
     ATTN_ERR_LAUNCH = -8,      /* the HIP runtime rejected a launch */
     ATTN_ERR_SCALE = -9,       /* scale is negative, NaN or infinite */
     ATTN_ERR_DEVICE = -10,     /* the current device is not a gfx950 GPU */
-    ATTN_ERR_BAD_TABLE = -11   /* ATTN_DEBUG=1 only: a length or block-table entry breaks the
+    ATTN_ERR_BAD_TABLE = -11,  /* ATTN_DEBUG=1 only: a length or block-table entry breaks the
                                   paged-attention contract (see paged_attn_check) */
+    ATTN_ERR_OPTION = -12      /* a field of attn_launch_opts_t is out of range */
 };
+
+/*
+ * Launch variants of the entry points that take an `opts` pointer.  NULL, or
+ * a field left at its "automatic" value (-1, or 0 where stated), selects what
+ * the library chooses for the shapes at hand (the measured fastest); the
+ * other values force one variant, for tests and tuning.  Set every field:
+ * start from attn_launch_opts_default().  Variants marked [same bits] give
+ * bit-identical results; the others change only the floating-point summation
+ * order (each is checked against the oracle like the default).
+ *
+ *   prefill_kernel : -1 auto; 0 the plain key loop (two LDS buffers, three
+ *                    workgroups per CU); 1 the software-pipelined key loop
+ *                    (four LDS buffers, two workgroups per CU) [same bits].
+ *   prefill_pair   : -1 auto; 0 one 128-row query tile per workgroup; 1
+ *                    query tiles t and n-1-t in one workgroup [same bits].
+ *   prefill_order  : -1 auto; tile order of causal grids: 0 per-head ranges,
+ *                    heaviest tile first; 1 complementary (heavy and light
+ *                    tiles dealt together, for grids of one dispatch round);
+ *                    3 tile-major [same bits].
+ *   paged_path     : -1 auto; 0 the vector decode kernel (only for max_q_len
+ *                    <= 4); 1 the MFMA tile kernel.
+ *   paged_split_tokens : 0 auto; otherwise the keys per context split
+ *                    (rounded up to whole pages, 64-key units on the tile
+ *                    kernel, at most 8192 there).
+ *   paged_decode_heads : 0 auto; 1, 2, 4 or 8 query heads of one K/V group
+ *                    per vector-decode workgroup (must divide H / H_kv; at
+ *                    most 4 with 32-token pages).
+ *   paged_tile_map : -1 auto; work mapping of the tile kernel: 0 contiguous
+ *                    ranges per XCD, 1 (request, K/V head) pairs dealt
+ *                    round-robin, 2 single items round-robin [same bits].
+ *   bwd_pair_q     : -1 auto (on for causal); 0 / 1: query tiles t and
+ *                    n-1-t in one dQ workgroup [same bits].
+ *   bwd_pair_kv    : -1 auto (on for causal); 0 / 1: key blocks kb and
+ *                    nkb-1-kb in one dK/dV workgroup [same bits].
+ */
+typedef struct {
+    int prefill_kernel;
+    int prefill_pair;
+    int prefill_order;
+    int paged_path;
+    int paged_split_tokens;
+    int paged_decode_heads;
+    int paged_tile_map;
+    int bwd_pair_q;
+    int bwd_pair_kv;
+} attn_launch_opts_t;
+
+/* Fills *opts with the automatic values (no-op for NULL). */
+void attn_launch_opts_default(attn_launch_opts_t* opts);
 
 /*
  * Prefill / dense attention (the block-wise forward of "Flash Attention and
@@ -113,7 +163,9 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
  * Device-side contract: 1 <= q_lens[r] <= ctx_lens[r] <= max_ctx_len,
  * q_lens[r] <= max_q_len, every block-table entry needed lies in
  * [0, num_blocks), and ceil(max_ctx_len / block_size) <= max_blocks_per_seq.
- * The kernels do not check it (a bad entry reads outside the pool);
+ * The kernels do not check it (a bad entry reads outside the pool; a
+ * ctx_lens[r] above max_ctx_len is read as max_ctx_len, so it cannot reach
+ * past the table row or the workspace, but the result is then wrong);
  * paged_attn_check does, and with the environment variable ATTN_DEBUG=1 every
  * paged call runs that check first, waits for it (the call then synchronises
  * `stream`) and returns ATTN_ERR_BAD_TABLE, launching nothing else, when the
@@ -155,19 +207,24 @@ size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size,
  *   on the MFMA tile kernel (from 4 heads per group, or query lengths > 4),
  *   up to 8 on the vector decode kernel (groups of 2, q_len <= 4).
  * paged_attn_gqa_workspace_bytes: the workspace paged_attn_gqa_fwd needs.
- * H % H_kv != 0 or H_kv < 1 is ATTN_ERR_SHAPE.
+ * H % H_kv != 0 or H_kv < 1 is ATTN_ERR_SHAPE.  `opts` selects launch
+ * variants (see attn_launch_opts_t; NULL = automatic); an out-of-range field
+ * is ATTN_ERR_OPTION.
  */
 int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int H, int H_kv, int N, int d, float scale, int causal,
-                         attn_dtype_t dtype, void* stream);
+                         attn_dtype_t dtype, const attn_launch_opts_t* opts, void* stream);
 int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
                        const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
                        int block_size, void* o, float* lse,
                        int num_seqs, int H, int H_kv, int d, float scale, int max_blocks_per_seq,
                        int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
-                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       const attn_launch_opts_t* opts, void* stream);
+/* Workspace for paged_attn_gqa_fwd with the same bounds and opts (0 if none
+   is needed or the arguments are invalid). */
 size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int block_size,
-                                      int max_q_len, int max_ctx_len);
+                                      int max_q_len, int max_ctx_len, const attn_launch_opts_t* opts);
 
 /*
  * Backward of the prefill attention ("Flash Attention and Paged Attention",
@@ -196,12 +253,13 @@ size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int 
  *
  * Launches: one kernel for dQ (it also stores each row's LSE and D in the
  * workspace) and one for dK and dV.  Deterministic: the same inputs give the
- * same bits (no atomics).
+ * same bits (no atomics), whatever opts->bwd_pair_q / bwd_pair_kv say.
  */
 int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,
                      int B, int H, int H_kv, int N, int d, float scale, int causal,
-                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                     const attn_launch_opts_t* opts, void* stream);
 
 /* Workspace bytes attn_prefill_bwd needs (0 for invalid sizes). */
 size_t attn_prefill_bwd_workspace_bytes(int B, int H, int N);
@@ -249,7 +307,8 @@ int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block
  *   new_ctx_lens : int32 [num_seqs] device output ctx + new, or NULL; must not
  *                  be ctx_lens itself.
  *   status       : int32 device scalar output, ATTN_APPEND_*.
- *   max_new_len  : host upper bound of new_lens (grid sizing only).
+ *   max_new_len  : host upper bound of new_lens (sizes the copy launch); a
+ *                  new_lens[r] above it is ATTN_APPEND_INVALID.
  *
  * Allocation follows the pages' allocator: a request that needs k more blocks
  * takes k ids off the top of the stack, one pop per block, and requests are
@@ -271,7 +330,8 @@ enum {
     ATTN_APPEND_OK = 0,
     ATTN_APPEND_EXHAUSTED = 1,   /* not enough free blocks for the batch */
     ATTN_APPEND_TABLE_FULL = 2,  /* a request would need more than max_blocks_per_seq blocks */
-    ATTN_APPEND_INVALID = 3      /* negative length, *free_count out of range, or bad block id */
+    ATTN_APPEND_INVALID = 3      /* negative length, a length above max_new_len, *free_count out of
+                                    range, or bad block id */
 };
 int paged_kv_append(const void* k_new, const void* v_new, const int32_t* ctx_lens, const int32_t* new_lens,
                     void* k_pool, void* v_pool, int32_t* block_table, int32_t* free_blocks, int32_t* free_count,
@@ -310,32 +370,6 @@ enum { ATTN_CHECK_OK = 0, ATTN_CHECK_LENGTHS = 1, ATTN_CHECK_TABLE = 2 };
 int paged_attn_check(const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens, int num_seqs,
                      int block_size, int max_blocks_per_seq, int num_blocks, int max_q_len, int max_ctx_len,
                      int32_t* status, void* stream);
-
-/*
- * Measurement aid, not part of the attention path: sustained rate of the
- * bf16 matrix-core instruction the bf16 kernels are built from
- * (v_mfma_f32_32x32x16_bf16, 32768 FLOPs per wave instruction).  The chip
- * holds its clock only while power allows, and that depends on the operand
- * data, so the rate reachable on real (random) data sits below the published
- * peak that roofline fractions are quoted against; this call measures it.
- *   fragments   : bf16 [n_fragments][8] device operand pool; n_fragments a
- *                 power of two >= 16.  Lane t of the grid loads fragments
- *                 (16 t + i) mod n_fragments, i < 16, and uses them as A and B
- *                 operands, a different pair every instruction.
- *   out         : fp32 [blocks * 256] device output (one value per lane, so
- *                 the work is not optimised away).
- *   blocks      : workgroups of 256 lanes (4 waves), 1 .. 65536.
- *   iters       : MFMA instructions per wave, a multiple of 32, up to 2^24.
- *   placement   : 0 .. 15, which of 16 placements of the loop in instruction
- *                 memory (each 4 bytes further on) to run.  A loop of nothing
- *                 but MFMAs issues at a placement-dependent rate on this GPU,
- *                 so a measurement tries all 16 and keeps the fastest.
- * FLOPs per call = blocks * 4 * iters * 32768.  Errors: ATTN_ERR_NULL,
- * ATTN_ERR_ALIGN (pointers not 16-byte aligned), ATTN_ERR_SHAPE (sizes or
- * placement out of range), ATTN_ERR_DEVICE, ATTN_ERR_LAUNCH.
- */
-int attn_probe_mfma(const void* fragments, int n_fragments, float* out, int blocks, int iters, int placement,
-                    void* stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* attn_strerror(int status);

@@ -12,8 +12,8 @@ import tiled_online_softmax_attention_amd as attn
 ROOT = Path(__file__).resolve().parent.parent
 HEADER = ROOT / "include" / "attn.h"
 
-OK, E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE = \
-    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11
+OK, E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE, E_OPT = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10, -11, -12
 
 
 def header_functions():
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_and_version():
     assert attn.attn_strerror(0) == "ok"
-    for code in (E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE):
+    for code in (E_NULL, E_SHAPE, E_HD, E_BS, E_DT, E_AL, E_WS, E_LAUNCH, E_SCALE, E_DEV, E_BAD_TABLE, E_OPT):
         s = attn.attn_strerror(code)
         assert s and s != "unknown attn status"
     assert attn.attn_strerror(-1234) == "unknown attn status"
@@ -128,7 +128,7 @@ def test_workspace_plan_is_pure_and_sane():
 def _max_splits(num_seqs, H, H_kv, d, bs, max_q, max_ctx):
     """Splits per (row, head) the plan chose, read back from the workspace
     size: d + 1 fp32 per (row, head, split), the O part rounded up to 256 B."""
-    ws = attn.paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, bs, max_q, max_ctx)
+    ws = attn.paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, bs, max_q, max_ctx, None)
     return ws // (num_seqs * max_q * H * (d + 1) * 4) if ws else 1
 
 
@@ -216,7 +216,7 @@ def test_release_rejects(kw, code):
 ])
 def test_prefill_gqa_rejects(kw, code):
     a = dict(q=P, k=P2, v=P3, o=P4, lse=NULL, B=1, H=8, H_kv=2, N=64, d=128, scale=0.125, causal=1, dtype=0,
-             stream=NULL)
+             opts=None, stream=NULL)
     a.update(kw)
     assert attn.attn_prefill_gqa_fwd(**a) == code
 
@@ -230,7 +230,7 @@ def test_paged_gqa_rejects(kw, code):
     a = dict(q=P, k_pool=P2, v_pool=P3, block_table=P4, ctx_lens=P, q_lens=P2, block_size=16, o=P3, lse=NULL,
              num_seqs=4, H=8, H_kv=2, d=128, scale=0.1, max_blocks_per_seq=64, kv_block_stride=2 * 2 * 16 * 128,
              num_blocks=100, max_q_len=1, max_ctx_len=1024, dtype=0, workspace=NULL, workspace_bytes=0,
-             stream=NULL)
+             opts=None, stream=NULL)
     a.update(kw)
     if code == E_DEV and attn.paged_attn_gqa_workspace_bytes(4, 8, 2, 128, 16, 1, 1024):
         a["workspace"] = ctypes.c_void_p(8 << 20)
@@ -247,7 +247,7 @@ def test_gqa_workspace_matches_plain_at_equal_heads():
 
 def bwd(**kw):
     a = dict(q=P, k=P2, v=P3, o=P4, lse=P, dout=P2, dq=P3, dk=P4, dv=P, B=2, H=8, H_kv=2, N=100, d=128, scale=0.125,
-             causal=1, dtype=0, workspace=P2, workspace_bytes=2 * 8 * 100 * 8, stream=NULL)
+             causal=1, dtype=0, workspace=P2, workspace_bytes=2 * 8 * 100 * 8, opts=None, stream=NULL)
     a.update(kw)
     return attn.attn_prefill_bwd(**a)
 
@@ -274,23 +274,63 @@ def test_bwd_workspace_bytes():
         assert attn.attn_prefill_bwd_workspace_bytes(*bad) == 0
 
 
-def probe(**kw):
-    a = dict(fragments=P, n_fragments=65536, out=P2, blocks=2048, iters=163840, placement=0, stream=NULL)
-    a.update(kw)
-    return attn.attn_probe_mfma(**a)
+def opts(**kw):
+    return attn._opts(kw)
 
 
-@pytest.mark.parametrize("kw,code", [
-    (dict(fragments=NULL), E_NULL), (dict(out=NULL), E_NULL),
-    (dict(fragments=ctypes.c_void_p((1 << 20) + 8)), E_AL), (dict(out=ctypes.c_void_p((2 << 20) + 4)), E_AL),
-    (dict(n_fragments=8), E_SHAPE), (dict(n_fragments=48), E_SHAPE), (dict(n_fragments=0), E_SHAPE),
-    (dict(blocks=0), E_SHAPE), (dict(blocks=(1 << 16) + 1), E_SHAPE),
-    (dict(iters=0), E_SHAPE), (dict(iters=48), E_SHAPE), (dict(iters=(1 << 24) + 32), E_SHAPE),
-    (dict(placement=-1), E_SHAPE), (dict(placement=16), E_SHAPE),
-    (dict(), E_DEV), (dict(n_fragments=16, blocks=1, iters=32, placement=15), E_DEV),
+def test_launch_opts_default_values():
+    o = attn.LaunchOpts()
+    for name, _ in attn.LaunchOpts._fields_:
+        setattr(o, name, 77)
+    attn.attn_launch_opts_default(ctypes.byref(o))
+    want = dict(prefill_kernel=-1, prefill_pair=-1, prefill_order=-1, paged_path=-1, paged_split_tokens=0,
+                paged_decode_heads=0, paged_tile_map=-1, bwd_pair_q=-1, bwd_pair_kv=-1)
+    assert {name: getattr(o, name) for name, _ in attn.LaunchOpts._fields_} == want
+    attn.attn_launch_opts_default(None)   # NULL is a no-op
+
+
+@pytest.mark.parametrize("field,bad", [
+    ("prefill_kernel", 2), ("prefill_kernel", -2), ("prefill_pair", 2), ("prefill_order", 2), ("prefill_order", 4),
+    ("paged_path", 2), ("paged_split_tokens", -1), ("paged_decode_heads", 3), ("paged_decode_heads", 16),
+    ("paged_tile_map", 3), ("bwd_pair_q", 5), ("bwd_pair_kv", -3),
 ])
-def test_probe_rejects(kw, code):
-    assert probe(**kw) == code
+def test_out_of_range_options_rejected(field, bad):
+    """Every entry point that takes opts rejects an out-of-range field with
+    ATTN_ERR_OPTION before anything is launched (and the workspace query
+    answers 0)."""
+    o = opts(**{field: bad})
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=NULL, B=1, H=8, H_kv=2, N=64, d=128, scale=0.125, causal=1, dtype=0,
+             opts=o, stream=NULL)
+    assert attn.attn_prefill_gqa_fwd(**a) == E_OPT
+    b = dict(q=P, k_pool=P2, v_pool=P3, block_table=P4, ctx_lens=P, q_lens=P2, block_size=16, o=P3, lse=NULL,
+             num_seqs=4, H=8, H_kv=2, d=128, scale=0.1, max_blocks_per_seq=64, kv_block_stride=2 * 2 * 16 * 128,
+             num_blocks=100, max_q_len=1, max_ctx_len=1024, dtype=0, workspace=ctypes.c_void_p(8 << 20),
+             workspace_bytes=1 << 30, opts=o, stream=NULL)
+    assert attn.paged_attn_gqa_fwd(**b) == E_OPT
+    assert attn.paged_attn_gqa_workspace_bytes(4, 8, 2, 128, 16, 1, 1024, o) == 0
+    assert bwd(opts=o) == E_OPT
+
+
+def test_decode_heads_option_must_divide_the_group():
+    b = dict(q=P, k_pool=P2, v_pool=P3, block_table=P4, ctx_lens=P, q_lens=P2, block_size=16, o=P3, lse=NULL,
+             num_seqs=4, H=12, H_kv=4, d=128, scale=0.1, max_blocks_per_seq=64, kv_block_stride=2 * 4 * 16 * 128,
+             num_blocks=100, max_q_len=1, max_ctx_len=1024, dtype=0, workspace=ctypes.c_void_p(8 << 20),
+             workspace_bytes=1 << 30, opts=opts(paged_decode_heads=2), stream=NULL)
+    assert attn.paged_attn_gqa_fwd(**b) == E_OPT          # groups of 3
+    b["opts"] = opts(paged_decode_heads=1)
+    assert attn.paged_attn_gqa_fwd(**b) == E_DEV
+    b.update(H=32, block_size=32, kv_block_stride=2 * 4 * 32 * 128, opts=opts(paged_decode_heads=8))
+    assert attn.paged_attn_gqa_fwd(**b) == E_OPT          # 8 heads per workgroup needs 16-token pages
+
+
+def test_split_option_sets_the_workspace():
+    """A forced split size changes the plan and so the workspace the call
+    needs; the automatic plan equals passing no options."""
+    auto = attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, None)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts()) == auto
+    s256 = attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=256))
+    assert s256 == (64 * 32 * 64 * 128 * 4 + 255) // 256 * 256 + 64 * 32 * 64 * 4
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=1 << 20)) == 0
 
 
 def check_call(**kw):

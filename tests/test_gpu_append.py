@@ -114,6 +114,34 @@ def test_failed_append_changes_nothing(what):
         assert torch.equal(a, b)
 
 
+def test_append_length_above_bound_changes_nothing():
+    """A new_lens[r] above the host bound max_new_len (which sizes the copy
+    launch) is ATTN_APPEND_INVALID: no block is taken, no table entry, pool
+    slot or count changes."""
+    ctx, new = [5, 40, 0], [30, 20, 16]
+    ai = inputs.append_inputs(ctx, new, 2, 128, 16, 78)
+    dc = DeviceCache(ai)
+    snap = (dc.pool.clone(), dc.table.clone(), dc.free.clone(), dc.count.clone())
+    k_new, v_new = ai.k_new.to(DEV), ai.v_new.to(DEV)
+    ctx_d = torch.tensor(ctx, dtype=torch.int32, device=DEV)
+    new_d = torch.tensor(new, dtype=torch.int32, device=DEV)
+    nctx = torch.full_like(ctx_d, -5)
+    _, status = attn.kv_append(k_new, v_new, ctx_d, new_d, dc.pool, dc.table, dc.free, dc.count, 16,
+                               max_new_len=29, new_ctx_lens=nctx, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == attn.APPEND_INVALID
+    assert torch.equal(snap[0].view(torch.int16), dc.pool.view(torch.int16))
+    for a, b in zip(snap[1:], (dc.table, dc.free, dc.count)):
+        assert torch.equal(a, b)
+    assert nctx.tolist() == [-5, -5, -5]
+    # the same call with the true bound succeeds and matches the oracle
+    free0 = dc.free.cpu().clone()
+    nctx2, status2 = dc.append(ctx, new, k_new, v_new)
+    assert status2 == attn.APPEND_OK and nctx2 == [35, 60, 16]
+    dc.oracle_append(ctx, new, k_new, v_new)
+    dc.assert_matches_oracle(free0)
+
+
 def test_release_then_append_reuses_last_released():
     ai = inputs.append_inputs([0, 0], [40, 3], 2, 64, 16, 91)
     dc = DeviceCache(ai)

@@ -111,6 +111,31 @@ def test_bwd_deterministic():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("B,H,H_kv,N,d", [(1, 2, 2, 300, 128), (1, 8, 2, 700, 128), (2, 4, 4, 391, 64)])
+def test_bwd_pairing_bit_identical(B, H, H_kv, N, d):
+    """Paired dQ query tiles (t, n-1-t) and paired dK/dV key blocks (kb,
+    nkb-1-kb) only change which workgroup runs which tile: every combination
+    gives the bits of the unpaired launch (odd tile and block counts, so a
+    middle tile / block runs alone; a grouped-query shape)."""
+    cfg = inputs.PrefillConfig("bwd_pair", B, H, N, d, torch.bfloat16, True, 17 + N, H_kv=H_kv)
+    q, k, v = inputs.prefill_inputs(cfg, DEV)
+    do = inputs.grad_output(cfg, DEV)
+    o, lse = attn.prefill(q, k, v, True, cfg.scale)
+    ref = None
+    for pq in (0, 1):
+        for pkv in (0, 1):
+            got = attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale,
+                                   options={"bwd_pair_q": pq, "bwd_pair_kv": pkv})
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = got
+            for a, b in zip(ref, got):
+                assert torch.equal(a.view(torch.int16), b.view(torch.int16)), (pq, pkv)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, cfg.scale, True)
+    for name, g, r in zip(("dq", "dk", "dv"), ref, (rq, rk, rv)):
+        check_grad(name, g, r)
+
+
 def test_bwd_workspace_contents_ignored():
     """A workspace full of garbage on entry gives the same gradients."""
     cfg = inputs.PrefillConfig("bwd_ws", 1, 2, 300, 128, torch.bfloat16, True, 8)

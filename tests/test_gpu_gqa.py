@@ -1,8 +1,6 @@
 """GPU parity of grouped-query attention (attn_prefill_gqa_fwd, paged_attn_gqa_fwd
 through the C ABI) against the fp64 oracle, and GQA == multi-head attention on
 explicitly repeated K/V heads."""
-import os
-
 import pytest
 import torch
 
@@ -15,26 +13,14 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-class env_set:
-    """Set library knobs (ATTN_SPLIT_TOKENS, ATTN_DECODE_PATH) for one block."""
-
-    def __init__(self, **kw):
-        self.kw = {k: str(v) for k, v in kw.items() if v is not None}
-
-    def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kw}
-        os.environ.update(self.kw)
-
-    def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
-def env_split(tokens, path=None):
-    return env_set(ATTN_SPLIT_TOKENS=tokens, ATTN_DECODE_PATH=path)
+def path_opts(split=None, path=None):
+    """Launch options forcing the context split size and the decode path."""
+    o = {}
+    if split is not None:
+        o["paged_split_tokens"] = int(split)
+    if path is not None:
+        o["paged_path"] = int(path)
+    return o or None
 
 
 @pytest.mark.parametrize("B,H,H_kv,N,d,causal,dtype", [
@@ -54,7 +40,8 @@ def test_prefill_gqa_matches_oracle(B, H, H_kv, N, d, causal, dtype):
         o = torch.empty_like(q)
         lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
         rc = attn.attn_prefill_gqa_fwd(attn._ptr(q), attn._ptr(k), attn._ptr(v), attn._ptr(o), attn._ptr(lse), B, H,
-                                       H_kv, N, d, cfg.scale, int(causal), attn._dtype_code(q), attn._stream(None))
+                                       H_kv, N, d, cfg.scale, int(causal), attn._dtype_code(q), None,
+                                       attn._stream(None))
         assert rc == 0
     else:
         o, lse = attn.prefill(q, k, v, causal, cfg.scale)
@@ -79,10 +66,9 @@ def make_gqa(ctx, ql, H, H_kv, d=128, bs=16, seed=1):
 
 
 def run_paged(pi, split=None, path=None):
-    with env_split(split, path):
-        o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
-                                      pi.scale)
-        torch.cuda.synchronize()
+    o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                  pi.scale, options=path_opts(split, path))
+    torch.cuda.synchronize()
     return o, lse
 
 
@@ -133,10 +119,9 @@ def test_paged_gqa_equals_repeated_heads(ql):
     pi = make_gqa(ctx, [ql] * 4, 32, 4, seed=33 + ql)
     # the default split size depends on the workgroup count; fix it for both
     o1, l1 = run_paged(pi, split=256, path=0)
-    with env_split(256, 0):
-        o2, l2 = attn.paged_attention(pi.q, repeat_pool(pi.pool, 8), pi.block_table, pi.ctx_lens, pi.q_lens, 16,
-                                      pi.scale)
-        torch.cuda.synchronize()
+    o2, l2 = attn.paged_attention(pi.q, repeat_pool(pi.pool, 8), pi.block_table, pi.ctx_lens, pi.q_lens, 16,
+                                  pi.scale, options=path_opts(256, 0))
+    torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
@@ -167,8 +152,7 @@ def test_c4_gqa8_full_size_sampled_rows():
     lg = torch.stack([lse[r, h] for r, h in trip])
     check_close("c4 gqa8 sampled", og, o_ref, lg, l_ref, torch.bfloat16)
     o1, l1 = run_paged(pi, split=512, path=0)
-    with env_split(512, 0):
-        o2, l2 = attn.paged_attention(pi.q, repeat_pool(pi.pool, 8), pi.block_table, pi.ctx_lens, pi.q_lens, 16,
-                                      pi.scale)
-        torch.cuda.synchronize()
+    o2, l2 = attn.paged_attention(pi.q, repeat_pool(pi.pool, 8), pi.block_table, pi.ctx_lens, pi.q_lens, 16,
+                                  pi.scale, options=path_opts(512, 0))
+    torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)

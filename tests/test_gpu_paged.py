@@ -1,6 +1,4 @@
 """GPU parity of paged_attn_fwd and paged_kv_gather (through the C ABI)."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -14,23 +12,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-class env_split:
-    """Force the context split size (tokens) for one call."""
-
-    def __init__(self, tokens):
-        self.tokens = tokens
-
-    def __enter__(self):
-        self.old = os.environ.get("ATTN_SPLIT_TOKENS")
-        if self.tokens is not None:
-            os.environ["ATTN_SPLIT_TOKENS"] = str(self.tokens)
-
-    def __exit__(self, *a):
-        if self.tokens is not None:
-            if self.old is None:
-                os.environ.pop("ATTN_SPLIT_TOKENS", None)
-            else:
-                os.environ["ATTN_SPLIT_TOKENS"] = self.old
+def split_opts(tokens):
+    """Launch options forcing the context split size (tokens), or None."""
+    return None if tokens is None else {"paged_split_tokens": int(tokens)}
 
 
 def make(ctx, ql, H=4, d=128, bs=16, seed=1, **kw):
@@ -41,10 +25,9 @@ def make(ctx, ql, H=4, d=128, bs=16, seed=1, **kw):
 def run(pi, split=None, name="paged"):
     log("%s: num_seqs=%d H=%d d=%d bs=%d ctx=%s q=%s split=%s" % (
         name, pi.num_seqs, pi.H, pi.d, pi.block_size, pi.ctx_lens.tolist()[:8], pi.q_lens.tolist()[:8], split))
-    with env_split(split):
-        o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
-                                      pi.scale)
-        torch.cuda.synchronize()
+    o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                  pi.scale, options=split_opts(split))
+    torch.cuda.synchronize()
     return o, lse
 
 
@@ -122,11 +105,11 @@ def test_permutation_bit_identity_and_aliasing():
     q = a.q.clone()
     q[1] = q[0]
     for split in (None, 128):
-        with env_split(split):
-            o1, l1 = attn.paged_attention(q, a.pool, a.block_table, a.ctx_lens, a.q_lens, bs)
-            o2, l2 = attn.paged_attention(q, pool2, table2, a.ctx_lens, a.q_lens, bs)
-            o3, l3 = attn.paged_attention(q, a.pool, table_alias, a.ctx_lens, a.q_lens, bs)
-            torch.cuda.synchronize()
+        op = split_opts(split)
+        o1, l1 = attn.paged_attention(q, a.pool, a.block_table, a.ctx_lens, a.q_lens, bs, options=op)
+        o2, l2 = attn.paged_attention(q, pool2, table2, a.ctx_lens, a.q_lens, bs, options=op)
+        o3, l3 = attn.paged_attention(q, a.pool, table_alias, a.ctx_lens, a.q_lens, bs, options=op)
+        torch.cuda.synchronize()
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         assert torch.equal(o3[0], o3[1]) and torch.equal(o3[0], o1[0]) and torch.equal(o3[2], o1[2])
 
@@ -244,15 +227,16 @@ def test_outputs_and_workspace_in_bounds(ql, split):
     lbuf = torch.full((2 * G + rows * H,), 3.0, dtype=torch.float32, device=DEV)
     o = obuf[G:G + rows * H * d].view(rows, H, d)
     lse = lbuf[G:G + rows * H].view(rows, H)
-    with env_split(split):
-        max_q, max_ctx = int(pi.q_lens.max()), int(pi.ctx_lens.max())
-        ws_bytes = attn.paged_attn_workspace_bytes(pi.num_seqs, H, d, pi.block_size, max_q, max_ctx)
-        wbuf = torch.full((ws_bytes + 2 * G,), 0x5A, dtype=torch.uint8, device=DEV)
-        ws = wbuf[G:G + ws_bytes] if ws_bytes else None   # offset G keeps the 256-byte alignment
-        log("canaries ql=%d split=%s ws=%d" % (ql, split, ws_bytes))
-        attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
-                             max_q_len=max_q, max_ctx_len=max_ctx, out=o, lse=lse, workspace=ws)
-        torch.cuda.synchronize()
+    op = split_opts(split)
+    max_q, max_ctx = int(pi.q_lens.max()), int(pi.ctx_lens.max())
+    ws_bytes = attn.paged_attn_gqa_workspace_bytes(pi.num_seqs, H, H, d, pi.block_size, max_q, max_ctx,
+                                                   attn._opts(op))
+    wbuf = torch.full((ws_bytes + 2 * G,), 0x5A, dtype=torch.uint8, device=DEV)
+    ws = wbuf[G:G + ws_bytes] if ws_bytes else None   # offset G keeps the 256-byte alignment
+    log("canaries ql=%d split=%s ws=%d" % (ql, split, ws_bytes))
+    attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
+                         max_q_len=max_q, max_ctx_len=max_ctx, out=o, lse=lse, workspace=ws, options=op)
+    torch.cuda.synchronize()
     assert bool((obuf[:G] == 7.0).all()) and bool((obuf[-G:] == 7.0).all())
     assert bool((lbuf[:G] == 3.0).all()) and bool((lbuf[-G:] == 3.0).all())
     assert bool((wbuf[:G] == 0x5A).all()) and bool((wbuf[-G:] == 0x5A).all())
@@ -270,18 +254,40 @@ def test_chunk_work_mappings_bit_identical(ctx, ql, H, H_kv):
     qls = [min(ql, c) for c in ctx]
     pi = inputs.build_paged(ctx, qls, H_kv, 128, 16, 77, DEV, H_q=H)
     outs = []
-    old = os.environ.get("ATTN_CHUNK_MAP")
-    try:
-        for m in ("0", "1", "2"):
-            os.environ["ATTN_CHUNK_MAP"] = m
-            outs.append(run(pi, split=256, name="map %s" % m))
-    finally:
-        if old is None:
-            os.environ.pop("ATTN_CHUNK_MAP", None)
-        else:
-            os.environ["ATTN_CHUNK_MAP"] = old
+    for m in (0, 1, 2):
+        log("chunk mapping %d" % m)
+        o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                      pi.scale, options={"paged_split_tokens": 256, "paged_tile_map": m})
+        torch.cuda.synchronize()
+        outs.append((o, lse))
     for o, l in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0][0].view(torch.int16)) and torch.equal(l, outs[0][1])
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
                                           pi.scale)
     check_close("chunk mappings", outs[0][0], o_ref, outs[0][1], l_ref, torch.bfloat16)
+
+
+def test_context_above_bound_reads_as_bound():
+    """A ctx_lens[r] above the host bound max_ctx_len breaks the contract; the
+    kernels read it as max_ctx_len, so no kernel reaches past the workspace
+    (guard words) and the result is attention over the bound's context.
+    Every table row holds the real contexts' pages, so table reads stay in the
+    row either way; only the split count, which sizes the workspace, depends
+    on the bound."""
+    ctx, ql = [1500, 900, 2100], [1, 1, 1]
+    pi = make(ctx, ql, H=4, d=128, bs=16, seed=61)
+    bound = 1000
+    op = {"paged_split_tokens": 256}
+    ws_bytes = attn.paged_attn_gqa_workspace_bytes(pi.num_seqs, 4, 4, 128, 16, 1, bound, attn._opts(op))
+    assert ws_bytes > 0
+    G = 1 << 16
+    wbuf = torch.full((ws_bytes + 2 * G,), 0x5A, dtype=torch.uint8, device=DEV)
+    ws = wbuf[G:G + ws_bytes]
+    o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, 16, pi.scale,
+                                  max_q_len=1, max_ctx_len=bound, workspace=ws, options=op)
+    torch.cuda.synchronize()
+    assert bool((wbuf[:G] == 0x5A).all()) and bool((wbuf[-G:] == 0x5A).all())
+    clamped = torch.clamp(pi.ctx_lens, max=bound)
+    o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, clamped, pi.q_lens, 16, pi.scale)
+    check_close("ctx above bound", o, o_ref, lse, l_ref, torch.bfloat16)
+

@@ -1,6 +1,5 @@
 """GPU parity of attn_prefill_fwd against the fp64 oracle (through the C ABI)."""
 import math
-import os
 
 import numpy as np
 import pytest
@@ -15,34 +14,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-class env_set:
-    """Set environment knobs of the library for one call."""
-
-    def __init__(self, **kw):
-        self.kw = {k: v for k, v in kw.items() if v is not None}
-
-    def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kw}
-        for k, v in self.kw.items():
-            os.environ[k] = str(v)
-
-    def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
-
-
-def run_case(B, H, N, d, dtype, causal, seed, pair=None, wide=None):
+def run_case(B, H, N, d, dtype, causal, seed, options=None):
     cfg = inputs.PrefillConfig("case", B, H, N, d, dtype, causal, seed)
-    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d pair=%s wide=%s"
-        % (B, H, N, d, dtype, causal, seed, pair, wide))
+    log("prefill case B=%d H=%d N=%d d=%d %s causal=%d seed=%d options=%s"
+        % (B, H, N, d, dtype, causal, seed, options))
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    with env_set(ATTN_PREFILL_PAIR=None if pair is None else int(pair),
-                 ATTN_PREFILL_WIDE=None if wide is None else int(wide)):
-        o, lse = attn.prefill(q, k, v, causal, cfg.scale)
-        torch.cuda.synchronize()
+    o, lse = attn.prefill(q, k, v, causal, cfg.scale, options=options)
+    torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, cfg.scale, causal)
     return check_close("B%dH%dN%dd%d" % (B, H, N, d), o, o_ref, lse, lse_ref, dtype), (q, k, v, o, lse)
 
@@ -77,7 +55,7 @@ def test_fp32_shapes(N, d, causal):
 
 @pytest.mark.parametrize("pair", [False, True])
 def test_pair_mode_matches_oracle(pair):
-    run_case(2, 4, 1000, 128, torch.bfloat16, True, 7, pair=pair)
+    run_case(2, 4, 1000, 128, torch.bfloat16, True, 7, options={"prefill_pair": int(pair)})
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 32, 2048, 128), (1, 8, 1000, 64), (2, 4, 640, 128), (1, 3, 700, 64),
@@ -90,9 +68,8 @@ def test_tile_order_bit_identical(B, H, N, d):
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     outs = []
     for order in (0, 1, 3):
-        with env_set(ATTN_PREFILL_ORDER=order):
-            outs.append(attn.prefill(q, k, v, True, cfg.scale))
-            torch.cuda.synchronize()
+        outs.append(attn.prefill(q, k, v, True, cfg.scale, options={"prefill_order": order}))
+        torch.cuda.synchronize()
     o0, l0 = outs[0]
     for o1, l1 in outs[1:]:
         assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)) and torch.equal(l0, l1)
@@ -113,42 +90,56 @@ def test_key_tile_counts(N, d, causal):
 
 @pytest.mark.parametrize("N", [1, 31, 200, 256, 257, 640, 1100])
 @pytest.mark.parametrize("causal", [False, True])
-def test_wide_kernel_matches_oracle(N, causal):
-    """The 64-rows-per-wave variant (ATTN_PREFILL_WIDE=1): no full tile, a
-    partial 256-row tile, pipelined key loops of 4 and more tiles followed by
+@pytest.mark.parametrize("d", [64, 128])
+def test_pipelined_key_loop_matches_oracle(N, causal, d):
+    """The software-pipelined key loop (prefill_kernel = 1): no full tile,
+    partial 128-row tiles, pipelined runs of 4 and more key tiles followed by
     masked tiles, and rows past N in the last tile."""
-    run_case(2, 3, N, 128, torch.bfloat16, causal, 700 + N, wide=1)
+    run_case(2, 3, N, d, torch.bfloat16, causal, 700 + N + d, options={"prefill_kernel": 1})
 
 
-def test_wide_kernel_grouped_heads_and_repeat():
-    """Grouped-query heads through the wide kernel, and two calls giving the
-    same bits."""
-    cfg = inputs.PrefillConfig("wide_gqa", 1, 8, 777, 128, torch.bfloat16, True, 31, H_kv=2)
+@pytest.mark.parametrize("B,H,H_kv,N,d,causal", [(1, 8, 8, 777, 128, True), (2, 4, 4, 300, 64, True),
+                                                 (1, 8, 2, 1100, 128, True), (1, 4, 4, 640, 128, False),
+                                                 (1, 32, 32, 2048, 128, True)])
+def test_key_loops_bit_identical(B, H, H_kv, N, d, causal):
+    """The plain and the pipelined key loop apply the same operations to O, l
+    and the offset in the same order: identical bits, for every tile order
+    and pairing they run under."""
+    cfg = inputs.PrefillConfig("loops", B, H, N, d, torch.bfloat16, causal, 31 + N, H_kv=H_kv)
     q, k, v = inputs.prefill_inputs(cfg, DEV)
-    with env_set(ATTN_PREFILL_WIDE=1):
-        o1, l1 = attn.prefill(q, k, v, True, cfg.scale)
-        o2, l2 = attn.prefill(q, k, v, True, cfg.scale)
-        torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    o_ref, l_ref = oracle.attention(q, k, v, cfg.scale, True)
-    check_close("wide_gqa", o1, o_ref, l1, l_ref, torch.bfloat16)
+    ref = None
+    for kernel in (0, 1):
+        for pair in (0, 1):
+            o, lse = attn.prefill(q, k, v, causal, cfg.scale, options={"prefill_kernel": kernel, "prefill_pair": pair})
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = (o, lse)
+            else:
+                assert torch.equal(ref[0].view(torch.int16), o.view(torch.int16)) and torch.equal(ref[1], lse), \
+                    (kernel, pair)
+    if B * H * N <= 8 * 1100:
+        o_ref, l_ref = oracle.attention(q, k, v, cfg.scale, causal)
+        check_close("loops", ref[0], o_ref, ref[1], l_ref, torch.bfloat16)
 
 
-def test_deterministic_and_pair_independent():
-    cfg = inputs.PrefillConfig("det", 1, 8, 777, 128, torch.bfloat16, True, 9)
+@pytest.mark.parametrize("N", [777, 1000])
+def test_deterministic_and_pair_independent(N):
+    """Repeat calls give the same bits, and so do one query tile per
+    workgroup and paired tiles t / n-1-t (per-head ranges, where pairing
+    applies; N = 777 has 7 tiles, so the middle tile runs alone)."""
+    cfg = inputs.PrefillConfig("det", 1, 8, N, 128, torch.bfloat16, True, 9)
     q, k, v = inputs.prefill_inputs(cfg, DEV)
     o1, l1 = attn.prefill(q, k, v, True, cfg.scale)
     o2, l2 = attn.prefill(q, k, v, True, cfg.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    os.environ["ATTN_PREFILL_PAIR"] = "0"
-    try:
-        o3, l3 = attn.prefill(q, k, v, True, cfg.scale)
+    res = {}
+    for pair in (0, 1):
+        res[pair] = attn.prefill(q, k, v, True, cfg.scale, options={"prefill_order": 0, "prefill_pair": pair})
         torch.cuda.synchronize()
-    finally:
-        os.environ.pop("ATTN_PREFILL_PAIR", None)
     # same tiles, same order of key tiles within a tile: identical bits
-    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    for o3, l3 in res.values():
+        assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
 def test_scale_zero_closed_form():

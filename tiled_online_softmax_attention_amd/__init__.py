@@ -16,8 +16,9 @@ __all__ = [
     "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
     "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
     "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "paged_attn_check",
-    "attn_probe_mfma", "attn_strerror", "attn_version", "prefill", "prefill_bwd", "paged_attention", "paged_check",
-    "probe_mfma", "CHECK_OK", "CHECK_LENGTHS", "CHECK_TABLE", "ERR_BAD_TABLE",
+    "attn_launch_opts_default", "LaunchOpts", "attn_strerror", "attn_version", "prefill", "prefill_bwd",
+    "paged_attention", "paged_check", "CHECK_OK", "CHECK_LENGTHS", "CHECK_TABLE", "ERR_BAD_TABLE",
+    "ERR_OPTION",
     "gather", "kv_append", "kv_release", "APPEND_OK", "APPEND_EXHAUSTED", "APPEND_TABLE_FULL",
     "APPEND_INVALID",
 ]
@@ -34,6 +35,7 @@ APPEND_OK, APPEND_EXHAUSTED, APPEND_TABLE_FULL, APPEND_INVALID = 0, 1, 2, 3
 # return under ATTN_DEBUG=1 when the check fails
 CHECK_OK, CHECK_LENGTHS, CHECK_TABLE = 0, 1, 2
 ERR_BAD_TABLE = -11
+ERR_OPTION = -12
 
 # every symbol include/attn.h declares
 exported_symbols = (
@@ -49,12 +51,34 @@ exported_symbols = (
     "attn_prefill_bwd",
     "attn_prefill_bwd_workspace_bytes",
     "paged_attn_check",
-    "attn_probe_mfma",
+    "attn_launch_opts_default",
     "attn_strerror",
     "attn_version",
 )
 
 _lib = None
+
+
+class LaunchOpts(ctypes.Structure):
+    """attn_launch_opts_t: launch variants of the entry points that take opts
+    (include/attn.h documents every field; -1 / 0 = automatic)."""
+    _fields_ = [(name, ctypes.c_int) for name in (
+        "prefill_kernel", "prefill_pair", "prefill_order", "paged_path", "paged_split_tokens",
+        "paged_decode_heads", "paged_tile_map", "bwd_pair_q", "bwd_pair_kv")]
+
+
+def _opts(options):
+    """ctypes pointer to an attn_launch_opts_t with the automatic values except
+    the fields named in `options` (a dict), or None for options=None."""
+    if options is None:
+        return None
+    o = LaunchOpts()
+    library().attn_launch_opts_default(ctypes.byref(o))
+    for k, v in options.items():
+        if k not in dict(LaunchOpts._fields_):
+            raise KeyError("unknown launch option %r" % k)
+        setattr(o, k, int(v))
+    return ctypes.pointer(o)
 
 
 class AttnError(RuntimeError):
@@ -89,20 +113,21 @@ def library():
     lib.paged_kv_append.restype = I
     lib.paged_kv_release.argtypes = [P, I, P, P, P, I, P]
     lib.paged_kv_release.restype = I
-    lib.attn_prefill_gqa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    OP = ctypes.POINTER(LaunchOpts)
+    lib.attn_launch_opts_default.argtypes = [OP]
+    lib.attn_launch_opts_default.restype = None
+    lib.attn_prefill_gqa_fwd.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, OP, P]
     lib.attn_prefill_gqa_fwd.restype = I
-    lib.paged_attn_gqa_fwd.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, F, I, I64, I, I, I, I, P, SZ, P]
+    lib.paged_attn_gqa_fwd.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, F, I, I64, I, I, I, I, P, SZ, OP, P]
     lib.paged_attn_gqa_fwd.restype = I
-    lib.paged_attn_gqa_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.paged_attn_gqa_workspace_bytes.argtypes = [I, I, I, I, I, I, I, OP]
     lib.paged_attn_gqa_workspace_bytes.restype = SZ
-    lib.attn_prefill_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, SZ, P]
+    lib.attn_prefill_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, I, P, SZ, OP, P]
     lib.attn_prefill_bwd.restype = I
     lib.attn_prefill_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_prefill_bwd_workspace_bytes.restype = SZ
     lib.paged_attn_check.argtypes = [P, P, P, I, I, I, I, I, I, P, P]
     lib.paged_attn_check.restype = I
-    lib.attn_probe_mfma.argtypes = [P, I, P, I, I, I, P]
-    lib.attn_probe_mfma.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -155,22 +180,27 @@ def paged_kv_append(k_new, v_new, ctx_lens, new_lens, k_pool, v_pool, block_tabl
                                      stream)
 
 
-def attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, stream):
+def attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H_kv, N, d, scale, causal, dtype, opts, stream):
     return library().attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H_kv, N, d, float(scale), int(causal), int(dtype),
-                                          stream)
+                                          opts, stream)
 
 
 def paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, H_kv, d,
                        scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len, dtype,
-                       workspace, workspace_bytes, stream):
+                       workspace, workspace_bytes, opts, stream):
     return library().paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse,
                                         num_seqs, H, H_kv, d, float(scale), max_blocks_per_seq, kv_block_stride,
                                         num_blocks, max_q_len, max_ctx_len, int(dtype), workspace, workspace_bytes,
-                                        stream)
+                                        opts, stream)
 
 
-def paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len) -> int:
-    return int(library().paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len))
+def paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len, opts=None) -> int:
+    return int(library().paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len,
+                                                        opts))
+
+
+def attn_launch_opts_default(opts):
+    library().attn_launch_opts_default(opts)
 
 
 def paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, stream):
@@ -178,9 +208,9 @@ def paged_kv_release(blocks, n, free_blocks, free_count, status, num_blocks, str
 
 
 def attn_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, scale, causal, dtype, workspace,
-                     workspace_bytes, stream):
+                     workspace_bytes, opts, stream):
     return library().attn_prefill_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, N, d, float(scale),
-                                      int(causal), int(dtype), workspace, workspace_bytes, stream)
+                                      int(causal), int(dtype), workspace, workspace_bytes, opts, stream)
 
 
 def attn_prefill_bwd_workspace_bytes(B, H, N) -> int:
@@ -193,10 +223,6 @@ def paged_attn_check(block_table, ctx_lens, q_lens, num_seqs, block_size, max_bl
                      max_ctx_len, status, stream):
     return library().paged_attn_check(block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq,
                                       num_blocks, max_q_len, max_ctx_len, status, stream)
-
-
-def attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream):
-    return library().attn_probe_mfma(fragments, n_fragments, out, blocks, iters, placement, stream)
 
 
 def _dtype_code(t):
@@ -219,9 +245,10 @@ def _ptr(t):
 
 
 def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None, want_lse=True,
-            stream=None):
+            stream=None, options=None):
     """O (and LSE) for q [B, H, N, d] and k, v [B, H_kv, N, d] on the GPU (H_kv < H:
-    grouped-query attention, query head h reads K/V head h // (H // H_kv))."""
+    grouped-query attention, query head h reads K/V head h // (H // H_kv)).
+    options: launch variants (a dict of attn_launch_opts_t fields) or None."""
     import torch
     B, H, N, d = q.shape
     H_kv = k.shape[1]
@@ -236,19 +263,19 @@ def prefill(q, k, v, causal: bool, scale: float | None = None, out=None, lse=Non
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if H_kv == H:
+    if H_kv == H and options is None:
         rc = attn_prefill_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
                               1 if causal else 0, _dtype_code(q), _stream(stream))
     else:
         rc = attn_prefill_gqa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, H_kv, N, d, scale,
-                                  1 if causal else 0, _dtype_code(q), _stream(stream))
+                                  1 if causal else 0, _dtype_code(q), _opts(options), _stream(stream))
     if rc != 0:
         raise AttnError(rc, "attn_prefill_fwd")
     return out, lse
 
 
 def prefill_bwd(q, k, v, o, lse, dout, causal: bool, scale: float | None = None, dq=None, dk=None, dv=None,
-                workspace=None, stream=None):
+                workspace=None, stream=None, options=None):
     """Gradients (dq, dk, dv) of ``prefill`` for the output gradient dout, from
     the forward's q, k, v, o and lse (q, o, dout [B, H, N, d]; k, v [B, H_kv,
     N, d]; lse [B, H, N] fp32); bf16 only."""
@@ -274,7 +301,7 @@ def prefill_bwd(q, k, v, o, lse, dout, causal: bool, scale: float | None = None,
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     rc = attn_prefill_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
                           B, H, H_kv, N, d, scale, 1 if causal else 0, _dtype_code(q), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream(stream))
+                          workspace.numel() * workspace.element_size(), _opts(options), _stream(stream))
     if rc != 0:
         raise AttnError(rc, "attn_prefill_bwd")
     return dq, dk, dv
@@ -282,7 +309,7 @@ def prefill_bwd(q, k, v, o, lse, dout, causal: bool, scale: float | None = None,
 
 def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, scale: float | None = None,
                     max_q_len: int | None = None, max_ctx_len: int | None = None, out=None, lse=None,
-                    want_lse=True, workspace=None, stream=None):
+                    want_lse=True, workspace=None, stream=None, options=None):
     """Paged attention over the pool [num_blocks, 2, H_kv, block_size, d] (K at 0, V at 1).
 
     q: packed [sum(q_lens), H, d] bf16 with H a multiple of H_kv (grouped-query
@@ -305,7 +332,8 @@ def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, sca
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
-    ws_bytes = paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len)
+    op = _opts(options)
+    ws_bytes = paged_attn_gqa_workspace_bytes(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len, op)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     kv_stride = 2 * H_kv * block_size * d
@@ -313,7 +341,7 @@ def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, sca
     v_ptr = k_ptr + H_kv * block_size * d * pool.element_size()
     sc = d ** -0.5 if scale is None else scale
     wsb = workspace.numel() if workspace is not None else 0
-    if H_kv == H:
+    if H_kv == H and options is None:
         rc = paged_attn_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
                             _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, d, sc,
                             maxb, kv_stride, num_blocks, max_q_len, max_ctx_len, _dtype_code(q), _ptr(workspace),
@@ -322,7 +350,7 @@ def paged_attention(q, pool, block_table, ctx_lens, q_lens, block_size: int, sca
         rc = paged_attn_gqa_fwd(_ptr(q), ctypes.c_void_p(k_ptr), ctypes.c_void_p(v_ptr), _ptr(block_table),
                                 _ptr(ctx_lens), _ptr(q_lens), block_size, _ptr(out), _ptr(lse), num_seqs, H, H_kv,
                                 d, sc, maxb, kv_stride, num_blocks, max_q_len, max_ctx_len, _dtype_code(q),
-                                _ptr(workspace), wsb, _stream(stream))
+                                _ptr(workspace), wsb, op, _stream(stream))
     if rc != 0:
         raise AttnError(rc, "paged_attn_fwd")
     return out, lse
@@ -418,24 +446,3 @@ def kv_release(blocks, free_blocks, free_count, num_blocks: int, status=None, ch
         if code != APPEND_OK:
             raise _status_error(code, "paged_kv_release")
     return status
-
-
-PROBE_PLACEMENTS = 16
-
-
-def probe_mfma(fragments, iters: int, blocks: int = 2048, placement: int = 0, out=None, stream=None):
-    """Launch the matrix-core rate probe (attn_probe_mfma) on `fragments`, a
-    contiguous bf16 device tensor of n x 8 elements (n a power of two >= 16),
-    with its loop at `placement` (0 .. PROBE_PLACEMENTS - 1).  Returns (out,
-    flops): the per-lane output tensor and the FLOPs the launch performs
-    (blocks * 4 waves * iters * 32768)."""
-    import torch
-    if fragments.dtype != torch.bfloat16 or not fragments.is_contiguous() or fragments.numel() % 8:
-        raise ValueError("fragments must be a contiguous bf16 tensor of n x 8 elements")
-    if out is None:
-        out = torch.empty(blocks * 256, dtype=torch.float32, device=fragments.device)
-    rc = attn_probe_mfma(_ptr(fragments), fragments.numel() // 8, _ptr(out), blocks, iters, placement,
-                         _stream(stream))
-    if rc != 0:
-        raise AttnError(rc, "attn_probe_mfma")
-    return out, blocks * 4 * iters * 32768

@@ -73,7 +73,9 @@ __global__ __launch_bounds__(kAllocThreads) void kv_alloc_kernel(AppendArgs a)
     int need_sum = 0, over = 0, bad = 0;
     for (int r = tid; r < a.num_seqs; r += kAllocThreads) {
         const int c = a.ctx_lens[r], n = a.new_lens[r];
-        if (c < 0 || n < 0 || c > INT32_MAX - n) {
+        // n above the host bound max_new_len would allocate blocks for tokens
+        // the write launch (sized by that bound) never copies
+        if (c < 0 || n < 0 || n > a.max_new_len || c > INT32_MAX - n) {
             bad = 1;
             continue;
         }

@@ -10,7 +10,6 @@
 #include "append_internal.h"
 #include "bwd_internal.h"
 #include "attn_internal.h"
-#include "probe_internal.h"
 #include "check_internal.h"
 
 namespace {
@@ -48,6 +47,26 @@ int check_scale(float scale)
     return ATTN_OK;
 }
 
+// Launch variants with every field in range (defaults where opts is NULL).
+int read_opts(const attn_launch_opts_t* in, attn_launch_opts_t* out)
+{
+    attn_launch_opts_default(out);
+    if (!in) return ATTN_OK;
+    *out = *in;
+    const attn_launch_opts_t& o = *out;
+    const bool ok = (o.prefill_kernel >= -1 && o.prefill_kernel <= 1) &&
+                    (o.prefill_pair >= -1 && o.prefill_pair <= 1) &&
+                    (o.prefill_order == -1 || o.prefill_order == 0 || o.prefill_order == 1 ||
+                     o.prefill_order == 3) &&
+                    (o.paged_path >= -1 && o.paged_path <= 1) &&
+                    (o.paged_split_tokens >= 0 && o.paged_split_tokens <= (1 << 24)) &&
+                    (o.paged_decode_heads == 0 || o.paged_decode_heads == 1 || o.paged_decode_heads == 2 ||
+                     o.paged_decode_heads == 4 || o.paged_decode_heads == 8) &&
+                    (o.paged_tile_map >= -1 && o.paged_tile_map <= 2) &&
+                    (o.bwd_pair_q >= -1 && o.bwd_pair_q <= 1) && (o.bwd_pair_kv >= -1 && o.bwd_pair_kv <= 1);
+    return ok ? ATTN_OK : ATTN_ERR_OPTION;
+}
+
 }  // namespace
 
 extern "C" {
@@ -68,15 +87,30 @@ const char* attn_strerror(int status)
         case ATTN_ERR_DEVICE: return "current device is not a gfx950 GPU";
         case ATTN_ERR_BAD_TABLE:
             return "a length or block-table entry breaks the paged-attention contract (ATTN_DEBUG check)";
+        case ATTN_ERR_OPTION: return "a launch option is out of range";
         default: return "unknown attn status";
     }
 }
 
-const char* attn_version(void) { return "attn_gfx950 1.0"; }
+const char* attn_version(void) { return "attn_gfx950 1.1"; }
+
+void attn_launch_opts_default(attn_launch_opts_t* opts)
+{
+    if (!opts) return;
+    opts->prefill_kernel = -1;
+    opts->prefill_pair = -1;
+    opts->prefill_order = -1;
+    opts->paged_path = -1;
+    opts->paged_split_tokens = 0;
+    opts->paged_decode_heads = 0;
+    opts->paged_tile_map = -1;
+    opts->bwd_pair_q = -1;
+    opts->bwd_pair_kv = -1;
+}
 
 int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int H, int H_kv, int N, int d, float scale, int causal,
-                         attn_dtype_t dtype, void* stream)
+                         attn_dtype_t dtype, const attn_launch_opts_t* opts, void* stream)
 {
     if (!q || !k || !v || !o) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
@@ -85,6 +119,9 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ((uintptr_t)lse & 3u))
         return ATTN_ERR_ALIGN;
     int rc = check_scale(scale);
+    if (rc) return rc;
+    attn_launch_opts_t op;
+    rc = read_opts(opts, &op);
     if (rc) return rc;
     if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_SHAPE;
     if ((int64_t)N * d * (dtype == ATTN_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;  // 32-bit row offsets
@@ -96,31 +133,11 @@ int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, f
     a.scale = scale;
     a.causal = causal ? 1 : 0;
     a.dtype = (dtype == ATTN_BF16) ? 0 : 1;
-    // bf16 query tiles: 128 rows (32 queries per wave, three workgroups per CU).
-    // Pairing tiles t and n-1-t (equal work per workgroup) is chosen by the
-    // launcher for causal grids (-1); ATTN_PREFILL_PAIR=0 / 1 forces it.
-    {
-        int pair = -1;
-        const char* env = getenv("ATTN_PREFILL_PAIR");
-        if (env && *env) pair = atoi(env) ? 1 : 0;
-        if (!a.causal || N <= 128) pair = 0;
-        a.pair = pair;
-        // tile order of causal grids (chosen by size in launch_prefill); for
-        // comparison ATTN_PREFILL_ORDER=0 / 1 / 3 forces per-head ranges /
-        // complementary / tile-major
-        a.order = -1;
-        // the 64-rows-per-wave kernel (bf16, d = 128) runs only when asked
-        // for with ATTN_PREFILL_WIDE=1 (measured slower than the 32-row
-        // kernel on the long causal prefill; kept for comparison)
-        a.wide = -1;
-        const char* wenv = getenv("ATTN_PREFILL_WIDE");
-        if (wenv && *wenv) a.wide = atoi(wenv) ? 1 : 0;
-        const char* oenv = getenv("ATTN_PREFILL_ORDER");
-        if (oenv && *oenv) {
-            const int ov = atoi(oenv);
-            a.order = (ov == 0 || ov == 1 || ov == 3) ? ov : -1;
-        }
-    }
+    // bf16: the launcher picks the key loop, the tile order and pairing for
+    // the grid (-1); the options force them
+    a.kernel = op.prefill_kernel;
+    a.pair = (!a.causal || N <= 128) ? 0 : op.prefill_pair;
+    a.order = op.prefill_order;
     rc = attn::launch_prefill(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
@@ -129,7 +146,7 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int N, int d, float scale, int causal,
                      attn_dtype_t dtype, void* stream)
 {
-    return attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, stream);
+    return attn_prefill_gqa_fwd(q, k, v, o, lse, B, H, H, N, d, scale, causal, dtype, nullptr, stream);
 }
 
 size_t attn_prefill_bwd_workspace_bytes(int B, int H, int N)
@@ -141,7 +158,8 @@ size_t attn_prefill_bwd_workspace_bytes(int B, int H, int N)
 int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                      const void* dout, void* dq, void* dk, void* dv,
                      int B, int H, int H_kv, int N, int d, float scale, int causal,
-                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+                     attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                     const attn_launch_opts_t* opts, void* stream)
 {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || N < 1 || H_kv < 1 || H % H_kv != 0) return ATTN_ERR_SHAPE;
@@ -151,6 +169,9 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
         !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u))
         return ATTN_ERR_ALIGN;
     int rc = check_scale(scale);
+    if (rc) return rc;
+    attn_launch_opts_t op;
+    rc = read_opts(opts, &op);
     if (rc) return rc;
     if ((int64_t)B * H > INT32_MAX / 2) return ATTN_ERR_SHAPE;
     if ((int64_t)N * d * 2 >= ((int64_t)1 << 32)) return ATTN_ERR_SHAPE;   // 32-bit row offsets
@@ -166,22 +187,26 @@ int attn_prefill_bwd(const void* q, const void* k, const void* v, const void* o,
     a.B = B; a.H = H; a.H_kv = H_kv; a.N = N; a.d = d;
     a.scale = scale;
     a.causal = causal ? 1 : 0;
+    a.pair_q = op.bwd_pair_q;
+    a.pair_kv = op.bwd_pair_kv;
     rc = attn::launch_bwd(a, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
 
 size_t paged_attn_gqa_workspace_bytes(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len,
-                                      int max_ctx_len)
+                                      int max_ctx_len, const attn_launch_opts_t* opts)
 {
     if (num_seqs < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || H / H_kv > 128 || (d != 64 && d != 128) ||
-        (block_size != 16 && block_size != 32) || max_q_len < 1 || max_ctx_len < 1)
+        (block_size != 16 && block_size != 32) || max_q_len < 1 || max_ctx_len < 1 || max_q_len > max_ctx_len)
         return 0;
-    return attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len).ws_bytes;
+    attn_launch_opts_t op;
+    if (read_opts(opts, &op) != ATTN_OK) return 0;
+    return attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len, op).ws_bytes;
 }
 
 size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size, int max_q_len, int max_ctx_len)
 {
-    return paged_attn_gqa_workspace_bytes(num_seqs, H, H, d, block_size, max_q_len, max_ctx_len);
+    return paged_attn_gqa_workspace_bytes(num_seqs, H, H, d, block_size, max_q_len, max_ctx_len, nullptr);
 }
 
 int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
@@ -189,7 +214,8 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
                        int block_size, void* o, float* lse,
                        int num_seqs, int H, int H_kv, int d, float scale, int max_blocks_per_seq,
                        int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
-                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes, void* stream)
+                       attn_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                       const attn_launch_opts_t* opts, void* stream)
 {
     if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !q_lens || !o) return ATTN_ERR_NULL;
     if (num_seqs < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || max_q_len < 1 ||
@@ -205,7 +231,13 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
         return ATTN_ERR_ALIGN;
     int rc = check_scale(scale);
     if (rc) return rc;
-    const attn::PagedPlan plan = attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len);
+    attn_launch_opts_t op;
+    rc = read_opts(opts, &op);
+    if (rc) return rc;
+    if (op.paged_decode_heads > 0 &&
+        ((H / H_kv) % op.paged_decode_heads != 0 || (block_size == 32 && op.paged_decode_heads == 8)))
+        return ATTN_ERR_OPTION;
+    const attn::PagedPlan plan = attn::plan_paged(num_seqs, H, H_kv, d, block_size, max_q_len, max_ctx_len, op);
     // grid sizes must fit 32 bits
     const int64_t rows = (int64_t)num_seqs * max_q_len;
     if (rows * H * plan.max_splits > (int64_t)INT32_MAX - 8) return ATTN_ERR_SHAPE;
@@ -235,6 +267,7 @@ int paged_attn_gqa_fwd(const void* q, const void* k_pool, const void* v_pool,
     a.max_splits = plan.max_splits;
     a.ws_o = plan.ws_bytes ? (float*)workspace : nullptr;
     a.ws_lse = plan.ws_bytes ? (float*)((char*)workspace + plan.ws_o_bytes) : nullptr;
+    a.tile_map = op.paged_tile_map;
     rc = attn::launch_paged(a, plan, (hipStream_t)stream);
     return rc == 0 ? ATTN_OK : (rc == -2 ? ATTN_ERR_SHAPE : ATTN_ERR_LAUNCH);
 }
@@ -248,7 +281,7 @@ int paged_attn_fwd(const void* q, const void* k_pool, const void* v_pool,
 {
     return paged_attn_gqa_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, H,
                               d, scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len,
-                              dtype, workspace, workspace_bytes, stream);
+                              dtype, workspace, workspace_bytes, nullptr, stream);
 }
 
 int paged_kv_gather(const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -340,22 +373,6 @@ int paged_attn_check(const int32_t* block_table, const int32_t* ctx_lens, const 
     attn::CheckArgs c{block_table, ctx_lens, q_lens, num_seqs, block_size, max_blocks_per_seq, num_blocks,
                       max_q_len, max_ctx_len, status};
     return attn::launch_paged_check(c, (hipStream_t)stream) == 0 ? ATTN_OK : ATTN_ERR_LAUNCH;
-}
-
-int attn_probe_mfma(const void* fragments, int n_fragments, float* out, int blocks, int iters, int placement,
-                    void* stream)
-{
-    if (!fragments || !out) return ATTN_ERR_NULL;
-    if (!aligned16(fragments) || !aligned16(out)) return ATTN_ERR_ALIGN;
-    if (n_fragments < 16 || (n_fragments & (n_fragments - 1)) != 0) return ATTN_ERR_SHAPE;
-    if (blocks < 1 || blocks > (1 << 16) || iters < 32 || (iters % 32) != 0 || iters > (1 << 24))
-        return ATTN_ERR_SHAPE;
-    if (placement < 0 || placement >= attn::kProbePlacements) return ATTN_ERR_SHAPE;
-    int rc = check_device();
-    if (rc) return rc;
-    return attn::launch_mfma_probe(fragments, n_fragments, out, blocks, iters, placement, (hipStream_t)stream) == 0
-               ? ATTN_OK
-               : ATTN_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn {
 
 struct PrefillArgs {
@@ -24,8 +26,7 @@ struct PrefillArgs {
     int order;      // bf16 causal: -1 automatic, 0 heaviest tile first per head in
                     // XCD-contiguous ranges, 1 complementary order within each XCD's share,
                     // 3 tile-major over the whole grid
-    int wide;       // bf16, d = 128: 1 takes the 64-rows-per-wave kernel (256-row query tiles,
-                    // one workgroup per CU); otherwise the 32-row kernel
+    int kernel;     // bf16 key loop: -1 launcher decides, 0 plain, 1 software-pipelined
     int n_work;     // filled by the launcher
 };
 
@@ -63,6 +64,7 @@ struct PagedArgs {
     int split_tokens, max_splits;
     float* ws_o;     // [num_seqs*max_q_len][H][max_splits][d]
     float* ws_lse;   // [num_seqs*max_q_len][H][max_splits]
+    int tile_map;    // tile kernel work mapping: -1 launcher decides, 0 ranges, 1 pairs, 2 items
 };
 
 struct GatherArgs {
@@ -82,7 +84,10 @@ constexpr int kDecodeMaxQ = 4;     // q_len up to this uses the vector decode ke
 constexpr int kDecodeMfmaGroup = 4; // ... unless this many query heads share a K/V head
 constexpr int kChunkMaxSplit = 8192;  // most keys per split on the MFMA tile path (multiple of 64)
 
-PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len);
+// opts: paged_path, paged_split_tokens and paged_decode_heads override the
+// plan's choices (validated by the caller).
+PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len,
+                     const attn_launch_opts_t& opts);
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream);
 int launch_paged(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream);

@@ -29,7 +29,7 @@
 //    32-lane pass) conflict-free.
 //  * Softmax runs in base 2: scores are scaled by scale*log2(e) inside one FMA
 //    and exponentiated with the hardware exp2.  P is rounded to bf16 (round to
-//    nearest even) for the MFMA and the running sum adds those rounded values.
+//    nearest even) for the MFMA; the running sum adds the fp32 values.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -180,7 +180,7 @@ struct WaveState {
     f32x16 o[TileCfg<D>::DBLK];
     float m;   // offset of this lane's query, raw score units (-inf: none yet)
     float ms;  // the same offset in the exponent's base-2 units, m * c2 (0 while m = -inf)
-    float l;   // running sum of this lane-half's rounded probabilities
+    float l;   // running sum of this lane-half's probabilities (fp32)
 };
 
 // Scores of one key tile: S^T blocks of 32 keys (accumulator register i of
@@ -296,28 +296,29 @@ __device__ __forceinline__ void update_offset(WaveState<D>& ws, float mt, float 
     }
 }
 
-// p = exp2(s*c2 - m*c2) rounded to bf16 (packed in pairs, the P^T operand
-// layout); l += the sum of the rounded p, added pair by pair onto l in key
-// order.  (c2 > 0 always: a zero scale is passed as a tiny positive c2, which
-// gives the same p = 1 for every allowed key and keeps exp2(-inf) = 0 for
-// masked ones.)
+// p = exp2(s*c2 - m*c2), rounded to bf16 (packed in pairs, the P^T operand
+// layout) for the P V product; l += the fp32 values of p, added one by one in
+// key order.  (The bf16 dot-product instruction that would add the rounded
+// pairs in one step occupies the matrix pipe -- it never issues beside an
+// MFMA -- while plain fp32 adds do.)  (c2 > 0 always: a zero scale is passed
+// as a tiny positive c2, which gives the same p = 1 for every allowed key and
+// keeps exp2(-inf) = 0 for masked ones.)
 template <int D>
 __device__ __forceinline__ void exp_tile(bf16x2 (&pk)[TileCfg<D>::KBLK][8], const TileScores<D>& S, WaveState<D>& ws,
                                          float c2)
 {
     using C = TileCfg<D>;
-    const bf16x2 ones = pack2(1.f, 1.f);
     const float ms = ws.ms;
     float l = ws.l;
 #pragma unroll
     for (int kb = 0; kb < C::KBLK; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-            const float t0 = __builtin_fmaf(S.s[kb][i], c2, -ms);
-            const float t1 = __builtin_fmaf(S.s[kb][i + 1], c2, -ms);
-            const bf16x2 w = pack2(__builtin_amdgcn_exp2f(t0), __builtin_amdgcn_exp2f(t1));
-            pk[kb][i >> 1] = w;
-            l = __builtin_amdgcn_fdot2_f32_bf16(w, ones, l, false);
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[kb][i], c2, -ms));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S.s[kb][i + 1], c2, -ms));
+            pk[kb][i >> 1] = pack2(e0, e1);
+            l += e0;
+            l += e1;
         }
     ws.l = l;
 }

@@ -1,7 +1,8 @@
 // attn_mfma_kernel.h -- the per-workgroup driver of the bf16 MFMA attention
 // forward: loads the query tile into registers, streams 32-key K/V tiles into
 // LDS with direct global->LDS copies issued one tile ahead (two LDS buffers,
-// one barrier per tile), runs the online-softmax tile step of
+// one barrier per tile; each tile's copies go out after the S MFMAs of the
+// tile before), runs the online-softmax tile step of
 // attn_mfma_core.h, and writes O (bf16, or fp32 partials) and the
 // log-sum-exp.  The source of K/V rows is a policy object, so the same driver
 // serves contiguous K/V ([B,H,N,d]) and the paged pool.
@@ -132,13 +133,16 @@ __device__ __forceinline__ void publish_copies()
 }
 
 // One key tile (K at buf, V at buf + TILE_BYTES) for this wave's 32 queries.
-template <int D, bool MASKED>
+// `copies` issues this wave's share of the next tile's copies; it runs after
+// the S MFMAs, whose K reads it would otherwise queue behind.
+template <int D, bool MASKED, class CP>
 __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
-                                          const char* buf, int key0)
+                                          const char* buf, int key0, const CP& copies)
 {
     using C = TileCfg<D>;
     TileScores<D> S;
     qk_tile(S, qf, buf, cx.lane);
+    copies();
     const float mt = tile_max<D, MASKED>(S, cx.lane, key0, cx.q_lim);
     update_offset(ws, mt, cx.c2, cx.thr);
     bf16x2 pk[C::KBLK][8];
@@ -163,22 +167,32 @@ __device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[Ti
     int j = 0;
     for (; j + 2 <= n_full; j += 2) {
         const int kb0 = cx.kv_begin + j * C::BN;
-        issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
-        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b0, kb0);
+        const auto c1 = [&]() { issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN); };
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b0, kb0, c1);
+        else c1();
         publish_copies();
-        if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
-        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN);
+        const auto c2 = [&]() {
+            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+        };
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN, c2);
+        else c2();
         publish_copies();
     }
     // j is even here, so tile j is in buffer 0
     for (; j < cx.ntile; j += 2) {
         const int kb0 = cx.kv_begin + j * C::BN;
-        if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
-        if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b0, kb0);
+        const auto c1 = [&]() {
+            if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        };
+        if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b0, kb0, c1);
+        else c1();
         publish_copies();
         if (j + 1 < cx.ntile) {
-            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
-            if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN);
+            const auto c2 = [&]() {
+                if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+            };
+            if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN, c2);
+            else c2();
             publish_copies();
         }
     }

@@ -696,16 +696,12 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
 {
     constexpr int BLK = 128;
     const int64_t nblk = (a.N + BLK - 1) / BLK;
-    // causal launches pair the dQ kernel's query tiles (t, nqt-1-t);
-    // ATTN_BWD_PAIR=0 / 1 forces one tile / pairs per workgroup
-    bool pair = a.causal && nblk > 1;
-    const char* env = getenv("ATTN_BWD_PAIR");
-    if (env && *env) pair = atoi(env) != 0 && nblk > 1;
+    // causal launches pair the dQ kernel's query tiles (t, nqt-1-t) and the
+    // dK/dV kernel's key blocks (kb, nkb-1-kb); a.pair_q / a.pair_kv force it
+    const bool pair = (a.pair_q < 0 ? a.causal != 0 : a.pair_q != 0) && nblk > 1;
     const int64_t n_dq = (int64_t)a.B * a.H * (pair ? (nblk + 1) / 2 : nblk);
     const int64_t nkb = (a.N + 32 * kRoleKB - 1) / (32 * kRoleKB);
-    bool pair_kv = a.causal && nkb > 1;
-    const char* env_kv = getenv("ATTN_BWD_PAIR_KV");
-    if (env_kv && *env_kv) pair_kv = atoi(env_kv) != 0 && nkb > 1;
+    const bool pair_kv = (a.pair_kv < 0 ? a.causal != 0 : a.pair_kv != 0) && nkb > 1;
     const int64_t n_kv = (int64_t)a.B * a.H_kv * (pair_kv ? (nkb + 1) / 2 : nkb);
     if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
     const int grid_dq = (int)((n_dq + 7) / 8 * 8);

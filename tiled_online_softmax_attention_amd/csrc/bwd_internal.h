@@ -23,6 +23,8 @@ struct BwdArgs {
     int B, H, H_kv, N, d;
     float scale;
     int causal;
+    int pair_q;          // dQ workgroups take query tiles t and n-1-t: -1 when causal, 0 no, 1 yes
+    int pair_kv;         // dK/dV workgroups take key blocks kb and nkb-1-kb: -1 when causal, 0 no, 1 yes
 };
 
 inline size_t bwd_workspace_bytes(int B, int H, int N)

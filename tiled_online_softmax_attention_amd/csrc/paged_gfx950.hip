@@ -26,6 +26,17 @@
 
 namespace attn {
 
+// Context length of request r as every paged kernel reads it: clamped to the
+// host bound max_ctx_len, so that a length above the bound (a broken contract,
+// which ATTN_DEBUG=1 reports) cannot make a kernel read block-table entries
+// past max_blocks_per_seq or the combine read split slots past max_splits.
+template <class A>
+__device__ __forceinline__ int req_ctx(const A& a, int r)
+{
+    return min(a.ctx_lens[r], a.max_ctx_len);
+}
+
+
 // ---- small wave helpers ------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x)
@@ -118,7 +129,7 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
     bid /= a.H_kv;
     const int i = bid % a.max_q_len;
     const int r = bid / a.max_q_len;
-    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    const int ctx = req_ctx(a, r), ql = a.q_lens[r];
     if (i >= ql) return;
     const int S = a.split_tokens;
     const int nsplit = (ctx + S - 1) / S;
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     }
     const int hk = pair % a.H_kv;
     const int r = pair / a.H_kv;
-    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    const int ctx = req_ctx(a, r), ql = a.q_lens[r];
     if (qt * ppt >= ql) return;
     const int S = a.split_tokens;
     const int nsplit = (ctx + S - 1) / S;
@@ -452,7 +463,7 @@ __global__ __launch_bounds__(256) void paged_combine_heads_kernel(PagedArgs a)
     const int hg = (int)(wid % hgroups);
     const int i = (int)((wid / hgroups) % a.max_q_len);
     const int r = (int)(wid / ((int64_t)hgroups * a.max_q_len));
-    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    const int ctx = req_ctx(a, r), ql = a.q_lens[r];
     if (i >= ql) return;                                   // uniform over the wave
     const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
     if (nsplit <= 1) return;
@@ -523,7 +534,7 @@ __global__ __launch_bounds__(256) void paged_combine_kernel(PagedArgs a)
     const int h = (int)(item % a.H);
     const int i = (int)((item / a.H) % a.max_q_len);
     const int r = (int)(item / ((int64_t)a.H * a.max_q_len));
-    const int ctx = a.ctx_lens[r], ql = a.q_lens[r];
+    const int ctx = req_ctx(a, r), ql = a.q_lens[r];
     if (i >= ql) return;
     const int nsplit = (ctx + a.split_tokens - 1) / a.split_tokens;
     if (nsplit <= 1) return;
@@ -611,14 +622,8 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(GatherArgs a)
 // decode 5.75 -> 5.69 TB/s).
 constexpr int kCombineHeadsMaxSplits = 8;
 
-static int env_int(const char* name, int dflt)
-{
-    const char* s = getenv(name);
-    if (!s || !*s) return dflt;
-    return atoi(s);
-}
-
-PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len)
+PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len,
+                     const attn_launch_opts_t& opts)
 {
     PagedPlan p{};
     const int G = H / H_kv;
@@ -626,8 +631,7 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     // grouped heads; from groups of kDecodeMfmaGroup heads up, the group's
     // rows make the MFMA tile kernel the better fit even for one query row.
     p.path = (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup) ? 0 : 1;
-    const int env_path = env_int("ATTN_DECODE_PATH", -1);
-    if ((env_path == 0 && max_q_len <= kDecodeMaxQ) || env_path == 1) p.path = env_path;
+    if ((opts.paged_path == 0 && max_q_len <= kDecodeMaxQ) || opts.paged_path == 1) p.path = opts.paged_path;
     const int64_t rows = (int64_t)num_seqs * max_q_len;
     // decode workgroups serve gc query heads of one K/V group (the largest of
     // 8, 4, 2, 1 that divides the group; at most 4 with 32-token pages, whose
@@ -638,9 +642,9 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
             p.gc = c;
             break;
         }
-    const int env_gc = env_int("ATTN_DECODE_GC", 0);
-    if (env_gc == 1 || env_gc == 2 || env_gc == 4 || env_gc == 8)
-        if (G % env_gc == 0 && !(block_size == 32 && env_gc == 8)) p.gc = env_gc;
+    const int hc = opts.paged_decode_heads;
+    if (hc == 1 || hc == 2 || hc == 4 || hc == 8)
+        if (G % hc == 0 && !(block_size == 32 && hc == 8)) p.gc = hc;
     p.n_chunks = G / p.gc;
     int S;
     if (p.path == 0) {
@@ -674,8 +678,7 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         s = (s + 63) / 64 * 64;
         S = (int)(s < 1024 ? 1024 : (s > 8192 ? 8192 : s));
     }
-    const int env = env_int("ATTN_SPLIT_TOKENS", 0);
-    if (env > 0) S = env;
+    if (opts.paged_split_tokens > 0) S = opts.paged_split_tokens;
     // a tile-path workgroup stages its split's block-table entries in LDS
     if (p.path == 1 && S > kChunkMaxSplit) S = kChunkMaxSplit;
     // whole pages; on the MFMA path a multiple of 64 keys (whole pages of 16
@@ -700,6 +703,7 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
 {
     if (plan.path == 0) {
         const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H_kv * plan.n_chunks * a.max_splits;
+        if (grid > (int64_t)INT32_MAX) return -2;
         const dim3 g((unsigned)grid), b(256);
         if (plan.gc == 8) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 8>), g, b, 0, stream, a);
         else if (plan.gc == 4) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 4>), g, b, 0, stream, a);
@@ -710,8 +714,7 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         const int64_t per_pair = (int64_t)plan.nqt * a.max_splits;
         const int64_t n_work = pairs * per_pair;
         int map = (pairs >= 8 * kChunkPairsPerXcd) ? kMapPairs : kMapItems;
-        const int env_map = env_int("ATTN_CHUNK_MAP", -1);
-        if (env_map >= kMapRanges && env_map <= kMapItems) map = env_map;
+        if (a.tile_map >= kMapRanges && a.tile_map <= kMapItems) map = a.tile_map;
         const int64_t grid = (map == kMapPairs) ? (pairs + 7) / 8 * 8 * per_pair
                            : (map == kMapRanges) ? (n_work + 7) / 8 * 8 : n_work;
         if (grid > (int64_t)INT32_MAX) return -2;

@@ -1,12 +1,17 @@
 // prefill_gfx950.hip -- dense / causal prefill attention for gfx950.
 //
-//  * bf16: fused MFMA kernel (attn_mfma_kernel.h), one workgroup of 4 waves per
-//    128-row query tile (or per pair of tiles, see below), K/V streamed through
-//    LDS in 32-key tiles, causal key tiles above the diagonal never loaded.
-//  * bf16, d = 128, on request (PrefillArgs::wide): the 64-rows-per-wave
-//    variant of attn_mfma_wide.h, 256-row query tiles, one workgroup per CU.
-//  * fp32: a vector-ALU kernel with the same online softmax (fp32 storage has
-//    no dense matrix path worth using at these sizes).
+//  * bf16: fused MFMA kernel, one workgroup of 4 waves per 128-row query tile
+//    (or per pair of tiles, see below), K/V streamed through LDS in 32-key
+//    tiles, causal key tiles above the diagonal never loaded.  Two key loops:
+//    the plain one of attn_mfma_kernel.h (two LDS buffers, three workgroups
+//    per CU) for grids of several dispatch rounds, and the software-pipelined
+//    one of attn_mfma_pipe.h (four LDS buffers, two workgroups per CU) for
+//    grids of about one round, whose few waves per SIMD need the MFMA and
+//    softmax work of each wave interleaved (1x32x2048x128 causal: 560 -> 622
+//    TFLOP/s; 16x32x8192x128: 1128 against 1111 for the pipelined loop).
+//    Both give the same bits.
+//  * fp32: a vector-ALU kernel with the same online softmax and 64-key tiles
+//    (fp32 storage has no dense matrix path worth using at these sizes).
 //
 // Work mapping (bf16).  Workgroups are dealt to the 8 XCDs round-robin by
 // block id; a causal launch picks one of three tile orders (launch_prefill):
@@ -34,7 +39,7 @@
 #include <stdint.h>
 
 #include "attn_mfma_kernel.h"
-#include "attn_mfma_wide.h"
+#include "attn_mfma_pipe.h"
 #include "attn_internal.h"
 
 namespace attn {
@@ -61,14 +66,25 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
     return (bid & 7) * per + (bid >> 3);
 }
 
-template <int D, bool PAIR>
-__global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
+// KIND 0: the plain key loop (attn_mfma_kernel.h: two LDS buffers, three
+// workgroups per CU).  KIND 1: the software-pipelined key loop of
+// attn_mfma_pipe.h (four LDS buffers, two workgroups per CU).
+template <int D, bool PAIR, int KIND>
+__global__ __launch_bounds__(256, KIND == 0 ? 3 : 2) void prefill_bf16_kernel(PrefillArgs a)
 {
     using C = TileCfg<D>;
+    constexpr bool PIPE = KIND != 0;
     constexpr int BM = kTileRows;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
     const TileBuffers buf{lds0, lds1};
+    PipeBuffers pbuf{{lds0, lds1, nullptr, nullptr}};
+    if constexpr (PIPE) {
+        __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
+        __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
+        pbuf.b[2] = lds2;
+        pbuf.b[3] = lds3;
+    }
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= a.n_work && (PAIR || a.order != 3)) return;
     const int nqt = (a.N + BM - 1) / BM;
@@ -129,58 +145,19 @@ __global__ __launch_bounds__(256, 3) void prefill_bf16_kernel(PrefillArgs a)
         out.lse_stride = 1;
         out.fp32_out = 0;
         if (it) __syncthreads();   // LDS reuse across the two tiles
-        run_query_tile<D>(P, kv, out, c2, buf);
+        if constexpr (PIPE) run_pipe_tile<D>(P, kv, out, c2, pbuf);
+        else run_query_tile<D>(P, kv, out, c2, buf);
     }
-}
-
-// 64 query rows per wave (attn_mfma_wide.h): one workgroup of 4 waves per
-// 256-row query tile, one workgroup per CU; per-head ranges on each XCD,
-// heaviest tile first within a head.
-template <int D>
-__global__ __launch_bounds__(256, 1) void prefill_bf16_wide_kernel(PrefillArgs a)
-{
-    using C = TileCfg<D>;
-    __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
-    const WideBuffers buf{{lds0, lds1, lds2, lds3}};
-    const int L = xcd_linear_id(blockIdx.x, gridDim.x);
-    if (L >= a.n_work) return;
-    const int nqt = (a.N + kWideRows - 1) / kWideRows;
-    const int bh = L / nqt, qt = nqt - 1 - L % nqt;
-    const int64_t head_off = (int64_t)bh * a.N * D * 2;
-    const int64_t kv_off = ((int64_t)(bh / a.H) * a.H_kv + (bh % a.H) / (a.H / a.H_kv)) * a.N * D * 2;
-    ContigKV<D> kv{(const char*)a.k + kv_off, (const char*)a.v + kv_off, (uint32_t)a.N * (uint32_t)(D * 2)};
-    const int q0 = qt * kWideRows;
-    TileProblem P;
-    P.q = (const char*)a.q + head_off + (int64_t)q0 * D * 2;
-    P.q_stride = D * 2;
-    P.q_hstride = 0;
-    P.rows_per_pos = 1;
-    P.n_rows = min(kWideRows, a.N - q0);
-    P.q_pos0 = q0;
-    P.causal = a.causal;
-    P.kv_begin = 0;
-    P.kv_end = a.N;
-    TileOut out;
-    out.o = (char*)a.o + head_off + (int64_t)q0 * D * 2;
-    out.o_stride = D * 2;
-    out.o_hstride = 0;
-    out.lse_hstride = 0;
-    out.lse = a.lse ? a.lse + (int64_t)bh * a.N + q0 : nullptr;
-    out.lse_stride = 1;
-    out.fp32_out = 0;
-    run_wide_tile<D>(P, kv, out, a.scale * kLog2e, buf);
 }
 
 // ---------------------------------------------------------------------------
 // fp32 kernel: 64 query rows per workgroup, 4 threads per row (each owns d/4
-// channels of q and of the output), 32-key K/V tiles staged in LDS as fp32.
+// channels of q and of the output), 64-key K/V tiles staged in LDS as fp32 (the
+// block size of the fp32 workload).
 template <int D>
 __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a)
 {
-    constexpr int BM = 64, BN = 32, SUB = D / 4;
+    constexpr int BM = 64, BN = 64, SUB = D / 4;
     __shared__ float ks[BN][D + 4];
     __shared__ float vs[BN][D + 4];
     const int nqt = (a.N + BM - 1) / BM;
@@ -262,14 +239,7 @@ constexpr int64_t kTileMajorMaxKV = (int64_t)256 << 20;
 int launch_prefill(const PrefillArgs& in, hipStream_t stream)
 {
     PrefillArgs a = in;
-    if (a.dtype == 0 && a.d == 128 && a.pair != 1 && a.wide == 1) {
-        const int nqt = (a.N + kWideRows - 1) / kWideRows;
-        const int64_t n_work = (int64_t)a.B * a.H * nqt;
-        if (n_work > (int64_t)INT32_MAX - 8) return -2;
-        a.n_work = (int)n_work;
-        const int grid = (int)((n_work + 7) / 8 * 8);
-        hipLaunchKernelGGL((prefill_bf16_wide_kernel<128>), dim3(grid), dim3(TileCfg<128>::kThreads), 0, stream, a);
-    } else if (a.dtype == 0) {
+    if (a.dtype == 0) {
         const int BM = kTileRows;
         const int nqt = (a.N + BM - 1) / BM;
         const int64_t bh = (int64_t)a.B * a.H;
@@ -296,21 +266,30 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         // order (1x32x2048x128 paired: -2.5 %)
         if (a.pair < 0) a.pair = (a.causal && a.order == 0 && nqt > 1) ? 1 : 0;
         if (a.pair) a.order = 0;
+        // the pipelined key loop for the one-round grids of the complementary
+        // order, the plain one otherwise
+        if (a.kernel < 0) a.kernel = (a.order == 1) ? 1 : 0;
         const int per_bh = a.pair ? (nqt + 1) / 2 : nqt;
         const int64_t n_work = bh * per_bh;
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
         const int grid = (int)((n_work + 7) / 8 * 8);
-#define ATTN_LAUNCH_PREFILL(DD, PP) \
-    hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
+#define ATTN_LAUNCH_PREFILL(DD, PP, KK) \
+    hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP, KK>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
+#define ATTN_LAUNCH_PREFILL_K(DD, PP)               \
+    do {                                            \
+        if (a.kernel == 1) ATTN_LAUNCH_PREFILL(DD, PP, 1); \
+        else ATTN_LAUNCH_PREFILL(DD, PP, 0);        \
+    } while (0)
         if (a.d == 128) {
-            if (a.pair) ATTN_LAUNCH_PREFILL(128, true);
-            else ATTN_LAUNCH_PREFILL(128, false);
+            if (a.pair) ATTN_LAUNCH_PREFILL_K(128, true);
+            else ATTN_LAUNCH_PREFILL_K(128, false);
         } else {
-            if (a.pair) ATTN_LAUNCH_PREFILL(64, true);
-            else ATTN_LAUNCH_PREFILL(64, false);
+            if (a.pair) ATTN_LAUNCH_PREFILL_K(64, true);
+            else ATTN_LAUNCH_PREFILL_K(64, false);
         }
 #undef ATTN_LAUNCH_PREFILL
+#undef ATTN_LAUNCH_PREFILL_K
     } else {
         const int nqt = (a.N + 63) / 64;
         const int64_t grid = (int64_t)a.B * a.H * nqt;
