@@ -190,6 +190,32 @@ size_t paged_attn_workspace_bytes(int num_seqs, int H, int d, int block_size,
                                   int max_q_len, int max_ctx_len);
 
 /*
+ * For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: exactly
+ * paged_attn_fwd (same arguments, validation, launches and bits), except
+ * that the split partials go to a workspace the library owns, a static
+ * device array of ATTN_STATIC_WORKSPACE_BYTES on each GPU it runs on (held
+ * until the process ends; its address is looked up on the first call on each
+ * device).  The call allocates and frees nothing.
+ *   - If paged_attn_workspace_bytes(...) for these bounds exceeds
+ *     ATTN_STATIC_WORKSPACE_BYTES the call returns ATTN_ERR_WORKSPACE and
+ *     launches nothing (64 MiB holds, e.g., 64 decode rows x 32 heads x d 128
+ *     with contexts up to ~30 K tokens; use paged_attn_fwd with a caller
+ *     workspace beyond that).
+ *   - Every call on one GPU uses that GPU's array, which keeps the last
+ *     call's contents; nothing in it needs to start at zero (each call writes
+ *     every slot it reads).  Calls that overlap on one GPU (other streams,
+ *     other host threads) race on it: serialise them.
+ */
+#define ATTN_STATIC_WORKSPACE_BYTES (64u << 20)
+int paged_attn_fwd_static(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, const int32_t* ctx_lens, const int32_t* q_lens,
+                          int block_size, void* o, float* lse,
+                          int num_seqs, int H, int d, float scale, int max_blocks_per_seq,
+                          int64_t kv_block_stride, int num_blocks, int max_q_len, int max_ctx_len,
+                          attn_dtype_t dtype, void* stream);
+
+/*
  * Grouped-query attention ("Sequence length doubles, inference time
  * quadruples", further optimisations: several query heads share one key and
  * value head; with one shared K/V head it is multi-query attention): H query

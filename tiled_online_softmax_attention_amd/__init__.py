@@ -13,7 +13,8 @@ from pathlib import Path
 
 __all__ = [
     "ATTN_BF16", "ATTN_F32", "AttnError", "library", "lib_path", "exported_symbols",
-    "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_kv_gather",
+    "attn_prefill_fwd", "paged_attn_fwd", "paged_attn_workspace_bytes", "paged_attn_fwd_static", "paged_kv_gather",
+    "STATIC_WORKSPACE_BYTES",
     "paged_kv_append", "paged_kv_release", "attn_prefill_gqa_fwd", "paged_attn_gqa_fwd",
     "paged_attn_gqa_workspace_bytes", "attn_prefill_bwd", "attn_prefill_bwd_workspace_bytes", "paged_attn_check",
     "attn_launch_opts_default", "LaunchOpts", "attn_strerror", "attn_version", "prefill", "prefill_bwd",
@@ -36,12 +37,15 @@ APPEND_OK, APPEND_EXHAUSTED, APPEND_TABLE_FULL, APPEND_INVALID = 0, 1, 2, 3
 CHECK_OK, CHECK_LENGTHS, CHECK_TABLE = 0, 1, 2
 ERR_BAD_TABLE = -11
 ERR_OPTION = -12
+# size of the library-owned workspace of paged_attn_fwd_static (per GPU)
+STATIC_WORKSPACE_BYTES = 64 << 20
 
 # every symbol include/attn.h declares
 exported_symbols = (
     "attn_prefill_fwd",
     "paged_attn_fwd",
     "paged_attn_workspace_bytes",
+    "paged_attn_fwd_static",
     "paged_kv_gather",
     "paged_kv_append",
     "paged_kv_release",
@@ -107,6 +111,8 @@ def library():
     lib.paged_attn_fwd.restype = I
     lib.paged_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.paged_attn_workspace_bytes.restype = SZ
+    lib.paged_attn_fwd_static.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, F, I, I64, I, I, I, I, P]
+    lib.paged_attn_fwd_static.restype = I
     lib.paged_kv_gather.argtypes = [P, P, P, P, I, I, I, I, I, I64, I, I, P, P, P]
     lib.paged_kv_gather.restype = I
     lib.paged_kv_append.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I64, I, I, I, P]
@@ -162,6 +168,14 @@ def paged_attn_fwd(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size,
 
 def paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len) -> int:
     return int(library().paged_attn_workspace_bytes(num_seqs, H, d, block_size, max_q_len, max_ctx_len))
+
+
+def paged_attn_fwd_static(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse, num_seqs, H, d,
+                          scale, max_blocks_per_seq, kv_block_stride, num_blocks, max_q_len, max_ctx_len, dtype,
+                          stream):
+    return library().paged_attn_fwd_static(q, k_pool, v_pool, block_table, ctx_lens, q_lens, block_size, o, lse,
+                                           num_seqs, H, d, float(scale), max_blocks_per_seq, kv_block_stride,
+                                           num_blocks, max_q_len, max_ctx_len, int(dtype), stream)
 
 
 def paged_kv_gather(k_pool, v_pool, block_table, ctx_lens, block_size, num_seqs, H, d, max_blocks_per_seq,

@@ -10,7 +10,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libattn_gfx950.so"
 SOURCES = ["attn_api.hip", "prefill_gfx950.hip", "paged_gfx950.hip", "append_gfx950.hip", "bwd_gfx950.hip",
-           "check_gfx950.hip"]
+           "check_gfx950.hip", "noalloc_gfx950.hip"]
 HEADERS = ["attn_internal.h", "append_internal.h", "bwd_internal.h", "attn_mfma_core.h", "attn_mfma_kernel.h",
            "attn_mfma_pipe.h", "check_internal.h"]
 
