@@ -42,7 +42,15 @@
 extern "C" {
 #endif
 
-typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype_t;
+/* Element type.  The two range markers are not types: they make every int a
+   valid value of the enum, so a caller's out-of-range dtype is an argument
+   error (ATTN_ERR_DTYPE), not undefined behaviour in the library's C++. */
+typedef enum {
+    ATTN_BF16 = 0,
+    ATTN_F32 = 1,
+    ATTN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    ATTN_DTYPE_RANGE_MAX_ = 2147483647
+} attn_dtype_t;
 
 enum {
     ATTN_OK = 0,
