@@ -98,6 +98,10 @@ enum {
  *   paged_tile_map : -1 auto; work mapping of the tile kernel: 0 contiguous
  *                    ranges per XCD, 1 (request, K/V head) pairs dealt
  *                    round-robin, 2 single items round-robin [same bits].
+ *   paged_tile_rows: -1 auto (128); query rows per tile-kernel workgroup:
+ *                    128 (four waves, the plain key loop) or 256 (eight
+ *                    waves, the pipelined loop; each K/V tile read once for
+ *                    256 rows) [same bits].
  *   bwd_pair_q     : -1 auto (on for causal); 0 / 1: query tiles t and
  *                    n-1-t in one dQ workgroup [same bits].
  *   bwd_pair_kv    : -1 auto (on for causal); 0 / 1: key blocks kb and
@@ -113,6 +117,7 @@ typedef struct {
     int paged_tile_map;
     int bwd_pair_q;
     int bwd_pair_kv;
+    int paged_tile_rows;
 } attn_launch_opts_t;
 
 /* Fills *opts with the automatic values (no-op for NULL). */

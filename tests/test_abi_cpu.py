@@ -284,7 +284,7 @@ def test_launch_opts_default_values():
         setattr(o, name, 77)
     attn.attn_launch_opts_default(ctypes.byref(o))
     want = dict(prefill_kernel=-1, prefill_pair=-1, prefill_order=-1, paged_path=-1, paged_split_tokens=0,
-                paged_decode_heads=0, paged_tile_map=-1, bwd_pair_q=-1, bwd_pair_kv=-1)
+                paged_decode_heads=0, paged_tile_map=-1, bwd_pair_q=-1, bwd_pair_kv=-1, paged_tile_rows=-1)
     assert {name: getattr(o, name) for name, _ in attn.LaunchOpts._fields_} == want
     attn.attn_launch_opts_default(None)   # NULL is a no-op
 
@@ -292,7 +292,8 @@ def test_launch_opts_default_values():
 @pytest.mark.parametrize("field,bad", [
     ("prefill_kernel", 2), ("prefill_kernel", -2), ("prefill_pair", 2), ("prefill_order", 2), ("prefill_order", 4),
     ("paged_path", 2), ("paged_split_tokens", -1), ("paged_decode_heads", 3), ("paged_decode_heads", 16),
-    ("paged_tile_map", 3), ("bwd_pair_q", 5), ("bwd_pair_kv", -3),
+    ("paged_tile_map", 3), ("bwd_pair_q", 5), ("bwd_pair_kv", -3), ("paged_tile_rows", 64),
+    ("paged_tile_rows", 0), ("paged_tile_rows", 512),
 ])
 def test_out_of_range_options_rejected(field, bad):
     """Every entry point that takes opts rejects an out-of-range field with

@@ -36,6 +36,7 @@ struct PagedPlan {
     int split_tokens;    // keys per context split (multiple of the page size)
     int max_splits;      // ceil(max_ctx_len / split_tokens)
     int nqt;             // query tiles per request (chunk path)
+    int tile_waves;      // chunk path: waves per workgroup (4: 128-row tiles, 8: 256-row tiles)
     int gc;              // decode path: query heads per workgroup (they share one K/V head)
     int n_chunks;        // decode path: workgroups per K/V head (= (H / H_kv) / gc)
     size_t ws_o_bytes;   // fp32 partial outputs

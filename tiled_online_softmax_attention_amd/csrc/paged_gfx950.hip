@@ -23,6 +23,7 @@
 
 #include "attn_internal.h"
 #include "attn_mfma_kernel.h"
+#include "attn_mfma_pipe.h"
 
 namespace attn {
 
@@ -323,6 +324,35 @@ struct PagedKV {
     }
     __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1) % BS; }
     __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
+    // Copies of the pipelined key loop.  The window holds the table entries
+    // of pages p0 + base .. p0 + base + 63 (lane l: base + l, clamped to the
+    // last page of the context); a tile's copies take the entry of the page
+    // holding the wave's copy group out of it with a lane read.
+    struct SrcWin {
+        int base;   // window start, relative to p0 (uniform)
+        int pg;     // lane l: table entry of page p0 + base + l
+    };
+    __device__ __forceinline__ SrcWin empty_win() const { return SrcWin{-(1 << 30), 0}; }
+    __device__ __forceinline__ void win_update(SrcWin& win, const WaveCtx& cx, int key_lo, int key_hi) const
+    {
+        const int last = (cx.kv_end - 1) / BS - p0;    // last page of the context, relative to p0
+        const int lo = min(key_lo / BS - p0, last), hi = min(key_hi / BS - p0, last);
+        if (lo < win.base || hi >= win.base + 64) {
+            win.base = lo;
+            win.pg = ptab[min(lo + cx.lane, last)];
+        }
+    }
+    __device__ __forceinline__ int copy_src(const SrcWin& win, const WaveCtx& cx, int key_base) const
+    {
+        const int cw = cx.w & 3;
+        const int gkey = key_base + 16 * (cw >= TileCfg<D>::GROUPS ? cw - TileCfg<D>::GROUPS : cw);
+        return __builtin_amdgcn_readlane(win.pg, min(gkey, cx.kv_end - 1) / BS - p0 - win.base);
+    }
+    template <int NW>
+    __device__ __forceinline__ void copy_tile(const WaveCtx& cx, char* buf, int key_base, int page) const
+    {
+        issue_tile_copies_paged<D, NW, BS>(kbase, vbase, blk_bytes, cx, buf, key_base, page);
+    }
 };
 
 // Work mapping.  An item is (request r, K/V head hk, context split, query
@@ -340,18 +370,28 @@ struct PagedKV {
 constexpr int kChunkPairsPerXcd = 4;
 enum { kMapRanges = 0, kMapPairs = 1, kMapItems = 2 };
 
-template <int D, int BS>
-__global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_work, int map)
+// NW = 4: 128-row query tiles, the plain key loop, three workgroups per CU;
+// NW = 8: 256-row query tiles, the pipelined key loop (attn_mfma_pipe.h), one
+// workgroup per CU, each K/V tile staged once for 256 rows.
+template <int D, int BS, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void paged_chunk_kernel(PagedArgs a, int n_work, int map)
 {
     using C = TileCfg<D>;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
     __shared__ int32_t ptab[kChunkMaxSplit / BS];
     const TileBuffers buf{lds0, lds1};
+    PipeBuffers pbuf{{lds0, lds1, nullptr, nullptr}};
+    if constexpr (NW == 8) {
+        __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
+        __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
+        pbuf.b[2] = lds2;
+        pbuf.b[3] = lds3;
+    }
     // A tile holds ppt query positions x G query heads (the heads of one K/V
     // group), so each K/V tile staged in LDS serves the whole group.
     const int G = a.H / a.H_kv;
-    const int ppt = kTileRows / G;                     // positions per tile
+    const int ppt = 32 * NW / G;                       // positions per tile
     const int nqt = (a.max_q_len + ppt - 1) / ppt;
     int qt, split, pair;                               // pair = r * H_kv + hk
     if (map == kMapPairs) {
@@ -395,7 +435,7 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
     const int kb = split * S, ke = min(ctx, (split + 1) * S);
     const int p0 = kb / BS, np = (ke - 1) / BS - p0 + 1;
     const int32_t* table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
-    for (int i = threadIdx.x; i < np; i += C::kThreads) ptab[i] = table[p0 + i];
+    for (int i = threadIdx.x; i < np; i += 64 * NW) ptab[i] = table[p0 + i];
     __syncthreads();
     PagedKV<D, BS> kv;
     kv.kbase = (const char*)a.k_pool + (int64_t)hk * BS * D * 2;
@@ -433,7 +473,8 @@ __global__ __launch_bounds__(256, 3) void paged_chunk_kernel(PagedArgs a, int n_
         out.lse_hstride = a.max_splits;
         out.fp32_out = 1;
     }
-    run_query_tile<D>(P, kv, out, a.scale * kLog2e, buf);
+    if constexpr (NW == 8) run_pipe_tile<D, NW>(P, kv, out, a.scale * kLog2e, pbuf);
+    else run_query_tile<D>(P, kv, out, a.scale * kLog2e, buf);
 }
 
 // ============================================================================
@@ -660,10 +701,22 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         while (S > s_min && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         if (S < s_min) S = s_min;
         p.nqt = 1;
+        p.tile_waves = 4;
     } else {
-        const int ppt = kTileRows / G;                 // query positions per tile
+        // 128-row workgroups (four waves, the plain key loop, three per CU)
+        // unless asked for 256 rows (eight waves, the pipelined loop, one per
+        // CU), which read each K/V tile once for twice the rows but keep the
+        // matrix cores less busy.  8 x 512-row chunks on 32 heads, contexts
+        // of 9-33K keys: 128 rows 949 TFLOP/s with K/V fetched 1.27x the
+        // algorithmic bytes (the four tiles of a request share it in L2 in
+        // part), 256 rows 879 TFLOP/s at 1.00x.
+        p.tile_waves = (opts.paged_tile_rows == 256) ? 8 : 4;
+        const int ppt = 32 * p.tile_waves / G;         // query positions per tile
         p.nqt = (max_q_len + ppt - 1) / ppt;
-        const int64_t items = (int64_t)num_seqs * p.nqt * H_kv;
+        // the split plan counts 128-row tiles whatever the workgroup size, so
+        // both sizes split the context alike (and give the same bits)
+        const int ppt128 = kTileRows / G;
+        const int64_t items = (int64_t)num_seqs * ((max_q_len + ppt128 - 1) / ppt128) * H_kv;
         // Decode-length queries (grouped heads on this path) leave one wave of
         // the tile with rows, so a workgroup is latency-bound and more, shorter
         // splits keep more of them in flight; longer queries have full tiles
@@ -718,8 +771,12 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         const int64_t grid = (map == kMapPairs) ? (pairs + 7) / 8 * 8 * per_pair
                            : (map == kMapRanges) ? (n_work + 7) / 8 * 8 : n_work;
         if (grid > (int64_t)INT32_MAX) return -2;
-        hipLaunchKernelGGL((paged_chunk_kernel<D, BS>), dim3((unsigned)grid), dim3(TileCfg<D>::kThreads), 0, stream, a,
-                           (int)n_work, map);
+        if (plan.tile_waves == 8)
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+                               (int)n_work, map);
+        else
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+                               (int)n_work, map);
     }
     if (a.max_splits > kCombineHeadsMaxSplits) {
         const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;

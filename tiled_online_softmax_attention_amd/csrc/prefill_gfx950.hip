@@ -56,6 +56,16 @@ struct ContigKV {
     __device__ __forceinline__ const char* k_group(int, int) const { return k; }
     __device__ __forceinline__ const char* v_group(int, int) const { return v; }
     __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1); }
+    // copies of the pipelined key loop: nothing to look up per tile
+    struct SrcWin {};
+    __device__ __forceinline__ SrcWin empty_win() const { return SrcWin{}; }
+    __device__ __forceinline__ void win_update(SrcWin&, const WaveCtx&, int, int) const {}
+    __device__ __forceinline__ int copy_src(const SrcWin&, const WaveCtx&, int) const { return 0; }
+    template <int NW>
+    __device__ __forceinline__ void copy_tile(const WaveCtx& cx, char* buf, int key_base, int) const
+    {
+        issue_tile_copies_flat<D, NW>(*this, cx, buf, key_base);
+    }
 };
 
 // Linear work id for this workgroup after the XCD-contiguous remap; the grid
@@ -68,7 +78,11 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
 
 // KIND 0: the plain key loop (attn_mfma_kernel.h: two LDS buffers, three
 // workgroups per CU).  KIND 1: the software-pipelined key loop of
-// attn_mfma_pipe.h (four LDS buffers, two workgroups per CU).
+// attn_mfma_pipe.h (four LDS buffers, two workgroups per CU).  (Eight waves
+// on 256-row tiles, one workgroup per CU, each K/V tile copied once for 256
+// rows, measured slower: 16x32x8192 1081 against 1102 TFLOP/s, 1x32x2048
+// 498 against 610, the second for want of two workgroups per CU to balance
+// the causal tiles.)
 template <int D, bool PAIR, int KIND>
 __global__ __launch_bounds__(256, KIND == 0 ? 3 : 2) void prefill_bf16_kernel(PrefillArgs a)
 {
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(256, KIND == 0 ? 3 : 2) void prefill_bf16_kernel(Pr
         out.lse_stride = 1;
         out.fp32_out = 0;
         if (it) __syncthreads();   // LDS reuse across the two tiles
-        if constexpr (PIPE) run_pipe_tile<D>(P, kv, out, c2, pbuf);
+        if constexpr (PIPE) run_pipe_tile<D, 4>(P, kv, out, c2, pbuf);
         else run_query_tile<D>(P, kv, out, c2, buf);
     }
 }
