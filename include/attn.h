@@ -88,20 +88,24 @@ enum {
  *                    tiles dealt together, for grids of one dispatch round);
  *                    3 tile-major [same bits].
  *   paged_path     : -1 auto; 0 the vector decode kernel (only for max_q_len
- *                    <= 4); 1 the MFMA tile kernel.
+ *                    <= 4); 1 the MFMA tile kernel; 2 the decode MFMA
+ *                    kernel (only for max_q_len * H / H_kv <= 16).
  *   paged_split_tokens : 0 auto; otherwise the keys per context split
  *                    (rounded up to whole pages, 64-key units on the tile
- *                    kernel, at most 8192 there).
+ *                    kernel; at most 8192 there and 64 pages on the decode
+ *                    MFMA kernel).
  *   paged_decode_heads : 0 auto; 1, 2, 4 or 8 query heads of one K/V group
  *                    per vector-decode workgroup (must divide H / H_kv; at
  *                    most 4 with 32-token pages).
  *   paged_tile_map : -1 auto; work mapping of the tile kernel: 0 contiguous
  *                    ranges per XCD, 1 (request, K/V head) pairs dealt
  *                    round-robin, 2 single items round-robin [same bits].
- *   paged_tile_rows: -1 auto (128); query rows per tile-kernel workgroup:
- *                    128 (four waves, the plain key loop) or 256 (eight
- *                    waves, the pipelined loop; each K/V tile read once for
- *                    256 rows) [same bits].
+ *   paged_tile_kernel: -1 auto; key loop and workgroup size of the tile
+ *                    kernel: 0 the plain loop on 128-row workgroups (three
+ *                    per CU); 1 the pipelined loop on 128-row workgroups
+ *                    (two per CU); 2 the pipelined loop on 256-row
+ *                    workgroups of eight waves (one per CU; each K/V tile
+ *                    read once for 256 rows) [same bits].
  *   bwd_pair_q     : -1 auto (on for causal); 0 / 1: query tiles t and
  *                    n-1-t in one dQ workgroup [same bits].
  *   bwd_pair_kv    : -1 auto (on for causal); 0 / 1: key blocks kb and
@@ -117,7 +121,7 @@ typedef struct {
     int paged_tile_map;
     int bwd_pair_q;
     int bwd_pair_kv;
-    int paged_tile_rows;
+    int paged_tile_kernel;
 } attn_launch_opts_t;
 
 /* Fills *opts with the automatic values (no-op for NULL). */
@@ -177,8 +181,9 @@ int attn_prefill_fwd(const void* q, const void* k, const void* v, void* o, float
  * q_lens[r] <= max_q_len, every block-table entry needed lies in
  * [0, num_blocks), and ceil(max_ctx_len / block_size) <= max_blocks_per_seq.
  * The kernels do not check it (a bad entry reads outside the pool; a
- * ctx_lens[r] above max_ctx_len is read as max_ctx_len, so it cannot reach
- * past the table row or the workspace, but the result is then wrong);
+ * ctx_lens[r] above max_ctx_len is read as max_ctx_len and a q_lens[r]
+ * above max_q_len as max_q_len, so neither can reach past the table row or
+ * the workspace, but the result is then wrong);
  * paged_attn_check does, and with the environment variable ATTN_DEBUG=1 every
  * paged call runs that check first, waits for it (the call then synchronises
  * `stream`) and returns ATTN_ERR_BAD_TABLE, launching nothing else, when the

@@ -137,6 +137,8 @@ def _max_splits(num_seqs, H, H_kv, d, bs, max_q, max_ctx):
     ((64, 32, 32, 128, 16, 1, 16384), 43),
     # the same lengths on 4 K/V heads (tile kernel, decode-length rows): 1280-key splits
     ((64, 32, 4, 128, 16, 1, 16384), 13),
+    # ... and 128 such requests (512 pairs: decode MFMA kernel, 8 rows): 1024-key splits
+    ((128, 32, 4, 128, 16, 1, 16384), 16),
     # chunked prefill, 8 x 512 rows on 32-token pages (tile kernel): 8192-key splits
     ((8, 32, 32, 128, 32, 512, 33280), 5),
     # small decode batches: splits halved down to one 16-token page per wave, no further
@@ -284,16 +286,16 @@ def test_launch_opts_default_values():
         setattr(o, name, 77)
     attn.attn_launch_opts_default(ctypes.byref(o))
     want = dict(prefill_kernel=-1, prefill_pair=-1, prefill_order=-1, paged_path=-1, paged_split_tokens=0,
-                paged_decode_heads=0, paged_tile_map=-1, bwd_pair_q=-1, bwd_pair_kv=-1, paged_tile_rows=-1)
+                paged_decode_heads=0, paged_tile_map=-1, bwd_pair_q=-1, bwd_pair_kv=-1, paged_tile_kernel=-1)
     assert {name: getattr(o, name) for name, _ in attn.LaunchOpts._fields_} == want
     attn.attn_launch_opts_default(None)   # NULL is a no-op
 
 
 @pytest.mark.parametrize("field,bad", [
     ("prefill_kernel", 2), ("prefill_kernel", -2), ("prefill_pair", 2), ("prefill_order", 2), ("prefill_order", 4),
-    ("paged_path", 2), ("paged_split_tokens", -1), ("paged_decode_heads", 3), ("paged_decode_heads", 16),
-    ("paged_tile_map", 3), ("bwd_pair_q", 5), ("bwd_pair_kv", -3), ("paged_tile_rows", 64),
-    ("paged_tile_rows", 0), ("paged_tile_rows", 512),
+    ("paged_path", 3), ("paged_split_tokens", -1), ("paged_decode_heads", 3), ("paged_decode_heads", 16),
+    ("paged_tile_map", 3), ("bwd_pair_q", 5), ("bwd_pair_kv", -3), ("paged_tile_kernel", 3),
+    ("paged_tile_kernel", -2),
 ])
 def test_out_of_range_options_rejected(field, bad):
     """Every entry point that takes opts rejects an out-of-range field with
@@ -332,6 +334,24 @@ def test_split_option_sets_the_workspace():
     s256 = attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=256))
     assert s256 == (64 * 32 * 64 * 128 * 4 + 255) // 256 * 256 + 64 * 32 * 64 * 4
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=1 << 20)) == 0
+
+
+def test_decode_mfma_plan():
+    """Decode on grouped heads (32 query heads on 4 K/V heads, one query row:
+    8 rows of the decode MFMA kernel's 16) on that kernel splits the context
+    into 1024-key splits for a 64-request batch, caps a forced split at 64
+    pages, and the kernel is not taken for more rows than 16 (q_len 3 on
+    groups of 8)."""
+    def ws(splits, rows=64 * 1, H=32):
+        return (rows * H * splits * 128 * 4 + 255) // 256 * 256 + rows * H * splits * 4
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 1, 16384, opts(paged_path=2)) == ws(16)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 1, 16384,
+                                               opts(paged_split_tokens=4096, paged_path=2)) == ws(16)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 32, 1, 16384,
+                                               opts(paged_split_tokens=4096, paged_path=2)) == ws(8)
+    # 3 rows x 8 heads = 24 > 16: the tile kernel's plan (64-key units, no page cap)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 3, 16384,
+                                               opts(paged_split_tokens=4096, paged_path=2)) == ws(4, rows=64 * 3)
 
 
 def check_call(**kw):

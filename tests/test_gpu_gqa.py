@@ -75,13 +75,14 @@ def run_paged(pi, split=None, path=None):
 @pytest.mark.parametrize("H,H_kv", [(32, 4), (32, 8), (32, 16), (32, 1), (12, 4), (6, 2)])
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("split", [None, 64])
-@pytest.mark.parametrize("path", [0, 1])
+@pytest.mark.parametrize("path", [0, 1, 2])
 def test_paged_decode_gqa_matches_oracle(H, H_kv, bs, split, path):
-    """Decode (q_len 1 to 3) on both paths.  Vector kernel: one workgroup
-    serves up to 8 (16-token pages) or 4 (32-token pages) query heads of a
-    group, larger groups split across workgroups (MQA at 32 query heads,
-    groups of 3).  MFMA tile kernel: a tile holds all heads of a group for
-    128 / G positions."""
+    """Decode (q_len 1 to 3) on the three paths.  Vector kernel: one
+    workgroup serves up to 8 (16-token pages) or 4 (32-token pages) query
+    heads of a group, larger groups split across workgroups (MQA at 32 query
+    heads, groups of 3).  MFMA tile kernel: a tile holds all heads of a group
+    for 128 / G positions.  Decode MFMA kernel: where G x 3 <= 16 (else the
+    launcher keeps its own choice)."""
     ctx = [700, 33, 1500, 5, 64]
     ql = [1, 3, 1, 1, 2]
     pi = make_gqa(ctx, ql, H, H_kv, bs=bs, seed=H + H_kv + bs)
@@ -89,6 +90,25 @@ def test_paged_decode_gqa_matches_oracle(H, H_kv, bs, split, path):
     o, lse = run_paged(pi, split, path)
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, bs, pi.scale)
     check_close("paged decode gqa", o, o_ref, lse, l_ref, torch.bfloat16)
+
+
+@pytest.mark.parametrize("H,H_kv,ql", [(32, 4, 1), (32, 4, 2), (32, 2, 1), (16, 4, 4), (8, 8, 1), (6, 2, 5)])
+@pytest.mark.parametrize("bs", [16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("split", [None, 32, 400, 4096])
+def test_paged_decode_mfma_matches_oracle(H, H_kv, ql, bs, d, split):
+    """The decode MFMA kernel (paged_path 2): groups of 8 and 16 heads at one
+    position, 8 x 2 and 4 x 4 rows (all 16), one plain head (1 row of 16), 3
+    heads x 5 positions (15 rows); contexts shorter than a 16-key tile, tiles
+    cut by the context end, splits of one or two pages, of a length that is
+    not a whole number of tiles per wave, and above the 64-page cap."""
+    ctx = [1, 15, 16, 17, 300, 1030, 5000]
+    qls = [min(ql, c) for c in ctx]
+    pi = make_gqa(ctx, qls, H, H_kv, d=d, bs=bs, seed=H + 3 * H_kv + ql + bs + d)
+    log("paged decode mfma H=%d H_kv=%d ql=%d bs=%d d=%d split=%s" % (H, H_kv, ql, bs, d, split))
+    o, lse = run_paged(pi, split, 2)
+    o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, bs, pi.scale)
+    check_close("paged decode mfma", o, o_ref, lse, l_ref, torch.bfloat16)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -136,21 +156,23 @@ def test_paged_gqa_mixed_batch():
 
 def test_c4_gqa8_full_size_sampled_rows():
     """The 64-request decode batch with 32 query heads on 4 K/V heads, in the
-    benchmark's launch configuration (MFMA tile path); 64 seeded (request,
-    head) pairs checked against the oracle; and, on the vector kernel, the
-    whole output against the repeated-head pool bit for bit."""
+    benchmark's launch configuration (MFMA tile kernel, pipelined loop) and
+    on the decode MFMA kernel; 64 seeded (request, head) pairs checked
+    against the oracle; and, on the vector kernel, the whole output against
+    the repeated-head pool bit for bit."""
     cfg = inputs.C4_GQA8
     pi = inputs.paged_inputs(cfg, DEV)
     log("c4 gqa8 full size: %d requests, sum ctx %d" % (pi.num_seqs, int(pi.ctx_lens.sum())))
-    o, lse = run_paged(pi)
     trip = inputs.sample_triples(cfg.seed, 64, (pi.num_seqs, cfg.H), edge=[(0, 0), (63, 31), (10, 7), (10, 8)])
     ridx = [r for r, _ in trip]
     hidx = [h for _, h in trip]
     o_ref, l_ref = oracle.paged_attention_rows(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, 16, pi.scale,
                                                ridx, hidx, [0] * len(trip))
-    og = torch.stack([o[r, h] for r, h in trip])
-    lg = torch.stack([lse[r, h] for r, h in trip])
-    check_close("c4 gqa8 sampled", og, o_ref, lg, l_ref, torch.bfloat16)
+    for path in (None, 2):
+        o, lse = run_paged(pi, path=path)
+        og = torch.stack([o[r, h] for r, h in trip])
+        lg = torch.stack([lse[r, h] for r, h in trip])
+        check_close("c4 gqa8 sampled path %s" % path, og, o_ref, lg, l_ref, torch.bfloat16)
     o1, l1 = run_paged(pi, split=512, path=0)
     o2, l2 = attn.paged_attention(pi.q, repeat_pool(pi.pool, 8), pi.block_table, pi.ctx_lens, pi.q_lens, 16,
                                   pi.scale, options=path_opts(512, 0))

@@ -81,53 +81,54 @@ def test_chunk_split_tile_counts(split):
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("split", [None, 128, 320, 4096])
-def test_chunk_tile_rows_bit_identical(bs, d, split):
-    """Tile-kernel workgroups of 128 rows (four waves, the plain key loop)
-    and of 256 rows (eight waves, the pipelined loop, page-table entries read
-    from a 64-page register window) give the same bits and match the oracle:
-    ragged chunks of one to five 128-row tiles, a 1-row request, splits of 2
-    to 128 key tiles (4096 keys = 256 pages of 16 tokens: the window moves
-    several times per split)."""
+def test_chunk_tile_kernels_bit_identical(bs, d, split):
+    """The tile kernel's three variants -- the plain key loop on 128-row
+    workgroups, the pipelined loop (page-table entries read from a 64-page
+    register window) on 128- and on 256-row workgroups -- give the same bits
+    and match the oracle: ragged chunks of one to five 128-row tiles, a 1-row
+    request, splits of 2 to 128 key tiles (4096 keys = 256 pages of 16
+    tokens: the window moves several times per split)."""
     ctx = [5, 129, 700, 1200, 5000, 1]
     ql = [5, 129, 300, 77, 600, 1]
     pi = make(ctx, ql, H=2, d=d, bs=bs, seed=31 + bs + d)
     outs = []
-    for rows in (128, 256):
-        log("chunk tile rows %d bs%d d%d split %s" % (rows, bs, d, split))
-        opts = {"paged_tile_rows": rows, "paged_path": 1}
+    for kind in (0, 1, 2):
+        log("chunk tile kernel %d bs%d d%d split %s" % (kind, bs, d, split))
+        opts = {"paged_tile_kernel": kind, "paged_path": 1}
         if split is not None:
             opts["paged_split_tokens"] = split
         o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
                                       pi.scale, options=opts)
         torch.cuda.synchronize()
         outs.append((o, lse))
-    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
-    assert torch.equal(outs[0][1], outs[1][1])
+    for o, l in outs[1:]:
+        assert torch.equal(outs[0][0].view(torch.int16), o.view(torch.int16)) and torch.equal(outs[0][1], l)
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
                                           pi.scale)
-    check_close("chunk 256 rows", outs[1][0], o_ref, outs[1][1], l_ref, torch.bfloat16)
+    check_close("chunk tile kernels", outs[2][0], o_ref, outs[2][1], l_ref, torch.bfloat16)
 
 
-@pytest.mark.parametrize("H,H_kv,ql", [(32, 8, 130), (8, 1, 40), (6, 2, 100)])
-def test_chunk_tile_rows_grouped_heads(H, H_kv, ql):
-    """256-row workgroups on grouped query heads (64, 32 and 85 positions of
-    4, 8 and 3 heads per workgroup): same bits as 128-row workgroups, and the
-    oracle."""
+@pytest.mark.parametrize("H,H_kv,ql", [(32, 8, 130), (8, 1, 40), (6, 2, 100), (32, 4, 1), (32, 4, 4)])
+def test_chunk_tile_kernels_grouped_heads(H, H_kv, ql):
+    """The tile kernel's variants on grouped query heads (positions of 4, 8,
+    3 and 8 heads per workgroup, down to decode rows: 8 or 32 valid rows of
+    128): same bits, and the oracle."""
     ctx = [900, 2000, 300, 4100]
     qls = [min(ql, c) for c in ctx]
-    pi = inputs.build_paged(ctx, qls, H_kv, 128, 16, 55 + H, DEV, H_q=H)
+    pi = inputs.build_paged(ctx, qls, H_kv, 128, 16, 55 + H + ql, DEV, H_q=H)
     outs = []
-    for rows in (128, 256):
-        log("grouped chunk tile rows %d H=%d H_kv=%d" % (rows, H, H_kv))
+    for kind in (0, 1, 2):
+        log("grouped chunk tile kernel %d H=%d H_kv=%d ql=%d" % (kind, H, H_kv, ql))
         o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
-                                      pi.scale, options={"paged_tile_rows": rows, "paged_split_tokens": 1024})
+                                      pi.scale, options={"paged_tile_kernel": kind, "paged_split_tokens": 1024,
+                                                         "paged_path": 1})
         torch.cuda.synchronize()
         outs.append((o, lse))
-    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
-    assert torch.equal(outs[0][1], outs[1][1])
+    for o, l in outs[1:]:
+        assert torch.equal(outs[0][0].view(torch.int16), o.view(torch.int16)) and torch.equal(outs[0][1], l)
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
                                           pi.scale)
-    check_close("grouped chunk 256 rows", outs[1][0], o_ref, outs[1][1], l_ref, torch.bfloat16)
+    check_close("grouped chunk tile kernels", outs[1][0], o_ref, outs[1][1], l_ref, torch.bfloat16)
 
 
 def test_chunk_mixed_with_decode_rows():

@@ -68,7 +68,7 @@ class LaunchOpts(ctypes.Structure):
     (include/attn.h documents every field; -1 / 0 = automatic)."""
     _fields_ = [(name, ctypes.c_int) for name in (
         "prefill_kernel", "prefill_pair", "prefill_order", "paged_path", "paged_split_tokens",
-        "paged_decode_heads", "paged_tile_map", "bwd_pair_q", "bwd_pair_kv", "paged_tile_rows")]
+        "paged_decode_heads", "paged_tile_map", "bwd_pair_q", "bwd_pair_kv", "paged_tile_kernel")]
 
 
 def _opts(options):

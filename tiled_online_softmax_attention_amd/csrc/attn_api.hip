@@ -58,13 +58,13 @@ int read_opts(const attn_launch_opts_t* in, attn_launch_opts_t* out)
                     (o.prefill_pair >= -1 && o.prefill_pair <= 1) &&
                     (o.prefill_order == -1 || o.prefill_order == 0 || o.prefill_order == 1 ||
                      o.prefill_order == 3) &&
-                    (o.paged_path >= -1 && o.paged_path <= 1) &&
+                    (o.paged_path >= -1 && o.paged_path <= 2) &&
                     (o.paged_split_tokens >= 0 && o.paged_split_tokens <= (1 << 24)) &&
                     (o.paged_decode_heads == 0 || o.paged_decode_heads == 1 || o.paged_decode_heads == 2 ||
                      o.paged_decode_heads == 4 || o.paged_decode_heads == 8) &&
                     (o.paged_tile_map >= -1 && o.paged_tile_map <= 2) &&
                     (o.bwd_pair_q >= -1 && o.bwd_pair_q <= 1) && (o.bwd_pair_kv >= -1 && o.bwd_pair_kv <= 1) &&
-                    (o.paged_tile_rows == -1 || o.paged_tile_rows == 128 || o.paged_tile_rows == 256);
+                    (o.paged_tile_kernel >= -1 && o.paged_tile_kernel <= 2);
     return ok ? ATTN_OK : ATTN_ERR_OPTION;
 }
 
@@ -107,7 +107,7 @@ void attn_launch_opts_default(attn_launch_opts_t* opts)
     opts->paged_tile_map = -1;
     opts->bwd_pair_q = -1;
     opts->bwd_pair_kv = -1;
-    opts->paged_tile_rows = -1;
+    opts->paged_tile_kernel = -1;
 }
 
 int attn_prefill_gqa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

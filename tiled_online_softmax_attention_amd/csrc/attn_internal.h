@@ -32,11 +32,11 @@ struct PrefillArgs {
 
 // Host-side plan of a paged launch: a pure function of the host bounds.
 struct PagedPlan {
-    int path;            // 0: vector decode kernel, 1: MFMA chunk kernel
+    int path;            // 0: vector decode kernel, 1: MFMA tile kernel, 2: decode MFMA kernel
     int split_tokens;    // keys per context split (multiple of the page size)
     int max_splits;      // ceil(max_ctx_len / split_tokens)
     int nqt;             // query tiles per request (chunk path)
-    int tile_waves;      // chunk path: waves per workgroup (4: 128-row tiles, 8: 256-row tiles)
+    int tile_kernel;     // tile path: 0 plain loop, 128 rows; 1 pipelined loop, 128 rows; 2 pipelined, 256 rows
     int gc;              // decode path: query heads per workgroup (they share one K/V head)
     int n_chunks;        // decode path: workgroups per K/V head (= (H / H_kv) / gc)
     size_t ws_o_bytes;   // fp32 partial outputs

@@ -380,9 +380,35 @@ __device__ __forceinline__ void pipe_key_loop(WaveState<D>& ws, const bf16x8 (&q
     __builtin_amdgcn_s_waitcnt(0x3f70);
 }
 
+// The loop of a wave with no valid query row: it takes part in the copies and
+// the barriers of pipe_key_loop only.  Every wave of the workgroup publishes
+// tile t (t = 0 .. ntile - 1) at one barrier and issues its copies of tile
+// t + 2 right after it, the copies of tiles 0 and 1 before the first.
+template <int D, int NW, class KV>
+__device__ __forceinline__ void pipe_copy_loop(const KV& kv, const PipeCtx<D>& pc, const PipeBuffers& buf)
+{
+    using C = TileCfg<D>;
+    const int ntile = pc.cx.ntile;
+    typename KV::SrcWin win = kv.empty_win();
+    pipe_copies<D, NW>(kv, win, pc.cx, buf.b[0], pc.cx.kv_begin);
+    pipe_copies<D, NW>(kv, win, pc.cx, buf.b[1], pc.cx.kv_begin + C::BN);
+    for (int t = 0; t < ntile; t += 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (t + i < ntile) {
+                publish_tile<D, NW>();
+                pipe_copies<D, NW>(kv, win, pc.cx, buf.b[(i + 2) % kPipeBufs], pc.cx.kv_begin + (t + i + 2) * C::BN);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0x3f70);
+}
+
 // One query tile of 32 * NW rows: Q fragments, the key loop, and the epilogue
-// (O / l and the log-sum-exp of the valid rows).  Every wave computes (rows
-// past n_rows run on zero queries and are never stored).  The key tiles the
+// (O / l and the log-sum-exp of the valid rows).  Waves with valid rows
+// compute (rows past n_rows run on zero queries and are never stored); waves
+// past the last valid row (the tail of a short tile, e.g. the few rows of a
+// decode step on grouped heads) only copy.  The key tiles the
 // workgroup runs are those its last row needs, and the full ones those its
 // first row sees in full: rows of a later 128-row block may see more keys of
 // a masked tile (the mask keeps exactly what each row sees), and a key tile
@@ -402,6 +428,10 @@ __device__ __forceinline__ void run_pipe_tile(const TileProblem& P, const KV& kv
     pc.cx.voff = copy_voff<D>(w & 3, pc.cx.lane);
     pc.nf4 = n_full & ~3;
     v_read_offsets<D>(pc.vro, pc.cx.lane);
+    if (w * 32 >= P.n_rows) {
+        pipe_copy_loop<D, NW>(kv, pc, buf);
+        return;
+    }
     WaveState<D> ws;
     clear_state(ws);
     pipe_key_loop<D, NW>(ws, qf, kv, pc, buf);

@@ -37,6 +37,14 @@ __device__ __forceinline__ int req_ctx(const A& a, int r)
     return min(a.ctx_lens[r], a.max_ctx_len);
 }
 
+// Query rows of request r that the kernels compute: clamped to max_q_len
+// likewise (the grid and the split partials are sized by it).
+template <class A>
+__device__ __forceinline__ int req_ql(const A& a, int r)
+{
+    return min(a.q_lens[r], a.max_q_len);
+}
+
 
 // ---- small wave helpers ------------------------------------------------------
 template <int CTRL>
@@ -291,6 +299,272 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 }
 
 // ============================================================================
+// Decode on the matrix cores, for grouped query heads: the G = H / H_kv query
+// heads of one K/V head at a few query positions give G x q_len <= 16 rows,
+// which form the N side of 16x16 MFMAs:
+//   S^T (16 keys x 16 rows)  = K (16 keys x d) Q^T      16x16x32 bf16, d/32 steps
+//   O^T (d x 16 rows)       += V^T (d x 16 keys) P^T     16x16x16 bf16, d/16 blocks
+// The S^T accumulator (lane l: row l % 16, keys 4 (l / 16) .. + 3) is the P^T
+// operand as it stands.  One workgroup of four waves per (request, K/V head,
+// split); each wave takes 16-key tiles w, w + 4, ... of the split and keeps
+// two of them in flight beyond the one it computes: K straight into
+// registers in the MFMA operand layout, V into a ring of three 16-row LDS
+// tiles private to the wave (direct global -> LDS copies, landing row-major
+// with the swizzle of v_ofs; read back transposed with ds_read_b64_tr_b16).
+// A wave only waits for its own loads -- no barrier ties the waves together.
+// The online softmax is the tile kernel's (base 2, lazy offset, p rounded to
+// bf16 for the product, the sum in fp32); the four waves' (offset, sum, O)
+// are merged through LDS at the end.
+// ============================================================================
+constexpr int kDecMfmaRows = 16;       // query rows (heads x positions) per workgroup
+constexpr int kDecMfmaMinPairs = 512;  // (request, K/V head) pairs from which it is the default
+
+__device__ __forceinline__ f32x4 mfma16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16(i16x4 a, i16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// max / sum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lanes holding
+// one row), through the row-swap permutes (no LDS traffic)
+__device__ __forceinline__ float row4_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return half_max(fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+}
+__device__ __forceinline__ float row4_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return half_sum(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
+{
+    constexpr int KS = D / 32;         // S^T steps of 32 channels
+    constexpr int DB = D / 16;         // O^T blocks of 16 channels
+    constexpr int ROW = D * 2;         // bytes per K/V row
+    constexpr int VC = TileCfg<D>::COPIES_PER_GROUP;   // wave-wide V copies per 16-key tile
+    constexpr int PER = KS + VC;                        // loads per tile (vmcnt units)
+    constexpr int VT = 16 * ROW;                        // bytes of a V tile
+    constexpr int RED = 4 * DB * 4 * 64 * 4;            // merge buffer: every wave's O^T registers
+    constexpr int LDS_BYTES = (4 * 3 * VT > RED) ? 4 * 3 * VT : RED;
+    static_assert(PER * 2 < 64, "vmcnt field");
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];   // V rings, then the merge buffer
+    __shared__ float red_ml[4][kDecMfmaRows][2];                     // per wave and row: offset, sum
+
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // split-major: consecutive blocks (dealt to the 8 XCDs in turn) take
+    // different (request, K/V head) pairs, so that every XCD gets a share of
+    // each split index -- with the split fastest, a split count that is a
+    // multiple of 8 puts split s on XCD s mod 8, and the high splits exist
+    // only for the longest contexts
+    const int n_pairs = a.num_seqs * a.H_kv;
+    const int split = (int)blockIdx.x / n_pairs;
+    const int pair = (int)blockIdx.x % n_pairs;
+    const int hk = pair % a.H_kv;
+    const int r = pair / a.H_kv;
+    const int ctx = req_ctx(a, r), ql = req_ql(a, r);
+    const int S = a.split_tokens;
+    const int nsplit = (ctx + S - 1) / S;
+    if (split >= nsplit) return;
+    const int G = a.H / a.H_kv;
+    const int kbeg = split * S, kend = min(kbeg + S, ctx);
+    const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
+    const float thr = kRescaleLog2 / c2;
+
+    // this lane's row t = l % 16: query position qi, query head hk * G + qg;
+    // rows at or past G * q_len run on zero queries and are never stored
+    const int t = lane & 15;
+    const int qi = t / G, qg = t % G;
+    const bool row_ok = qi < ql;
+    const int vis_end = min(row_ok ? ctx - ql + qi + 1 : kend, kend);   // keys < vis_end are visible
+    const int64_t prow0 = prefix_len(a.q_lens, r, lane);                // packed row of position 0
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row_ok)
+            v = *(const u32x4*)((const char*)a.q + (((prow0 + qi) * a.H + hk * G + qg) * D + 32 * ks + 8 * (lane >> 4)) * 2);
+        qf[ks] = as_bf16x8(v);
+    }
+
+    // block-table entries of the split's pages (at most 64: the plan caps the
+    // split), lane i holding page p0 + i
+    const int p0 = kbeg / BS, np = (kend - 1) / BS - p0 + 1;
+    const int pgv = a.block_table[(int64_t)r * a.max_blocks_per_seq + p0 + min(lane, np - 1)];
+    const int64_t blk_bytes = a.kv_block_stride * 2;
+    const char* kbase = (const char*)a.k_pool + (int64_t)hk * BS * ROW;
+    const char* vbase = (const char*)a.v_pool + (int64_t)hk * BS * ROW;
+    const int last = kend - 1;
+
+    // Loads of 16-key tile tt (keys kbeg + 16 tt ..; a tile lies in one page):
+    // K lane l: key l % 16, channels 32 ks + 8 (l / 16) .. + 7 (the A operand
+    // of S^T); V: the copies of issue_tile_copies for one 16-row group, into
+    // the LDS tile vt.  Keys at or past kend are read from key kend - 1
+    // (valid data; the mask removes them).  KS register loads, then VC copies.
+    const auto load_tile = [&](int tt, u32x4 (&kr)[KS], char* vt) {
+        const int key0 = kbeg + 16 * tt;
+        const int64_t pg = __builtin_amdgcn_readlane(pgv, key0 / BS - p0);
+        const char* kp = kbase + pg * blk_bytes;
+        const int krow = min(key0 + (lane & 15), last) & (BS - 1);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[ks] = *(const u32x4*)(kp + krow * ROW + 64 * ks + 16 * (lane >> 4));
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vbase + pg * blk_bytes, (uint32_t)(BS * ROW));
+        const uint32_t vcol = v_dma_col<D>(lane);
+#pragma unroll
+        for (int i = 0; i < VC; ++i) {
+            const int vrow = min(key0 + i * TileCfg<D>::ROWS_PER_DMA + v_dma_row<D>(lane), last) & (BS - 1);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, ATTN_LDS(vt + i * 1024), 16, (uint32_t)vrow * ROW + vcol, 0,
+                                                     0, 0);
+        }
+#endif
+    };
+    // wait for this wave's loads of a tile, `later` tiles having been issued
+    // after it (vmcnt counts a wave's loads in issue order)
+    const auto wait_tile = [](int later) {
+        asm volatile("" ::: "memory");
+        if (later >= 2) __builtin_amdgcn_s_waitcnt(0x3f70 | (2 * PER));
+        else if (later == 1) __builtin_amdgcn_s_waitcnt(0x3f70 | PER);
+        else __builtin_amdgcn_s_waitcnt(0x3f70);
+        asm volatile("" ::: "memory");
+    };
+
+    f32x4 o[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, ms = 0.f, l = 0.f;
+    char* vring = lds + w * 3 * VT;
+    // this lane's transposing V read (A operand of O^T: channel 16 db + l % 16,
+    // keys 4 (l / 16) .. + 3): row 4 (l / 16) + (l % 16) / 4, channels
+    // 16 db + 4 (l % 4) .. + 3
+    const uint32_t tr_row = 4u * (uint32_t)(lane >> 4) + (uint32_t)((lane & 15) >> 2);
+
+    const auto compute = [&](int tt, const u32x4 (&kr)[KS], const char* vt) {
+        const int key0 = kbeg + 16 * tt;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) s = mfma16x32(as_bf16x8(kr[ks]), qf[ks], s);
+        // keys key0 + 4 (l / 16) + i; visible while below vis_end
+        const int nvis = vis_end - (key0 + 4 * (lane >> 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = (i < nvis) ? s[i] : -INFINITY;
+        const float mt = row4_max(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
+        if (__builtin_amdgcn_ballot_w64(mt > m + thr) != 0) {
+            const float m_new = fmaxf(m, mt);
+            const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * c2);
+            m = m_new;
+            ms = (m_new == -INFINITY) ? 0.f : m_new * c2;
+            l *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        }
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -ms));
+            l += p[i];
+        }
+        bf16x4 pb;
+        pb[0] = (__bf16)p[0];
+        pb[1] = (__bf16)p[1];
+        pb[2] = (__bf16)p[2];
+        pb[3] = (__bf16)p[3];
+        const i16x4 pbi = __builtin_bit_cast(i16x4, pb);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const uint32_t cb = (uint32_t)(32 * db + 8 * (lane & 3));    // byte column
+            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(vt + v_ofs<D>(tr_row, cb >> 4) + (cb & 15u)));
+            o[db] = mfma16x16(va, pbi, o[db]);
+        }
+    };
+
+    // this wave's tiles w + 4 k, k < nmine, in register sets / LDS tiles
+    // k % 3; the loads of tiles k + 1 and k + 2 are in flight while tile k is
+    // computed
+    const int ntile = (kend - kbeg + 15) / 16;
+    const int nmine = (w < ntile) ? (ntile - w + 3) / 4 : 0;
+    u32x4 ka[KS], kb[KS], kc[KS];
+    char* const v0 = vring;
+    char* const v1 = vring + VT;
+    char* const v2 = vring + 2 * VT;
+    if (nmine > 0) load_tile(w, ka, v0);
+    if (nmine > 1) load_tile(w + 4, kb, v1);
+    for (int k = 0; k < nmine; k += 3) {
+        // an LDS tile is reloaded only after the reads of its last use are done
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (k + 2 < nmine) load_tile(w + 4 * (k + 2), kc, v2);
+        wait_tile(min(2, nmine - 1 - k));
+        compute(w + 4 * k, ka, v0);
+        if (k + 1 >= nmine) break;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (k + 3 < nmine) load_tile(w + 4 * (k + 3), ka, v0);
+        wait_tile(min(2, nmine - 2 - k));
+        compute(w + 4 * (k + 1), kb, v1);
+        if (k + 2 >= nmine) break;
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (k + 4 < nmine) load_tile(w + 4 * (k + 4), kb, v1);
+        wait_tile(min(2, nmine - 3 - k));
+        compute(w + 4 * (k + 2), kc, v2);
+    }
+
+    // merge the four waves: O^T registers, offsets and row sums through LDS
+    // (the V rings' space, once every wave is done with its ring)
+    const float lrow = row4_sum(l);
+    __syncthreads();
+    float (*red_o)[DB][4][64] = (float (*)[DB][4][64])lds;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red_o[w][db][i][lane] = o[db][i];
+    if (lane < kDecMfmaRows) {
+        red_ml[w][lane][0] = m;
+        red_ml[w][lane][1] = lrow;
+    }
+    __syncthreads();
+    const int64_t slot0 = (int64_t)r * a.max_q_len;
+    for (int item = threadIdx.x; item < kDecMfmaRows * D; item += 256) {
+        const int tr = item / D, c = item % D;
+        const int pi = tr / G, pg = tr % G;
+        if (pi >= ql) break;            // rows are ascending in item
+        float M = -INFINITY;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) M = fmaxf(M, red_ml[x][tr][0]);
+        const float Ms = (M == -INFINITY) ? 0.f : M * c2;
+        float L = 0.f, acc = 0.f;
+        const int src_lane = tr + 16 * ((c & 15) >> 2);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const float mx = red_ml[x][tr][0];
+            const float sc = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx * c2 - Ms);
+            L += sc * red_ml[x][tr][1];
+            acc += sc * red_o[x][c >> 4][c & 3][src_lane];
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float lse = L > 0.f ? (Ms + __log2f(L)) * kLn2 : -INFINITY;
+        const int h = hk * G + pg;
+        const int64_t row = prow0 + pi;
+        if (nsplit == 1) {
+            ((__bf16*)a.o)[(row * a.H + h) * D + c] = (__bf16)(acc * inv);
+            if (a.lse && c == 0) a.lse[row * a.H + h] = lse;
+        } else {
+            const int64_t slot = ((slot0 + pi) * a.H + h) * a.max_splits + split;
+            a.ws_o[slot * D + c] = acc * inv;
+            if (c == 0) a.ws_lse[slot] = lse;
+        }
+    }
+}
+
+// ============================================================================
 // Chunked-prefill kernel: the bf16 MFMA tile driver with K/V rows fetched
 // through the block table.  One workgroup per (request, 128-row query tile,
 // head, split); query tiles of one (request, head, split) are adjacent in the
@@ -370,19 +644,26 @@ struct PagedKV {
 constexpr int kChunkPairsPerXcd = 4;
 enum { kMapRanges = 0, kMapPairs = 1, kMapItems = 2 };
 
-// NW = 4: 128-row query tiles, the plain key loop, three workgroups per CU;
-// NW = 8: 256-row query tiles, the pipelined key loop (attn_mfma_pipe.h), one
-// workgroup per CU, each K/V tile staged once for 256 rows.
-template <int D, int BS, int NW>
-__global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void paged_chunk_kernel(PagedArgs a, int n_work, int map)
+// KIND 0: 128-row query tiles, the plain key loop, three workgroups per CU;
+// KIND 1: 128-row query tiles, the pipelined key loop (attn_mfma_pipe.h), two
+// workgroups per CU; KIND 2: 256-row query tiles of eight waves, the
+// pipelined loop, one workgroup per CU, each K/V tile staged once for 256
+// rows.
+template <int KIND>
+constexpr int chunk_waves() { return KIND == 2 ? 8 : 4; }
+
+template <int D, int BS, int KIND>
+__global__ __launch_bounds__(64 * chunk_waves<KIND>(), KIND == 0 ? 3 : (KIND == 1 ? 2 : 1))
+void paged_chunk_kernel(PagedArgs a, int n_work, int map)
 {
     using C = TileCfg<D>;
+    constexpr int NW = chunk_waves<KIND>();
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
     __shared__ int32_t ptab[kChunkMaxSplit / BS];
     const TileBuffers buf{lds0, lds1};
     PipeBuffers pbuf{{lds0, lds1, nullptr, nullptr}};
-    if constexpr (NW == 8) {
+    if constexpr (KIND != 0) {
         __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
         __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
         pbuf.b[2] = lds2;
@@ -421,7 +702,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void paged_chunk_kernel(P
     }
     const int hk = pair % a.H_kv;
     const int r = pair / a.H_kv;
-    const int ctx = req_ctx(a, r), ql = a.q_lens[r];
+    const int ctx = req_ctx(a, r), ql = req_ql(a, r);
     if (qt * ppt >= ql) return;
     const int S = a.split_tokens;
     const int nsplit = (ctx + S - 1) / S;
@@ -473,7 +754,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 3 : 1) void paged_chunk_kernel(P
         out.lse_hstride = a.max_splits;
         out.fp32_out = 1;
     }
-    if constexpr (NW == 8) run_pipe_tile<D, NW>(P, kv, out, a.scale * kLog2e, pbuf);
+    if constexpr (KIND != 0) run_pipe_tile<D, NW>(P, kv, out, a.scale * kLog2e, pbuf);
     else run_query_tile<D>(P, kv, out, a.scale * kLog2e, buf);
 }
 
@@ -670,9 +951,18 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     const int G = H / H_kv;
     // The vector decode kernel serves short queries of plain or lightly
     // grouped heads; from groups of kDecodeMfmaGroup heads up, the group's
-    // rows make the MFMA tile kernel the better fit even for one query row.
-    p.path = (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup) ? 0 : 1;
-    if ((opts.paged_path == 0 && max_q_len <= kDecodeMaxQ) || opts.paged_path == 1) p.path = opts.paged_path;
+    // rows go to the matrix cores: for batches of many (request, K/V head)
+    // pairs the decode MFMA kernel, while the rows fit its 16, else the tile
+    // kernel.  (Decode on 32 query heads / 4 K/V heads, contexts U[512,16384],
+    // 16-token pages, TB/s for the tile kernel / the decode MFMA kernel: 64
+    // requests 4.90 / 4.72, 256 requests 4.76 / 5.32, 512 requests 5.13 /
+    // 5.22.)
+    const bool dec_rows = (int64_t)max_q_len * G <= kDecMfmaRows;
+    p.path = (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup) ? 0
+           : ((dec_rows && (int64_t)num_seqs * H_kv >= kDecMfmaMinPairs) ? 2 : 1);
+    if ((opts.paged_path == 0 && max_q_len <= kDecodeMaxQ) || opts.paged_path == 1 ||
+        (opts.paged_path == 2 && dec_rows))
+        p.path = opts.paged_path;
     const int64_t rows = (int64_t)num_seqs * max_q_len;
     // decode workgroups serve gc query heads of one K/V group (the largest of
     // 8, 4, 2, 1 that divides the group; at most 4 with 32-token pages, whose
@@ -701,17 +991,31 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         while (S > s_min && items * ((max_ctx_len + S - 1) / S) < 4096) S /= 2;
         if (S < s_min) S = s_min;
         p.nqt = 1;
-        p.tile_waves = 4;
+        p.tile_kernel = 0;
+    } else if (p.path == 2) {
+        // decode MFMA kernel: 4 waves x 4 tiles of 16 keys, doubled while the
+        // batch keeps the chip busy, up to 64 pages (the block-table entries
+        // of a split sit in one register) and 1024 keys
+        const int64_t items = (int64_t)num_seqs * H_kv;
+        S = 256;
+        const int s_max = min(64 * block_size, 1024);
+        while (S < s_max && items * ((max_ctx_len + 2 * S - 1) / (2 * S)) >= 2048) S *= 2;
+        p.nqt = 1;
+        p.tile_kernel = 0;
     } else {
-        // 128-row workgroups (four waves, the plain key loop, three per CU)
-        // unless asked for 256 rows (eight waves, the pipelined loop, one per
-        // CU), which read each K/V tile once for twice the rows but keep the
-        // matrix cores less busy.  8 x 512-row chunks on 32 heads, contexts
-        // of 9-33K keys: 128 rows 949 TFLOP/s with K/V fetched 1.27x the
+        // The plain key loop on 128-row workgroups (three per CU) unless asked
+        // otherwise.  256-row workgroups (eight waves, the pipelined loop, one
+        // per CU) read each K/V tile once for twice the rows but keep the
+        // matrix cores less busy: 8 x 512-row chunks on 32 heads, contexts
+        // of 9-33K keys, 128 rows 949 TFLOP/s with K/V fetched 1.27x the
         // algorithmic bytes (the four tiles of a request share it in L2 in
         // part), 256 rows 879 TFLOP/s at 1.00x.
-        p.tile_waves = (opts.paged_tile_rows == 256) ? 8 : 4;
-        const int ppt = 32 * p.tile_waves / G;         // query positions per tile
+        // Decode-length rows (one wave of the workgroup has rows) take the
+        // pipelined loop: two workgroups per CU with two tiles in flight each
+        // keep more K/V in flight than three with one (64 requests, 32 query
+        // heads on 4 K/V heads: 4.92 against 4.76 TB/s).
+        p.tile_kernel = (opts.paged_tile_kernel >= 0) ? opts.paged_tile_kernel : (max_q_len <= kDecodeMaxQ ? 1 : 0);
+        const int ppt = (p.tile_kernel == 2 ? 2 * kTileRows : kTileRows) / G;   // query positions per tile
         p.nqt = (max_q_len + ppt - 1) / ppt;
         // the split plan counts 128-row tiles whatever the workgroup size, so
         // both sizes split the context alike (and give the same bits)
@@ -732,11 +1036,13 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         S = (int)(s < 1024 ? 1024 : (s > 8192 ? 8192 : s));
     }
     if (opts.paged_split_tokens > 0) S = opts.paged_split_tokens;
-    // a tile-path workgroup stages its split's block-table entries in LDS
+    // a tile-path workgroup stages its split's block-table entries in LDS, a
+    // decode-MFMA wave holds them in one register
     if (p.path == 1 && S > kChunkMaxSplit) S = kChunkMaxSplit;
-    // whole pages; on the MFMA path a multiple of 64 keys (whole pages of 16
+    if (p.path == 2 && S > 64 * block_size) S = 64 * block_size;
+    // whole pages; on the tile path a multiple of 64 keys (whole pages of 16
     // or 32 tokens, so every split starts on a page boundary)
-    const int unit = (p.path == 0) ? block_size : (block_size > 64 ? block_size : 64);
+    const int unit = (p.path != 1) ? block_size : (block_size > 64 ? block_size : 64);
     S = ((S + unit - 1) / unit) * unit;
     p.split_tokens = S;
     p.max_splits = (max_ctx_len + S - 1) / S;
@@ -754,7 +1060,11 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
 template <int D, int BS>
 static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
 {
-    if (plan.path == 0) {
+    if (plan.path == 2) {
+        const int64_t grid = (int64_t)a.num_seqs * a.H_kv * a.max_splits;
+        if (grid > (int64_t)INT32_MAX) return -2;
+        hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
+    } else if (plan.path == 0) {
         const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H_kv * plan.n_chunks * a.max_splits;
         if (grid > (int64_t)INT32_MAX) return -2;
         const dim3 g((unsigned)grid), b(256);
@@ -771,11 +1081,14 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         const int64_t grid = (map == kMapPairs) ? (pairs + 7) / 8 * 8 * per_pair
                            : (map == kMapRanges) ? (n_work + 7) / 8 * 8 : n_work;
         if (grid > (int64_t)INT32_MAX) return -2;
-        if (plan.tile_waves == 8)
-            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 8>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+        if (plan.tile_kernel == 2)
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a,
+                               (int)n_work, map);
+        else if (plan.tile_kernel == 1)
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 1>), dim3((unsigned)grid), dim3(256), 0, stream, a,
                                (int)n_work, map);
         else
-            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 4>), dim3((unsigned)grid), dim3(256), 0, stream, a,
+            hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a,
                                (int)n_work, map);
     }
     if (a.max_splits > kCombineHeadsMaxSplits) {
