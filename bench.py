@@ -47,7 +47,7 @@ KERNEL_SOURCES = {
     "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "prefill_gfx950.hip",
                    "attn_internal.h"],
     "decode_c4": ["paged_gfx950.hip", "attn_internal.h"],
-    "chunk_c5": ["attn_mfma_core.h", "attn_mfma_kernel.h", "paged_gfx950.hip", "attn_internal.h"],
+    "chunk_c5": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "paged_gfx950.hip", "attn_internal.h"],
     "bwd_c3": ["attn_mfma_core.h", "bwd_gfx950.hip", "bwd_internal.h"],
 }
 
@@ -348,7 +348,7 @@ def bench_bwd(args):
                  "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                               "traffic": read_traffic("bwd_c3") if key == "mha" else None,
-                              "kernels": "bwd_dq_kernel<128> + bwd_dkdv_kernel<128>",
+                              "kernels": "bwd_dq_kernel<128, true> + bwd_dkdv_kernel<128, true>",
                               "flops_per_launch": fl,
                               "executed_flops_per_launch": fl * 7 / 5,
                               "algorithmic_bytes_per_launch": bwd_bytes(cfg.B, cfg.H, cfg.N, cfg.d,
@@ -502,7 +502,7 @@ KERNELS = {
     "c3": "prefill_bf16_kernel<128, true, 0>",
     "c2": "prefill_bf16_kernel<128, false, 1>",
     "c4": "paged_decode_kernel<128, 16, 1> + paged_combine_kernel<128>",
-    "c5": "paged_chunk_kernel<128, 32> + paged_combine_heads_kernel<128>",
+    "c5": "paged_chunk_kernel<128, 32, 0> + paged_combine_heads_kernel<128>",
 }
 
 
