@@ -23,8 +23,8 @@
 //                    through LDS.  Each 32-key block has two waves: the P wave
 //                    (its keys' K in registers) computes S and P, passes P on
 //                    through LDS and accumulates dV^T += dO^T P; the dS wave
-//                    (V in registers) computes dP, then dS = P (dP - D), and
-//                    accumulates dK^T += Q^T dS.
+//                    (V in registers), one query tile behind, computes dP,
+//                    then dS = P (dP - D), and accumulates dK^T += Q^T dS.
 // Computing dQ apart from dK/dV costs a second recomputation of S and dP (7
 // matrix products per (query tile, key tile) pair instead of 5) and saves a
 // float atomic read-modify-write of dQ for every such pair.
@@ -222,6 +222,39 @@ __device__ __forceinline__ void run_tiles(char* b0, char* b1, int tb, int te, in
         step(b0, t);
         publish_copies();
     }
+}
+
+// Runs tiles [tb, te) of a stream of nt tiles in three buffers (tile t lives
+// in buffer t % 3) for the two wave roles of the dK/dV kernel: the step of
+// tile t issues the copies of tile t + 1 (into the buffer of tile t - 2,
+// which both roles were done with at the last barrier), runs p(t) (the P
+// waves) and d(t - 1) (the dS waves, one tile behind, reading the P the P
+// waves left in the previous step), and ends with "wait for my copies,
+// barrier", which publishes tile t + 1 and this step's P.  One barrier per
+// tile.  On entry tile tb has been published.  Buffers are chosen
+// statically (unrolled by three, the first tiles peeled to a multiple of
+// three), so LDS reads of one buffer are never ordered behind copies in
+// flight into another.
+template <class Issue, class PStep, class DStep>
+__device__ __forceinline__ void run_tiles_lag(char* b0, char* b1, char* b2, int tb, int te, int nt,
+                                              const Issue& issue, const PStep& p, const DStep& d)
+{
+    const auto one = [&](char* bc, char* bp, char* bn, int t) {
+        if (t + 1 < nt) issue(bn, t + 1);
+        p(bc, t);
+        if (t > 0) d(bp, t - 1);
+        publish_copies();
+    };
+    int t = tb;
+    if (t < te && t % 3 == 1) one(b1, b0, b2, t++);
+    if (t < te && t % 3 == 2) one(b2, b1, b0, t++);
+    for (; t + 3 <= te; t += 3) {
+        one(b0, b2, b1, t);
+        one(b1, b0, b2, t + 1);
+        one(b2, b1, b0, t + 2);
+    }
+    if (t < te) one(b0, b2, b1, t++);
+    if (t < te) one(b1, b0, b2, t++);
 }
 
 // ---------------------------------------------------------------------------
@@ -422,15 +455,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a, int n_work)
 // 4 + k its dS wave (the hardware puts both on SIMD k).  With one wave per
 // key block holding K, V, dK and dV (~350 registers) only one wave fits a
 // SIMD and nothing hides its exponentials; split in two, two waves fit.
-// Per 32-query tile:
-//   P wave : S = Q K^T, P = exp2(s c2 - lse2) (masked), P to LDS (bf16),
-//            dV^T += dO^T P
-//   dS wave: dP = dO V^T; after the barrier that publishes P,
-//            dS = P (dP - D), dK^T += Q^T dS
-// Each wave holds half the stationary state (K or V, dV or dK), which leaves
-// room for two waves per SIMD: one's exponentials or dS run beside the
-// other's MFMAs.  The workspace rows are planar here: lse2 of a head's N rows,
-// then D of its N rows.
+// Per 32-query tile t:
+//   P wave : S = Q K^T, P = exp2(s c2 - lse2) (masked), P to an LDS exchange
+//            slot (bf16), dV^T += dO^T P
+//   dS wave, one tile behind (tile t - 1, whose P the barrier ending the
+//            previous step published): dP = dO V^T, dS = P (dP - D),
+//            dK^T += Q^T dS
+// so a tile step has one barrier (three tile buffers and two exchange slots;
+// run_tiles_lag), and the two waves of a SIMD never wait for each other
+// inside it.  Each wave holds half the stationary state (K or V, dV or dK),
+// which leaves room for two waves per SIMD: one's exponentials or dS run
+// beside the other's MFMAs.  The workspace rows are planar here: lse2 of a
+// head's N rows, then D of its N rows.
 constexpr int kRoleKB = 4;                     // 32-key blocks per workgroup
 constexpr int kRoleWaves = 2 * kRoleKB;
 
@@ -453,8 +489,9 @@ struct RoleCfg {
     static constexpr int XCH_BYTES = 64 * 32;                       // P of one key block: 16 bf16 per lane
 };
 
-// P wave, one tile: S = Q K^T, P to LDS, the barrier that publishes it,
-// then dV^T += dO^T P.
+// P wave, one tile: S = Q K^T, P to its exchange slot in LDS (read by the
+// dS wave one step later, after the barrier that ends this step), then
+// dV^T += dO^T P.
 template <int D, bool MASKED>
 __device__ __forceinline__ void role_p_tile(f32x16 (&dv)[BwdCfg<D>::DBLK], const bf16x8 (&kf)[BwdCfg<D>::KSTEPS],
                                             const char* buf, char* xch, const LaneOfs<D>& lo, int lane, float c2,
@@ -503,7 +540,6 @@ __device__ __forceinline__ void role_p_tile(f32x16 (&dv)[BwdCfg<D>::DBLK], const
     }
     *(bf16x8*)(xch + lane * 32) = cat8(pk[0], pk[1], pk[2], pk[3]);
     *(bf16x8*)(xch + lane * 32 + 16) = cat8(pk[4], pk[5], pk[6], pk[7]);
-    __syncthreads();   // P of this tile is visible to the dS wave
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const bf16x8 bp = cat8(pk[4 * h + 0], pk[4 * h + 1], pk[4 * h + 2], pk[4 * h + 3]);
@@ -512,8 +548,8 @@ __device__ __forceinline__ void role_p_tile(f32x16 (&dv)[BwdCfg<D>::DBLK], const
     }
 }
 
-// dS wave, one tile: dP = dO V^T, the barrier after which P is in LDS,
-// dS = P (dP - D), dK^T += Q^T dS.
+// dS wave, one tile (the tile the P wave took one step earlier, whose P is
+// in xch): dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS.
 template <int D>
 __device__ __forceinline__ void role_ds_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], const bf16x8 (&vf)[BwdCfg<D>::KSTEPS],
                                              const char* buf, const char* xch, const LaneOfs<D>& lo, int lane)
@@ -543,7 +579,6 @@ __device__ __forceinline__ void role_ds_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], cons
 #pragma unroll
     for (int a4 = 0; a4 < 4; ++a4) dd[a4] = *(const f32x4*)(st + 32 + a4 * 8 + 4 * g);
     __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();   // the P wave's P of this tile is in xch
     const u32x4 p0 = *(const u32x4*)(xch + lane * 32);
     const u32x4 p1 = *(const u32x4*)(xch + lane * 32 + 16);
     const uint32_t pw[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
@@ -572,7 +607,7 @@ __device__ __forceinline__ void role_ds_tile(f32x16 (&dk)[BwdCfg<D>::DBLK], cons
 // body of bwd_dkdv_kernel; a paired workgroup runs it for two blocks).
 template <int D>
 __device__ __forceinline__ void dkdv_key_block(const BwdArgs& a, int bhk, int k0, char* lds0, char* lds1,
-                                               char* xch_all)
+                                               char* lds2, char* xch_all)
 {
     using C = BwdCfg<D>;
     using R = RoleCfg<D>;
@@ -589,7 +624,8 @@ __device__ __forceinline__ void dkdv_key_block(const BwdArgs& a, int bhk, int k0
     const int key = k0 + 32 * kb + r32;                     // this lane's key
     const bool kvalid = key < N;
     const float c2 = fmaxf(a.scale * kLog2e, 1e-30f);
-    char* xch = xch_all + kb * R::XCH_BYTES;
+    // P of tile t goes to exchange slot t % 2
+    const auto xch = [&](int t) { return xch_all + ((t & 1) * KB + kb) * R::XCH_BYTES; };
 
     // K (P wave) or V (dS wave) fragments of the lane's key
     bf16x8 kvf[C::KSTEPS];
@@ -626,13 +662,13 @@ __device__ __forceinline__ void dkdv_key_block(const BwdArgs& a, int bhk, int k0
     auto q_of = [&](int t) { return (qt0 + t % per_head) * 32; };
     const LaneOfs<D> lo = lane_offsets<D>(lane);
     auto p_full = [&](const char* buf, int t) {
-        role_p_tile<D, false>(acc, kvf, buf, xch, lo, lane, c2, q_of(t), key, N, a.causal);
+        role_p_tile<D, false>(acc, kvf, buf, xch(t), lo, lane, c2, q_of(t), key, N, a.causal);
     };
     auto p_masked = [&](const char* buf, int t) {
-        role_p_tile<D, true>(acc, kvf, buf, xch, lo, lane, c2, q_of(t), key, N, a.causal);
+        role_p_tile<D, true>(acc, kvf, buf, xch(t), lo, lane, c2, q_of(t), key, N, a.causal);
     };
-    auto ds_step = [&](const char* buf, int) { role_ds_tile<D>(acc, kvf, buf, xch, lo, lane); };
-    auto none = [&](const char*, int) { __syncthreads(); };
+    auto ds_step = [&](const char* buf, int t) { role_ds_tile<D>(acc, kvf, buf, xch(t), lo, lane); };
+    auto none = [&](const char*, int) {};
     const int n_head_masked = a.causal ? min(KB, per_head) : 0;
     const int n_tail_masked = (N % 32 != 0 && per_head - 1 >= n_head_masked) ? 1 : 0;
     if (nt > 0) {
@@ -640,16 +676,26 @@ __device__ __forceinline__ void dkdv_key_block(const BwdArgs& a, int bhk, int k0
         publish_copies();
     }
     if (k0 + 32 * kb >= N) {
-        run_tiles(lds0, lds1, 0, nt, nt, issue, none);
+        run_tiles_lag(lds0, lds1, lds2, 0, nt, nt, issue, none, none);
     } else if (p_role) {
         for (int gh = 0; gh < G; ++gh) {
             const int tb = gh * per_head;
-            run_tiles(lds0, lds1, tb, tb + n_head_masked, nt, issue, p_masked);
-            run_tiles(lds0, lds1, tb + n_head_masked, tb + per_head - n_tail_masked, nt, issue, p_full);
-            run_tiles(lds0, lds1, tb + per_head - n_tail_masked, tb + per_head, nt, issue, p_masked);
+            run_tiles_lag(lds0, lds1, lds2, tb, tb + n_head_masked, nt, issue, p_masked, none);
+            run_tiles_lag(lds0, lds1, lds2, tb + n_head_masked, tb + per_head - n_tail_masked, nt, issue, p_full,
+                          none);
+            run_tiles_lag(lds0, lds1, lds2, tb + per_head - n_tail_masked, tb + per_head, nt, issue, p_masked,
+                          none);
         }
     } else {
-        run_tiles(lds0, lds1, 0, nt, nt, issue, ds_step);
+        run_tiles_lag(lds0, lds1, lds2, 0, nt, nt, issue, none, ds_step);
+        // the last tile's dS step (its P was published by the last barrier;
+        // no copies are in flight and nothing overwrites its buffer)
+        if (nt > 0) {
+            const int t = nt - 1;
+            if (t % 3 == 0) ds_step(lds0, t);
+            else if (t % 3 == 1) ds_step(lds1, t);
+            else ds_step(lds2, t);
+        }
     }
 
     if (kvalid) {
@@ -677,16 +723,17 @@ __global__ __launch_bounds__(64 * kRoleWaves, 1) void bwd_dkdv_kernel(BwdArgs a,
     constexpr int KB = kRoleKB, BLK = 32 * KB;
     __shared__ __attribute__((aligned(16))) char lds0[R::BUF_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[R::BUF_BYTES];
-    __shared__ __attribute__((aligned(16))) char xch_all[KB * R::XCH_BYTES];
+    __shared__ __attribute__((aligned(16))) char lds2[R::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char xch_all[2 * KB * R::XCH_BYTES];
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
     if (L >= n_work) return;
     const int nkb = (a.N + BLK - 1) / BLK;
     const int per = PAIR ? (nkb + 1) / 2 : nkb;
     const int bhk = L / per, t = L % per;
-    dkdv_key_block<D>(a, bhk, t * BLK, lds0, lds1, xch_all);
+    dkdv_key_block<D>(a, bhk, t * BLK, lds0, lds1, lds2, xch_all);
     if (PAIR && t != nkb - 1 - t) {
         __syncthreads();   // LDS reuse across the two blocks
-        dkdv_key_block<D>(a, bhk, (nkb - 1 - t) * BLK, lds0, lds1, xch_all);
+        dkdv_key_block<D>(a, bhk, (nkb - 1 - t) * BLK, lds0, lds1, lds2, xch_all);
     }
 }
 
