@@ -83,6 +83,24 @@ def test_bwd_matches_oracle(B, H, H_kv, N, d, causal):
     check_grad("dv", dv, rv)
 
 
+@pytest.mark.parametrize("N", [32, 64, 96, 160, 224, 250])
+@pytest.mark.parametrize("H,H_kv", [(2, 2), (6, 2)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_tile_stream_lengths(N, H, H_kv, causal):
+    """The dK/dV loop runs its query-tile stream through three LDS buffers
+    with the dS waves one tile behind: streams of 1, 2, 3, 5, 7 and 8 tiles
+    per query head (every remainder modulo three, with and without a ragged
+    last tile), one and three query heads per K/V head (each head's range of
+    the stream starting at another buffer), causal and not."""
+    cfg = inputs.PrefillConfig("bwd_len", 1, H, N, 128, torch.bfloat16, causal, 40 + N + H, H_kv=H_kv)
+    log("bwd tile stream N=%d H=%d H_kv=%d causal=%d" % (N, H, H_kv, causal))
+    (q, k, v, do), (dq, dk, dv) = run(cfg)
+    rq, rk, rv = oracle.attention_bwd(q, k, v, do, cfg.scale, causal)
+    check_grad("dq", dq, rq)
+    check_grad("dk", dk, rk)
+    check_grad("dv", dv, rv)
+
+
 def test_bwd_single_key_closed_form():
     """N = 1: P = 1, so dV = dO summed over the group and dQ = dK = 0 (up to
     the fp32 rounding of dP - D, two sums of the same 128 products)."""
