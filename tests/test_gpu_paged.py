@@ -344,3 +344,19 @@ def test_context_above_bound_reads_as_bound():
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, clamped, pi.q_lens, 16, pi.scale)
     check_close("ctx above bound", o, o_ref, lse, l_ref, torch.bfloat16)
 
+
+@pytest.mark.parametrize("H,H_kv", [(8, 8), (32, 4)])
+def test_long_context_decode(H, H_kv):
+    """Decode over very long contexts (262144 and 100003 tokens, 16-token
+    pages scattered over the pool): hundreds of splits per row, so the
+    combine walks its split partials in several batches of 64; plain heads
+    (vector decode kernel) and eight query heads per K/V head (MFMA tile
+    kernel).  Every row against the oracle."""
+    ctx = [262144, 100003]
+    pi = inputs.build_paged(ctx, [1, 1], H_kv, 128, 16, 91 + H, DEV, H_q=H)
+    log("long decode H=%d H_kv=%d ctx=%s" % (H, H_kv, ctx))
+    o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
+                                          pi.scale)
+    check_close("long decode", o, o_ref, lse, l_ref, torch.bfloat16)

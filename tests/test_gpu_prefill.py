@@ -142,6 +142,30 @@ def test_deterministic_and_pair_independent(N):
         assert torch.equal(o1, o3) and torch.equal(l1, l3)
 
 
+@pytest.mark.parametrize("N,H,H_kv,causal", [(131072, 1, 1, True), (65536, 4, 1, True), (65536, 2, 2, False)])
+def test_long_context_sampled_rows(N, H, H_kv, causal):
+    """Long contexts in the default launch configuration: 512 or 1024 query
+    tiles against up to 4096 key tiles of one head (the first row's single key
+    and the last row's full sum of fp32 probabilities both in the sample),
+    four query heads on one K/V head, and a non-causal case.  32 seeded
+    rows plus edge rows against the oracle."""
+    cfg = inputs.PrefillConfig("long", 1, H, N, 128, torch.bfloat16, causal, 7 + N + H, H_kv=H_kv)
+    log("long context N=%d H=%d H_kv=%d causal=%d" % (N, H, H_kv, causal))
+    q, k, v = inputs.prefill_inputs(cfg, DEV)
+    o, lse = attn.prefill(q, k, v, causal, cfg.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    trip = inputs.sample_triples(cfg.seed, 32, (1, H, N),
+                                 edge=[(0, 0, 0), (0, 0, 1), (0, H - 1, 127), (0, H - 1, 128), (0, 0, N - 128),
+                                       (0, H - 1, N - 1)])
+    qs, ks, vs = q.cpu(), k.cpu(), v.cpu()
+    o_ref, l_ref = oracle.attention_rows(qs, ks, vs, cfg.scale, causal, [0] * len(trip), [h for _, h, _ in trip],
+                                         [r for _, _, r in trip])
+    og = torch.stack([o[0, h, r] for _, h, r in trip])
+    lg = torch.stack([lse[0, h, r] for _, h, r in trip])
+    check_close("long", og, o_ref, lg, l_ref, torch.bfloat16)
+
+
 def test_scale_zero_closed_form():
     """scale 0: O_i = mean of V[0..i], LSE_i = ln(i+1)."""
     cfg = inputs.PrefillConfig("s0", 1, 2, 300, 128, torch.bfloat16, True, 10)
