@@ -29,6 +29,11 @@ row's mean error is a few thousandths of its rms (C3: about 3.5e-3), and
 margin catches.  The floor is 1e-3 of the smallest row rms of the workloads
 (~0.009 at 33K keys).  The LSE margin is five times the score-rounding bound
 above; with random inputs the fp32 sum contributes about sqrt(n) u ~ 1e-5.
+The long-context cases (up to 262144 keys in one row) are past the length
+for which the worst case (n - 1) u of the fp32 sum stays under the LSE bound
+(it reaches 1.6e-2 there); the rounding errors of a sum of positive terms
+that are not adversarially ordered grow like sqrt(n) u (~3e-5 at 262144),
+and those cases are held to the same bounds and margins.
 """
 from __future__ import annotations
 
