@@ -78,7 +78,7 @@ enum {
  * bit-identical results; the others change only the floating-point summation
  * order (each is checked against the oracle like the default).
  *
- *   prefill_kernel : -1 auto; 0 the plain key loop (two LDS buffers, three
+ *   prefill_kernel : -1 auto; 0 the plain key loop (three LDS buffers, three
  *                    workgroups per CU); 1 the software-pipelined key loop
  *                    (four LDS buffers, two workgroups per CU) [same bits].
  *   prefill_pair   : -1 auto; 0 one 128-row query tile per workgroup; 1

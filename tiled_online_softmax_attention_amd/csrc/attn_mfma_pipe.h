@@ -206,7 +206,7 @@ __device__ __forceinline__ void issue_tile_copies_flat(const KV& kv, const WaveC
 // data that the mask removes), so no copy reads outside the context; when the
 // whole group lies past kv_end every row is that row, in the page looked up.
 // K and V differ only in which lane fetches which row and 16-byte chunk (the
-// layouts of issue_tile_copies), so both go through the same branch-free code.
+// layouts of k_dma_row / v_dma_row), so both go through the same branch-free code.
 template <int D, int NW, int BS>
 __device__ __forceinline__ void issue_tile_copies_paged(const char* kbase, const char* vbase, int64_t blk_bytes,
                                                         const WaveCtx& cx, char* buf, int key_base, int page)

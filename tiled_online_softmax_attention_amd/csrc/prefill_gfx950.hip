@@ -3,7 +3,7 @@
 //  * bf16: fused MFMA kernel, one workgroup of 4 waves per 128-row query tile
 //    (or per pair of tiles, see below), K/V streamed through LDS in 32-key
 //    tiles, causal key tiles above the diagonal never loaded.  Two key loops:
-//    the plain one of attn_mfma_kernel.h (two LDS buffers, three workgroups
+//    the plain one of attn_mfma_kernel.h (three LDS buffers, three workgroups
 //    per CU) for grids of several dispatch rounds, and the software-pipelined
 //    one of attn_mfma_pipe.h (four LDS buffers, two workgroups per CU) for
 //    grids of about one round, whose few waves per SIMD need the MFMA and
@@ -44,9 +44,9 @@
 
 namespace attn {
 
-// K/V rows of one head of a contiguous [B, H, N, d] tensor.  The head slab is
-// one group: row offsets are absolute (N * d * 2 < 4 GiB is checked on the
-// host), clamped to the last row of the context.
+// K/V rows of one head of a contiguous [B, H, N, d] tensor: the copies
+// address the head slab from its base (N * d * 2 < 4 GiB is checked on the
+// host), and the descriptor's range check returns zero for rows past N.
 template <int D>
 struct ContigKV {
     const char* k;   // head base (bytes)
@@ -55,8 +55,7 @@ struct ContigKV {
     __device__ __forceinline__ uint32_t group_bytes() const { return head_bytes; }
     __device__ __forceinline__ const char* k_group(int, int) const { return k; }
     __device__ __forceinline__ const char* v_group(int, int) const { return v; }
-    __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1); }
-    // copies of the pipelined key loop: nothing to look up per tile
+    // copies of the key loops: nothing to look up per tile
     struct SrcWin {};
     __device__ __forceinline__ SrcWin empty_win() const { return SrcWin{}; }
     __device__ __forceinline__ void win_update(SrcWin&, const WaveCtx&, int, int) const {}
@@ -76,7 +75,7 @@ __device__ __forceinline__ int xcd_linear_id(int bid, int grid)
     return (bid & 7) * per + (bid >> 3);
 }
 
-// KIND 0: the plain key loop (attn_mfma_kernel.h: two LDS buffers, three
+// KIND 0: the plain key loop (attn_mfma_kernel.h: three LDS buffers, three
 // workgroups per CU).  KIND 1: the software-pipelined key loop of
 // attn_mfma_pipe.h (four LDS buffers, two workgroups per CU).  (Eight waves
 // on 256-row tiles, one workgroup per CU, each K/V tile copied once for 256
@@ -91,12 +90,11 @@ __global__ __launch_bounds__(256, KIND == 0 ? 3 : 2) void prefill_bf16_kernel(Pr
     constexpr int BM = kTileRows;
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
-    const TileBuffers buf{lds0, lds1};
-    PipeBuffers pbuf{{lds0, lds1, nullptr, nullptr}};
+    __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
+    const TileBuffers buf{lds0, lds1, lds2};
+    PipeBuffers pbuf{{lds0, lds1, lds2, nullptr}};
     if constexpr (PIPE) {
-        __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
         __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
-        pbuf.b[2] = lds2;
         pbuf.b[3] = lds3;
     }
     const int L = xcd_linear_id(blockIdx.x, gridDim.x);
