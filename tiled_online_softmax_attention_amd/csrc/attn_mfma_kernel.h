@@ -1,28 +1,41 @@
 // attn_mfma_kernel.h -- the per-workgroup driver of the bf16 MFMA attention
 // forward: loads the query tile into registers, streams 32-key K/V tiles into
-// LDS with direct global->LDS copies issued two tiles ahead (three LDS
-// buffers, one barrier per tile; each tile's copies go out after the S MFMAs
-// of the tile two before), runs the online-softmax tile step of
-// attn_mfma_core.h, and writes O (bf16, or fp32 partials) and the
-// log-sum-exp.  The source of K/V rows is a policy object, so the same driver
-// serves contiguous K/V ([B,H,N,d]) and the paged pool.
+// LDS with direct global->LDS copies (one barrier per tile; each tile's
+// copies go out after the S MFMAs of an earlier tile), runs the
+// online-softmax tile step of attn_mfma_core.h, and writes O (bf16, or fp32
+// partials) and the log-sum-exp.  The source of K/V rows is a policy object,
+// so the same driver serves contiguous K/V ([B,H,N,d]) and the paged pool.
+// Two copy schedules, chosen by the source's kCopiesAhead:
+//   2: three LDS buffers, copies two tiles ahead (contiguous K/V);
+//   1: two LDS buffers, copies one tile ahead (the paged pool, where copies
+//      two tiles ahead were measured to fetch ~1.8x the pool bytes from
+//      memory, against 1.14x, and to run no faster).
 //
-// K/V source policy interface (all members device functions; the copy
-// helpers they call are in attn_mfma_pipe.h, whose key loop uses the same
-// interface):
-//   SrcWin, SrcWin empty_win()
-//       a small per-wave state that locates the rows of a range of keys
-//       (empty for a contiguous slab, a window of page-table entries for the
-//       paged pool).
-//   void win_update(SrcWin&, const WaveCtx&, int key_lo, int key_hi)
-//       make the state cover the copies of keys [key_lo, key_hi].
-//   int copy_src(const SrcWin&, const WaveCtx&, int key_base)
-//       what this wave's copies of the tile at key_base need (no memory access).
-//   template <int NW> void copy_tile(const WaveCtx&, char* buf, int key_base, int src)
-//       this wave's share (of NW waves) of the branch-free copies of the tile
-//       at key_base into buf: K at byte 0, V at TILE_BYTES, in the layouts
-//       of attn_mfma_core.h.  Rows at or past kv_end hold data that the mask
-//       removes; no copy reads outside the K/V allocation.
+// K/V source policy interface (all members device functions):
+//   static constexpr int kCopiesAhead (1 or 2, above)
+//   for kCopiesAhead == 2 (the copy helpers are in attn_mfma_pipe.h, whose
+//   key loop uses the same members):
+//     SrcWin, SrcWin empty_win()
+//         a small per-wave state that locates the rows of a range of keys.
+//     void win_update(SrcWin&, const WaveCtx&, int key_lo, int key_hi)
+//         make the state cover the copies of keys [key_lo, key_hi].
+//     int copy_src(const SrcWin&, const WaveCtx&, int key_base)
+//         what this wave's copies of the tile at key_base need.
+//     template <int NW> void copy_tile(const WaveCtx&, char* buf, int key_base, int src)
+//         this wave's share (of NW waves) of the branch-free copies of the
+//         tile at key_base into buf: K at byte 0, V at TILE_BYTES, in the
+//         layouts of attn_mfma_core.h.  Rows at or past kv_end hold data
+//         that the mask removes; no copy reads outside the K/V allocation.
+//   for kCopiesAhead == 1:
+//     const char* k_group(int key, int kv_end) / v_group(...)
+//         wave-uniform base address of the 16-row group holding key
+//         min(key, kv_end - 1); rows of one group are contiguous (ROW_BYTES
+//         apart) in memory, which holds for any page of 16 or 32 tokens
+//         (groups are 16-aligned).
+//     int group_row(int key, int kv_end)
+//         row of key min(key, kv_end - 1) relative to that group base.
+//     uint32_t group_bytes()
+//         bytes addressable from a group base (range of the copy descriptor).
 #pragma once
 
 #include <type_traits>
@@ -64,9 +77,10 @@ struct TileOut {
 // Query rows per workgroup: 4 waves x 32 queries.
 constexpr int kTileRows = 128;
 
-// LDS of one workgroup: three buffers, each holding one K tile then one V
-// tile.  They are distinct __shared__ objects, so reads of one are not
-// ordered behind copies in flight into another.
+// LDS of one workgroup: three buffers (two, b2 unused, for copies one tile
+// ahead), each holding one K tile then one V tile.  They are distinct
+// __shared__ objects, so reads of one are not ordered behind copies in
+// flight into another.
 struct TileBuffers {
     char* b0;
     char* b1;
@@ -91,6 +105,57 @@ struct WaveCtx {
     int kv_begin, kv_end, ntile;
     uint32_t voff;       // this lane's copy source offset within a full group
 };
+
+// Issue this wave's copies of one tile into buffer `buf` (K tile at byte 0, V
+// tile at TILE_BYTES): wave w < GROUPS copies K group w, the others V group
+// w - GROUPS.  Rows at or past kv_end are fetched from row kv_end - 1 (valid
+// data, masked out of S), so no copy reads outside the context.  For a full
+// group the per-lane source offset is loop-invariant (cx.voff) and the
+// group's position goes in the scalar offset.
+template <int D, class KV>
+__device__ __forceinline__ void issue_tile_copies(const KV& kv, const WaveCtx& cx, char* buf, int key_base)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = TileCfg<D>;
+    const bool is_v = cx.w >= C::GROUPS;                      // uniform
+    const int grp = is_v ? cx.w - C::GROUPS : cx.w;
+    const int kv_end = cx.kv_end;
+    const int gkey = key_base + 16 * grp;                     // first key of the group (uniform)
+    const __amdgpu_buffer_rsrc_t r =
+        raw_rsrc(is_v ? kv.v_group(gkey, kv_end) : kv.k_group(gkey, kv_end), kv.group_bytes());
+    char* dst = buf + (is_v ? C::TILE_BYTES : 0) + grp * 16 * C::ROW_BYTES;
+    if (__builtin_expect(gkey + 16 <= kv_end, 1)) {
+        const uint32_t soff = (uint32_t)kv.group_row(gkey, kv_end) * C::ROW_BYTES;
+        const uint32_t step = is_v ? kVDmaStep : kKDmaStep;
+#pragma unroll
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16, cx.voff + i * step, soff, 0,
+                                                     0);
+    } else if (!is_v) {
+        const uint32_t koff = (uint32_t)kv.group_row(gkey + k_dma_row<D>(cx.lane), kv_end) * C::ROW_BYTES +
+                              k_dma_col<D>(cx.lane);
+#pragma unroll
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16, koff + i * kKDmaStep, 0, 0, 0);
+    } else {
+        const uint32_t vcol = v_dma_col<D>(cx.lane);
+#pragma unroll
+        for (int i = 0; i < C::COPIES_PER_GROUP; ++i) {
+            const int vrow = kv.group_row(gkey + i * C::ROWS_PER_DMA + v_dma_row<D>(cx.lane), kv_end);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + i * 1024), 16,
+                                                     (uint32_t)vrow * C::ROW_BYTES + vcol, 0, 0, 0);
+        }
+    }
+#endif
+}
+
+// Copies one tile ahead: wait until this wave's copies have landed, then the
+// barrier that publishes the tile.
+__device__ __forceinline__ void publish_copies()
+{
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+    __syncthreads();
+}
 
 // Wait until this wave's copies of the next tile have landed -- the copies
 // of the tile after it, this wave's last COPIES_PER_GROUP vector-memory
@@ -128,33 +193,36 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
     pv_tile(ws, pk, buf + C::TILE_BYTES, cx.lane);
 }
 
-// The key loop of one wave: tiles [0, n_full) unmasked, the rest masked.
+// The key loops of one wave: tiles [0, n_full) unmasked, the rest masked.
 // COMPUTE false: the wave only copies its share of every tile and joins the
 // barriers (it has no valid query row).
 //
-// Tile j lives in buffer j % 3.  The step of tile j issues the copies of
-// tile j + 2 (into the buffer of tile j - 1, which every wave was done with
-// at the barrier that ended step j - 1), whether or not tile j + 2 exists
-// (rows past the context hold data that no step reads), and ends with "wait
-// until only tile j + 2's copies are in flight, barrier", which publishes
-// tile j + 1: each tile's copies have a step and a half to land.  The copies
+// Copies two tiles ahead.  Tile j lives in buffer j % 3.  The step of tile
+// j issues the copies of tile min(j + 2, nt - 1) (into the buffer of tile
+// j - 1, which every wave was done with at the barrier that ended step
+// j - 1; past the last tile it fetches the last tile again, out of L2,
+// rather than keys beyond the causal limit), and ends with "wait until only
+// those copies are in flight, barrier", which publishes tile j + 1: each
+// tile's copies have a step and a half to land.  The copies
 // are the K/V source's branch-free ones (copy_tile, its source looked up in
 // a window updated once per three tiles), and the buffers are chosen
 // statically (unrolled by three): with a branch in the copies, the compiler
 // orders the next LDS reads behind every copy in flight.
 template <int D, bool COMPUTE, class KV>
-__device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
+__device__ __forceinline__ void key_loop_ahead2(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
                                          const KV& kv, const TileBuffers& buf, int n_full)
 {
     using C = TileCfg<D>;
     const int nt = cx.ntile;
     if (nt == 0) return;
+    const int last_kb = cx.kv_begin + (nt - 1) * C::BN;
     typename KV::SrcWin win = kv.empty_win();
     const auto copy = [&](char* dst, int key_base) {
         kv.template copy_tile<C::kWaves>(cx, dst, key_base, kv.copy_src(win, cx, key_base));
     };
     // the window covers the copies of the three tiles from tile j on
     const auto cover = [&](int j) {
+        j = min(j, nt - 1);
         kv.win_update(win, cx, cx.kv_begin + j * C::BN, cx.kv_begin + (j + 3) * C::BN - 1);
     };
     cover(0);
@@ -164,7 +232,7 @@ __device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[Ti
     // step of tile j in buffer cur; tile j + 2 goes to buffer nxt2
     const auto step = [&](auto masked, char* cur, char* nxt2, int j) {
         const int kb0 = cx.kv_begin + j * C::BN;
-        const auto cp = [&]() { copy(nxt2, kb0 + 2 * C::BN); };
+        const auto cp = [&]() { copy(nxt2, min(kb0 + 2 * C::BN, last_kb)); };
         if (COMPUTE) tile_step<D, decltype(masked)::value>(ws, qf, cx, cur, kb0, cp);
         else cp();
         publish_copies_ahead<D>();
@@ -188,6 +256,61 @@ __device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[Ti
     // the copies past the last tile may still be in flight: drain them
     // before the workgroup's LDS can be handed on
     __builtin_amdgcn_s_waitcnt(0x3f70);
+}
+
+// Copies one tile ahead.  Tile j lives in buffer j % 2; its copies are
+// issued while tile j - 1 is being consumed; "wait for my copies, then
+// barrier" publishes it.
+template <int D, bool COMPUTE, class KV>
+__device__ __forceinline__ void key_loop_ahead1(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS],
+                                                const WaveCtx& cx, const KV& kv, const TileBuffers& buf, int n_full)
+{
+    using C = TileCfg<D>;
+    if (cx.ntile > 0) {
+        issue_tile_copies<D>(kv, cx, buf.b0, cx.kv_begin);
+        publish_copies();
+    }
+    int j = 0;
+    for (; j + 2 <= n_full; j += 2) {
+        const int kb0 = cx.kv_begin + j * C::BN;
+        const auto c1 = [&]() { issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN); };
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b0, kb0, c1);
+        else c1();
+        publish_copies();
+        const auto c2 = [&]() {
+            if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+        };
+        if (COMPUTE) tile_step<D, false>(ws, qf, cx, buf.b1, kb0 + C::BN, c2);
+        else c2();
+        publish_copies();
+    }
+    // j is even here, so tile j is in buffer 0
+    for (; j < cx.ntile; j += 2) {
+        const int kb0 = cx.kv_begin + j * C::BN;
+        const auto c1 = [&]() {
+            if (j + 1 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b1, kb0 + C::BN);
+        };
+        if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b0, kb0, c1);
+        else c1();
+        publish_copies();
+        if (j + 1 < cx.ntile) {
+            const auto c2 = [&]() {
+                if (j + 2 < cx.ntile) issue_tile_copies<D>(kv, cx, buf.b0, kb0 + 2 * C::BN);
+            };
+            if (COMPUTE) tile_step<D, true>(ws, qf, cx, buf.b1, kb0 + C::BN, c2);
+            else c2();
+            publish_copies();
+        }
+    }
+}
+
+template <int D, bool COMPUTE, class KV>
+__device__ __forceinline__ void key_loop(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
+                                         const KV& kv, const TileBuffers& buf, int n_full)
+{
+    static_assert(KV::kCopiesAhead == 1 || KV::kCopiesAhead == 2, "copy schedule");
+    if constexpr (KV::kCopiesAhead == 2) key_loop_ahead2<D, COMPUTE>(ws, qf, cx, kv, buf, n_full);
+    else key_loop_ahead1<D, COMPUTE>(ws, qf, cx, kv, buf, n_full);
 }
 
 // Per-wave set-up of one query tile: the Q^T fragments of this lane's query,

@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
 
     // Loads of 16-key tile tt (keys kbeg + 16 tt ..; a tile lies in one page):
     // K lane l: key l % 16, channels 32 ks + 8 (l / 16) .. + 7 (the A operand
-    // of S^T); V: the copy layout of v_dma_row / v_dma_col for one 16-row group, into
-    // the LDS tile vt.  Keys at or past kend are read from key kend - 1
+    // of S^T); V: the copy layout of v_dma_row / v_dma_col for one 16-row
+    // group, into the LDS tile vt.  Keys at or past kend are read from key kend - 1
     // (valid data; the mask removes them).  KS register loads, then VC copies.
     const auto load_tile = [&](int tt, u32x4 (&kr)[KS], char* vt) {
         const int key0 = kbeg + 16 * tt;
@@ -571,12 +571,9 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
 // XCD-contiguous order so they share K/V pages in that XCD's L2.
 // ============================================================================
 // K/V rows through the block table.  A 16-row group of keys (16-aligned)
-// lies inside one page of 16 or 32 tokens, so a copy group takes one table
-// entry; keys are clamped to the last key of the context first, so no page
-// past the context is ever looked up.  The entries come from the
-// workgroup's LDS copy of its pages' table entries (staged once; a global
-// table read at the head of each tile step would hold up that tile's copies
-// by a memory latency).
+// lies inside one page of 16 or 32 tokens, so the group base is one scalar
+// table read; keys are clamped to the last key of the context first, so no
+// page past the context is ever looked up.
 template <int D, int BS>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
@@ -584,7 +581,27 @@ struct PagedKV {
     const int32_t* ptab;     // LDS copy of the block-table entries of pages p0, p0 + 1, ...
     int p0;                  // first page of this workgroup's keys
     int64_t blk_bytes;
-    // Copies of the key loops.  The window holds the table entries
+    // The plain key loop copies one tile ahead (two tiles ahead fetched
+    // about 1.8x the pool bytes on the chunked-prefill batch).
+    static constexpr int kCopiesAhead = 1;
+    // The page of every key tile comes from the workgroup's LDS copy of its
+    // pages' table entries (staged once; a global table read at the head of
+    // each tile step would hold up that tile's copies by a memory latency).
+    __device__ __forceinline__ int64_t page_of(int key, int kv_end) const
+    {
+        return (int64_t)__builtin_amdgcn_readfirstlane(ptab[min(key, kv_end - 1) / BS - p0]);
+    }
+    __device__ __forceinline__ const char* k_group(int key, int kv_end) const
+    {
+        return kbase + page_of(key, kv_end) * blk_bytes;
+    }
+    __device__ __forceinline__ const char* v_group(int key, int kv_end) const
+    {
+        return vbase + page_of(key, kv_end) * blk_bytes;
+    }
+    __device__ __forceinline__ int group_row(int key, int kv_end) const { return min(key, kv_end - 1) % BS; }
+    __device__ __forceinline__ uint32_t group_bytes() const { return (uint32_t)(BS * D * 2); }
+    // Copies of the pipelined key loop.  The window holds the table entries
     // of pages p0 + base .. p0 + base + 63 (lane l: base + l, clamped to the
     // last page of the context); a tile's copies take the entry of the page
     // holding the wave's copy group out of it with a lane read.
@@ -646,12 +663,13 @@ void paged_chunk_kernel(PagedArgs a, int n_work, int map)
     constexpr int NW = chunk_waves<KIND>();
     __shared__ __attribute__((aligned(16))) char lds0[2 * C::TILE_BYTES];
     __shared__ __attribute__((aligned(16))) char lds1[2 * C::TILE_BYTES];
-    __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
     __shared__ int32_t ptab[kChunkMaxSplit / BS];
-    const TileBuffers buf{lds0, lds1, lds2};
-    PipeBuffers pbuf{{lds0, lds1, lds2, nullptr}};
+    const TileBuffers buf{lds0, lds1, nullptr};
+    PipeBuffers pbuf{{lds0, lds1, nullptr, nullptr}};
     if constexpr (KIND != 0) {
+        __shared__ __attribute__((aligned(16))) char lds2[2 * C::TILE_BYTES];
         __shared__ __attribute__((aligned(16))) char lds3[2 * C::TILE_BYTES];
+        pbuf.b[2] = lds2;
         pbuf.b[3] = lds3;
     }
     // A tile holds ppt query positions x G query heads (the heads of one K/V

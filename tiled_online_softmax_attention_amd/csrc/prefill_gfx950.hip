@@ -52,6 +52,7 @@ struct ContigKV {
     const char* k;   // head base (bytes)
     const char* v;
     uint32_t head_bytes;
+    static constexpr int kCopiesAhead = 2;
     __device__ __forceinline__ uint32_t group_bytes() const { return head_bytes; }
     __device__ __forceinline__ const char* k_group(int, int) const { return k; }
     __device__ __forceinline__ const char* v_group(int, int) const { return v; }
