@@ -43,7 +43,9 @@
 // consecutive chunks) -- so tiles are stored row-major with an XOR swizzle of
 // the chunk index that keeps both patterns free of LDS bank conflicts
 // (dual_xor).  Tiles are copied global -> LDS directly (buffer loads to LDS,
-// no registers), one tile ahead into two buffers, one barrier per tile.
+// no registers) one tile ahead, one barrier per tile: into two buffers in
+// the dQ kernel, three in the dK/dV kernel (whose dS waves read a tile one
+// step after the P waves).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
