@@ -133,8 +133,11 @@ def _max_splits(num_seqs, H, H_kv, d, bs, max_q, max_ctx):
 
 
 @pytest.mark.parametrize("args,splits", [
-    # 64-request decode on 16-token pages (vector kernel): 384-token splits
-    ((64, 32, 32, 128, 16, 1, 16384), 43),
+    # 64-request decode on 16-token pages (decode MFMA kernel, plain heads at
+    # d = 128 on 2048 pairs): 1024-key splits
+    ((64, 32, 32, 128, 16, 1, 16384), 16),
+    # the same at d = 64 (vector kernel): 384-token splits
+    ((64, 32, 32, 64, 16, 1, 16384), 43),
     # the same lengths on 4 K/V heads (tile kernel, decode-length rows): 1280-key splits
     ((64, 32, 4, 128, 16, 1, 16384), 13),
     # ... and 128 such requests (512 pairs: decode MFMA kernel, 8 rows): 1024-key splits
@@ -333,7 +336,10 @@ def test_split_option_sets_the_workspace():
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts()) == auto
     s256 = attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=256))
     assert s256 == (64 * 32 * 64 * 128 * 4 + 255) // 256 * 256 + 64 * 32 * 64 * 4
-    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=1 << 20)) == 0
+    # on the vector kernel a split longer than every context is one split (the
+    # decode MFMA kernel, this shape's default, caps a split at 64 pages)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384,
+                                               opts(paged_split_tokens=1 << 20, paged_path=0)) == 0
 
 
 def test_decode_mfma_plan():

@@ -207,7 +207,8 @@ __device__ __forceinline__ void issue_tile_copies_flat(const KV& kv, const WaveC
 // whole group lies past kv_end every row is that row, in the page looked up.
 // K and V differ only in which lane fetches which row and 16-byte chunk (the
 // layouts of k_dma_row / v_dma_row), so both go through the same branch-free code.
-template <int D, int NW, int BS>
+// CPOL: the copies' cache policy (0, or kCopyStream for K/V read once).
+template <int D, int NW, int BS, int CPOL>
 __device__ __forceinline__ void issue_tile_copies_paged(const char* kbase, const char* vbase, int64_t blk_bytes,
                                                         const WaveCtx& cx, char* buf, int key_base, int page)
 {
@@ -233,7 +234,7 @@ __device__ __forceinline__ void issue_tile_copies_paged(const char* kbase, const
     for (int k = 0; k < CPW; ++k) {
         const int row = min(lrow + k * rstep, last) & (BS - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, ATTN_LDS(dst + k * 1024), 16,
-                                                 (uint32_t)row * C::ROW_BYTES + lcol, k * cstep, 0, 0);
+                                                 (uint32_t)row * C::ROW_BYTES + lcol, k * cstep, 0, CPOL);
     }
 #endif
 }

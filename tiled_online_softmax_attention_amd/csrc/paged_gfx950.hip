@@ -169,6 +169,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 
     const int pbeg = kbeg / BS;
     const int pend = (kend > kbeg) ? (kend + BS - 1) / BS : pbeg;
+    // K/V loads are non-temporal: every page is read by this workgroup alone
+    // (5.91 -> 6.23 TB/s on the 64-request decode batch)
     u32x4 kr[LOADS], vr[LOADS], kn[LOADS], vn[LOADS];
     int p = pbeg + w;
     if (p < pend) {
@@ -177,8 +179,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
         const char* vp = vbase + pb * blk_bytes;
 #pragma unroll
         for (int j = 0; j < LOADS; ++j) {
-            kr[j] = *(const u32x4*)(kp + (j * TPL + sub) * D * 2);
-            vr[j] = *(const u32x4*)(vp + (j * TPL + sub) * D * 2);
+            kr[j] = __builtin_nontemporal_load((const u32x4*)(kp + (j * TPL + sub) * D * 2));
+            vr[j] = __builtin_nontemporal_load((const u32x4*)(vp + (j * TPL + sub) * D * 2));
         }
     }
     for (; p < pend; p += 4) {
@@ -189,8 +191,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
             const char* vp = vbase + pb * blk_bytes;
 #pragma unroll
             for (int j = 0; j < LOADS; ++j) {
-                kn[j] = *(const u32x4*)(kp + (j * TPL + sub) * D * 2);
-                vn[j] = *(const u32x4*)(vp + (j * TPL + sub) * D * 2);
+                kn[j] = __builtin_nontemporal_load((const u32x4*)(kp + (j * TPL + sub) * D * 2));
+                vn[j] = __builtin_nontemporal_load((const u32x4*)(vp + (j * TPL + sub) * D * 2));
             }
         }
         // scores of this lane group's tokens, for every query head
@@ -407,7 +409,8 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
     // Loads of 16-key tile tt (keys kbeg + 16 tt ..; a tile lies in one page):
     // K lane l: key l % 16, channels 32 ks + 8 (l / 16) .. + 7 (the A operand
     // of S^T); V: the copy layout of v_dma_row / v_dma_col for one 16-row
-    // group, into the LDS tile vt.  Keys at or past kend are read from key kend - 1
+    // group, into the LDS tile vt.  Both non-temporal (read by this
+    // workgroup alone).  Keys at or past kend are read from key kend - 1
     // (valid data; the mask removes them).  KS register loads, then VC copies.
     const auto load_tile = [&](int tt, u32x4 (&kr)[KS], char* vt) {
         const int key0 = kbeg + 16 * tt;
@@ -415,7 +418,8 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
         const char* kp = kbase + pg * blk_bytes;
         const int krow = min(key0 + (lane & 15), last) & (BS - 1);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[ks] = *(const u32x4*)(kp + krow * ROW + 64 * ks + 16 * (lane >> 4));
+        for (int ks = 0; ks < KS; ++ks)
+            kr[ks] = __builtin_nontemporal_load((const u32x4*)(kp + krow * ROW + 64 * ks + 16 * (lane >> 4)));
 #if defined(__HIP_DEVICE_COMPILE__)
         const __amdgpu_buffer_rsrc_t rv = raw_rsrc(vbase + pg * blk_bytes, (uint32_t)(BS * ROW));
         const uint32_t vcol = v_dma_col<D>(lane);
@@ -423,7 +427,7 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
         for (int i = 0; i < VC; ++i) {
             const int vrow = min(key0 + i * TileCfg<D>::ROWS_PER_DMA + v_dma_row<D>(lane), last) & (BS - 1);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, ATTN_LDS(vt + i * 1024), 16, (uint32_t)vrow * ROW + vcol, 0,
-                                                     0, 0);
+                                                     0, kCopyStream);
         }
 #endif
     };
@@ -573,8 +577,10 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
 // K/V rows through the block table.  A 16-row group of keys (16-aligned)
 // lies inside one page of 16 or 32 tokens, so the group base is one scalar
 // table read; keys are clamped to the last key of the context first, so no
-// page past the context is ever looked up.
-template <int D, int BS>
+// page past the context is ever looked up.  STREAM: the pipelined loop's
+// copies are non-temporal (kCopyStream), for the decode-length variant,
+// where a split's K/V tiles are read by its one workgroup.
+template <int D, int BS, bool STREAM>
 struct PagedKV {
     const char* kbase;       // k_pool + head offset (bytes)
     const char* vbase;
@@ -628,7 +634,8 @@ struct PagedKV {
     template <int NW>
     __device__ __forceinline__ void copy_tile(const WaveCtx& cx, char* buf, int key_base, int page) const
     {
-        issue_tile_copies_paged<D, NW, BS>(kbase, vbase, blk_bytes, cx, buf, key_base, page);
+        constexpr int CPOL = STREAM ? kCopyStream : 0;
+        issue_tile_copies_paged<D, NW, BS, CPOL>(kbase, vbase, blk_bytes, cx, buf, key_base, page);
     }
 };
 
@@ -721,7 +728,9 @@ void paged_chunk_kernel(PagedArgs a, int n_work, int map)
     const int32_t* table = a.block_table + (int64_t)r * a.max_blocks_per_seq;
     for (int i = threadIdx.x; i < np; i += 64 * NW) ptab[i] = table[p0 + i];
     __syncthreads();
-    PagedKV<D, BS> kv;
+    // decode-length rows (KIND 1 by default) read each K/V tile in one
+    // workgroup; chunks share them between the query tiles of a request
+    PagedKV<D, BS, KIND == 1> kv;
     kv.kbase = (const char*)a.k_pool + (int64_t)hk * BS * D * 2;
     kv.vbase = (const char*)a.v_pool + (int64_t)hk * BS * D * 2;
     kv.ptab = ptab;
@@ -960,9 +969,22 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     // 16-token pages, TB/s for the tile kernel / the decode MFMA kernel: 64
     // requests 4.90 / 4.72, 256 requests 4.76 / 5.32, 512 requests 5.13 /
     // 5.22.)
+    // Below kDecodeMfmaGroup heads per group the vector kernel is the
+    // default, except where the decode MFMA kernel (its K/V loads
+    // non-temporal, like the vector kernel's) measured faster: several query
+    // positions (the vector kernel reads every page once per query row),
+    // 32-token pages (two pages per lane crowd the vector kernel's
+    // registers), and plain heads at d = 128 on batches of many pairs.  (Same
+    // box, 32 heads, contexts U[512,16384], TB/s vector / MFMA: 64 requests
+    // 6.21 / 6.40, 16 requests 5.94 / 6.19, 256 requests 6.11 / 6.35, 8
+    // requests 5.47 / 5.24; 32-token pages 4.73 / 6.48; 4 query positions
+    // 1.55 / 5.77; d = 64 6.56 / 6.19; 16 K/V heads 6.42 / 6.06.)
     const bool dec_rows = (int64_t)max_q_len * G <= kDecMfmaRows;
-    p.path = (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup) ? 0
-           : ((dec_rows && (int64_t)num_seqs * H_kv >= kDecMfmaMinPairs) ? 2 : 1);
+    const bool many_pairs = (int64_t)num_seqs * H_kv >= kDecMfmaMinPairs;
+    if (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup)
+        p.path = (dec_rows && (max_q_len > 1 || block_size == 32 || (G == 1 && d == 128 && many_pairs))) ? 2 : 0;
+    else
+        p.path = (dec_rows && many_pairs) ? 2 : 1;
     if ((opts.paged_path == 0 && max_q_len <= kDecodeMaxQ) || opts.paged_path == 1 ||
         (opts.paged_path == 2 && dec_rows))
         p.path = opts.paged_path;
