@@ -46,7 +46,7 @@ METRIC = "causal prefill TFLOP/s + paged-decode KV GB/s (and % roofline), 1 MI35
 KERNEL_SOURCES = {
     "prefill_c3": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "prefill_gfx950.hip",
                    "attn_internal.h"],
-    "decode_c4": ["paged_gfx950.hip", "attn_internal.h"],
+    "decode_c4": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "paged_gfx950.hip", "attn_internal.h"],
     "chunk_c5": ["attn_mfma_core.h", "attn_mfma_kernel.h", "attn_mfma_pipe.h", "paged_gfx950.hip", "attn_internal.h"],
     "bwd_c3": ["attn_mfma_core.h", "bwd_gfx950.hip", "bwd_internal.h"],
 }
