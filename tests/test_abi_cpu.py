@@ -134,14 +134,18 @@ def _max_splits(num_seqs, H, H_kv, d, bs, max_q, max_ctx):
 
 @pytest.mark.parametrize("args,splits", [
     # 64-request decode on 16-token pages (decode MFMA kernel, plain heads at
-    # d = 128 on 2048 pairs): 1024-key splits
-    ((64, 32, 32, 128, 16, 1, 16384), 16),
+    # d = 128 on 2048 pairs): 2048-key splits
+    ((64, 32, 32, 128, 16, 1, 16384), 8),
+    # ... 16 such requests (512 pairs): 1024-key splits
+    ((16, 32, 32, 128, 16, 1, 16384), 16),
     # the same at d = 64 (vector kernel): 384-token splits
     ((64, 32, 32, 64, 16, 1, 16384), 43),
     # the same lengths on 4 K/V heads (tile kernel, decode-length rows): 1280-key splits
     ((64, 32, 4, 128, 16, 1, 16384), 13),
-    # ... and 128 such requests (512 pairs: decode MFMA kernel, 8 rows): 1024-key splits
-    ((128, 32, 4, 128, 16, 1, 16384), 16),
+    # ... 128 such requests (512 pairs, still the tile kernel): 2368-key splits
+    ((128, 32, 4, 128, 16, 1, 16384), 7),
+    # ... and 256 (1024 pairs: decode MFMA kernel, 8 rows): 2048-key splits
+    ((256, 32, 4, 128, 16, 1, 16384), 8),
     # chunked prefill, 8 x 512 rows on 32-token pages (tile kernel): 8192-key splits
     ((8, 32, 32, 128, 32, 512, 33280), 5),
     # small decode batches: splits halved down to one 16-token page per wave, no further
@@ -345,16 +349,16 @@ def test_split_option_sets_the_workspace():
 def test_decode_mfma_plan():
     """Decode on grouped heads (32 query heads on 4 K/V heads, one query row:
     8 rows of the decode MFMA kernel's 16) on that kernel splits the context
-    into 1024-key splits for a 64-request batch, caps a forced split at 64
-    pages, and the kernel is not taken for more rows than 16 (q_len 3 on
-    groups of 8)."""
+    into 1024-key splits for a 64-request batch (256 pairs: no doubling to
+    2048 below 1024 pairs), caps a forced split at 128 pages, and the kernel
+    is not taken for more rows than 16 (q_len 3 on groups of 8)."""
     def ws(splits, rows=64 * 1, H=32):
         return (rows * H * splits * 128 * 4 + 255) // 256 * 256 + rows * H * splits * 4
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 1, 16384, opts(paged_path=2)) == ws(16)
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 1, 16384,
-                                               opts(paged_split_tokens=4096, paged_path=2)) == ws(16)
-    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 32, 1, 16384,
                                                opts(paged_split_tokens=4096, paged_path=2)) == ws(8)
+    assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 32, 1, 16384,
+                                               opts(paged_split_tokens=8192, paged_path=2)) == ws(4)
     # 3 rows x 8 heads = 24 > 16: the tile kernel's plan (64-key units, no page cap)
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 4, 128, 16, 3, 16384,
                                                opts(paged_split_tokens=4096, paged_path=2)) == ws(4, rows=64 * 3)

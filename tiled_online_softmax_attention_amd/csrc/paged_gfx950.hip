@@ -319,7 +319,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(PagedArgs a)
 // are merged through LDS at the end.
 // ============================================================================
 constexpr int kDecMfmaRows = 16;       // query rows (heads x positions) per workgroup
-constexpr int kDecMfmaMinPairs = 512;  // (request, K/V head) pairs from which it is the default
+constexpr int kDecMfmaMinPairs = 512;  // (request, K/V head) pairs from which it is the default ...
+constexpr int kDecMfmaMinPairsGrouped = 1024;   // ... for groups of kDecodeMfmaGroup heads and more
 
 __device__ __forceinline__ f32x4 mfma16x32(bf16x8 a, bf16x8 b, f32x4 c)
 {
@@ -397,10 +398,12 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
         qf[ks] = as_bf16x8(v);
     }
 
-    // block-table entries of the split's pages (at most 64: the plan caps the
-    // split), lane i holding page p0 + i
+    // block-table entries of the split's pages (at most 128: the plan caps
+    // the split) in two registers, lane i holding pages p0 + i and p0 + 64 + i
     const int p0 = kbeg / BS, np = (kend - 1) / BS - p0 + 1;
-    const int pgv = a.block_table[(int64_t)r * a.max_blocks_per_seq + p0 + min(lane, np - 1)];
+    const int32_t* trow = a.block_table + (int64_t)r * a.max_blocks_per_seq + p0;
+    const int pgv0 = trow[min(lane, np - 1)];
+    const int pgv1 = trow[min(64 + lane, np - 1)];
     const int64_t blk_bytes = a.kv_block_stride * 2;
     const char* kbase = (const char*)a.k_pool + (int64_t)hk * BS * ROW;
     const char* vbase = (const char*)a.v_pool + (int64_t)hk * BS * ROW;
@@ -414,7 +417,8 @@ __global__ __launch_bounds__(256, 3) void paged_decode_mfma_kernel(PagedArgs a)
     // (valid data; the mask removes them).  KS register loads, then VC copies.
     const auto load_tile = [&](int tt, u32x4 (&kr)[KS], char* vt) {
         const int key0 = kbeg + 16 * tt;
-        const int64_t pg = __builtin_amdgcn_readlane(pgv, key0 / BS - p0);
+        const int pi = key0 / BS - p0;   // < 128, wave-uniform
+        const int64_t pg = (pi < 64) ? __builtin_amdgcn_readlane(pgv0, pi) : __builtin_amdgcn_readlane(pgv1, pi - 64);
         const char* kp = kbase + pg * blk_bytes;
         const int krow = min(key0 + (lane & 15), last) & (BS - 1);
 #pragma unroll
@@ -979,12 +983,16 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     // 6.21 / 6.40, 16 requests 5.94 / 6.19, 256 requests 6.11 / 6.35, 8
     // requests 5.47 / 5.24; 32-token pages 4.73 / 6.48; 4 query positions
     // 1.55 / 5.77; d = 64 6.56 / 6.19; 16 K/V heads 6.42 / 6.06.)
+    // From groups of kDecodeMfmaGroup heads up, the tile kernel leads up to
+    // 512 pairs (GQA-8, 128 requests: tile 5.41, decode MFMA 5.27 TB/s) and
+    // the decode MFMA kernel from 1024 (256 requests: 4.27 / 5.59).
     const bool dec_rows = (int64_t)max_q_len * G <= kDecMfmaRows;
-    const bool many_pairs = (int64_t)num_seqs * H_kv >= kDecMfmaMinPairs;
+    const int64_t pairs = (int64_t)num_seqs * H_kv;
     if (max_q_len <= kDecodeMaxQ && G < kDecodeMfmaGroup)
-        p.path = (dec_rows && (max_q_len > 1 || block_size == 32 || (G == 1 && d == 128 && many_pairs))) ? 2 : 0;
+        p.path = (dec_rows && (max_q_len > 1 || block_size == 32 || (G == 1 && d == 128 && pairs >= kDecMfmaMinPairs)))
+                     ? 2 : 0;
     else
-        p.path = (dec_rows && many_pairs) ? 2 : 1;
+        p.path = (dec_rows && pairs >= kDecMfmaMinPairsGrouped) ? 2 : 1;
     if ((opts.paged_path == 0 && max_q_len <= kDecodeMaxQ) || opts.paged_path == 1 ||
         (opts.paged_path == 2 && dec_rows))
         p.path = opts.paged_path;
@@ -1019,12 +1027,17 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
         p.tile_kernel = 0;
     } else if (p.path == 2) {
         // decode MFMA kernel: 4 waves x 4 tiles of 16 keys, doubled while the
-        // batch keeps the chip busy, up to 64 pages (the block-table entries
-        // of a split sit in one register) and 1024 keys
+        // batch keeps the chip busy, up to 128 pages (the block-table entries
+        // of a split sit in two registers) and 2048 keys, the last doubling
+        // only from 1024 pairs (2048-key against 1024-key splits, TB/s: 64
+        // requests x 32 heads 6.22 / 6.21-6.44, 256 x 32 6.52 / 6.37, 4 query
+        // positions 6.02 / 5.79, GQA-8 256 requests 5.59 / 5.25; 16 x 32
+        // heads 5.90 / 6.03-6.24)
         const int64_t items = (int64_t)num_seqs * H_kv;
         S = 256;
-        const int s_max = min(64 * block_size, 1024);
-        while (S < s_max && items * ((max_ctx_len + 2 * S - 1) / (2 * S)) >= 2048) S *= 2;
+        const int s_max = min(128 * block_size, 2048);
+        while (S < s_max && items * ((max_ctx_len + 2 * S - 1) / (2 * S)) >= 2048 && (S < 1024 || items >= 1024))
+            S *= 2;
         p.nqt = 1;
         p.tile_kernel = 0;
     } else {
@@ -1062,9 +1075,9 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     }
     if (opts.paged_split_tokens > 0) S = opts.paged_split_tokens;
     // a tile-path workgroup stages its split's block-table entries in LDS, a
-    // decode-MFMA wave holds them in one register
+    // decode-MFMA wave holds them in two registers
     if (p.path == 1 && S > kChunkMaxSplit) S = kChunkMaxSplit;
-    if (p.path == 2 && S > 64 * block_size) S = 64 * block_size;
+    if (p.path == 2 && S > 128 * block_size) S = 128 * block_size;
     // whole pages; on the tile path a multiple of 64 keys (whole pages of 16
     // or 32 tokens, so every split starts on a page boundary)
     const int unit = (p.path != 1) ? block_size : (block_size > 64 ? block_size : 64);
