@@ -501,7 +501,7 @@ def bench_gqa(args):
 KERNELS = {
     "c3": "prefill_bf16_kernel<128, true, 0>",
     "c2": "prefill_bf16_kernel<128, false, 1>",
-    "c4": "paged_decode_mfma_kernel<128, 16> + paged_combine_kernel<128>",
+    "c4": "paged_decode_mfma_kernel<128, 16> + paged_combine_heads_kernel<128>",
     "c5": "paged_chunk_kernel<128, 32, 0> + paged_combine_heads_kernel<128>",
 }
 
