@@ -203,14 +203,14 @@ __device__ __forceinline__ void tile_step(WaveState<D>& ws, const bf16x8 (&qf)[T
 // j - 1; past the last tile it fetches the last tile again, out of L2,
 // rather than keys beyond the causal limit), and ends with "wait until only
 // those copies are in flight, barrier", which publishes tile j + 1: each
-// tile's copies have a step and a half to land.  The copies
-// are the K/V source's branch-free ones (copy_tile, its source looked up in
-// a window updated once per three tiles), and the buffers are chosen
-// statically (unrolled by three): with a branch in the copies, the compiler
-// orders the next LDS reads behind every copy in flight.
+// tile's copies have a step and a half to land.  The copies are the K/V
+// source's branch-free ones (copy_tile, its source looked up in a window
+// updated once per three tiles), and the buffers are chosen statically
+// (unrolled by three): with a branch in the copies, the compiler orders the
+// next LDS reads behind every copy in flight.
 template <int D, bool COMPUTE, class KV>
-__device__ __forceinline__ void key_loop_ahead2(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS], const WaveCtx& cx,
-                                         const KV& kv, const TileBuffers& buf, int n_full)
+__device__ __forceinline__ void key_loop_ahead2(WaveState<D>& ws, const bf16x8 (&qf)[TileCfg<D>::KSTEPS],
+                                                const WaveCtx& cx, const KV& kv, const TileBuffers& buf, int n_full)
 {
     using C = TileCfg<D>;
     const int nt = cx.ntile;

@@ -953,11 +953,12 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(GatherArgs a)
 // ============================================================================
 // host side
 // ============================================================================
-// The combine of few splits per row (chunked prefill: C5 has at most 5) runs
-// lane groups per head, each lane walking its head's log-sum-exps itself;
-// with many splits (decode: up to 64) a wave per head reads them in parallel
+// The combine of few splits per row (chunked prefill: C5 has at most 5; the
+// 64-request decode on the decode MFMA kernel 8) runs lane groups per head,
+// each lane walking its head's log-sum-exps itself; with many splits (the
+// vector decode kernel's: up to 64) a wave per head reads them in parallel
 // (same-box A/B: heads kernel C5 call 920 -> 939 TFLOP/s, but 64-request
-// decode 5.75 -> 5.69 TB/s).
+// decode on the vector kernel, 43 splits, 5.75 -> 5.69 TB/s).
 constexpr int kCombineHeadsMaxSplits = 8;
 
 PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int max_q_len, int max_ctx_len,
