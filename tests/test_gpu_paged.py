@@ -12,9 +12,15 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def split_opts(tokens):
-    """Launch options forcing the context split size (tokens), or None."""
-    return None if tokens is None else {"paged_split_tokens": int(tokens)}
+def split_opts(tokens, path=None):
+    """Launch options forcing the context split size (tokens) and the decode
+    path (0 vector kernel, 2 decode MFMA kernel), or None."""
+    o = {}
+    if tokens is not None:
+        o["paged_split_tokens"] = int(tokens)
+    if path is not None:
+        o["paged_path"] = int(path)
+    return o or None
 
 
 def make(ctx, ql, H=4, d=128, bs=16, seed=1, **kw):
@@ -22,17 +28,17 @@ def make(ctx, ql, H=4, d=128, bs=16, seed=1, **kw):
                               seed, DEV, **kw)
 
 
-def run(pi, split=None, name="paged"):
-    log("%s: num_seqs=%d H=%d d=%d bs=%d ctx=%s q=%s split=%s" % (
-        name, pi.num_seqs, pi.H, pi.d, pi.block_size, pi.ctx_lens.tolist()[:8], pi.q_lens.tolist()[:8], split))
+def run(pi, split=None, name="paged", path=None):
+    log("%s: num_seqs=%d H=%d d=%d bs=%d ctx=%s q=%s split=%s path=%s" % (
+        name, pi.num_seqs, pi.H, pi.d, pi.block_size, pi.ctx_lens.tolist()[:8], pi.q_lens.tolist()[:8], split, path))
     o, lse = attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
-                                  pi.scale, options=split_opts(split))
+                                  pi.scale, options=split_opts(split, path))
     torch.cuda.synchronize()
     return o, lse
 
 
-def check_full(pi, split=None, name="paged"):
-    o, lse = run(pi, split, name)
+def check_full(pi, split=None, name="paged", path=None):
+    o, lse = run(pi, split, name, path)
     o_ref, l_ref = oracle.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size,
                                           pi.scale)
     check_close(name, o, o_ref, lse, l_ref, torch.bfloat16)
@@ -42,19 +48,24 @@ def check_full(pi, split=None, name="paged"):
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("split", [None, 64])
-def test_decode_ragged(bs, d, split):
+@pytest.mark.parametrize("path", [None, 0, 2])
+def test_decode_ragged(bs, d, split, path):
+    # plain heads, one query row: the plan's kernel (the vector kernel here but
+    # on 32-token pages), and each decode kernel forced
     ctx = [1, 15, 16, 17, 100, 513, 1030, 2047]
     pi = make(ctx, [1] * len(ctx), H=3, d=d, bs=bs, seed=bs + d)
-    check_full(pi, split, "decode bs%d d%d" % (bs, d))
+    check_full(pi, split, "decode bs%d d%d" % (bs, d), path)
 
 
 @pytest.mark.parametrize("bs", [16, 32])
 @pytest.mark.parametrize("split", [None, 256])
-def test_small_q_decode_path(bs, split):
-    # q_len 2..4 goes through the vector decode kernel, one query row per workgroup
+@pytest.mark.parametrize("path", [None, 0])
+def test_small_q_decode_path(bs, split, path):
+    # q_len 2..4: the decode MFMA kernel by default (all of a request's rows
+    # in one workgroup), the vector kernel (one query row per workgroup) forced
     ctx = [4, 40, 333, 1000]
     pi = make(ctx, [2, 4, 3, 4], H=2, bs=bs, seed=3)
-    check_full(pi, split, "decode q<=4 bs%d" % bs)
+    check_full(pi, split, "decode q<=4 bs%d" % bs, path)
 
 
 @pytest.mark.parametrize("bs", [16, 32])
