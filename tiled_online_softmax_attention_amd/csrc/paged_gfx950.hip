@@ -957,7 +957,7 @@ __global__ __launch_bounds__(256) void paged_gather_kernel(GatherArgs a)
 // 64-request decode on the decode MFMA kernel 8) runs lane groups per head,
 // each lane walking its head's log-sum-exps itself; with many splits (the
 // vector decode kernel's: up to 64) a wave per head reads them in parallel
-// (same-box A/B: heads kernel C5 call 920 -> 939 TFLOP/s, but 64-request
+// (same-machine A/B: heads kernel C5 call 920 -> 939 TFLOP/s, but 64-request
 // decode on the vector kernel, 43 splits, 5.75 -> 5.69 TB/s).
 constexpr int kCombineHeadsMaxSplits = 8;
 
@@ -980,7 +980,7 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
     // positions (the vector kernel reads every page once per query row),
     // 32-token pages (two pages per lane crowd the vector kernel's
     // registers), and plain heads at d = 128 on batches of many pairs.  (Same
-    // box, 32 heads, contexts U[512,16384], TB/s vector / MFMA: 64 requests
+    // machine, 32 heads, contexts U[512,16384], TB/s vector / MFMA: 64 requests
     // 6.21 / 6.40, 16 requests 5.94 / 6.19, 256 requests 6.11 / 6.35, 8
     // requests 5.47 / 5.24; 32-token pages 4.73 / 6.48; 4 query positions
     // 1.55 / 5.77; d = 64 6.56 / 6.19; 16 K/V heads 6.42 / 6.06.)
