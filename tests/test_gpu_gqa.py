@@ -101,7 +101,8 @@ def test_paged_decode_mfma_matches_oracle(H, H_kv, ql, bs, d, split):
     position, 8 x 2 and 4 x 4 rows (all 16), one plain head (1 row of 16), 3
     heads x 5 positions (15 rows); contexts shorter than a 16-key tile, tiles
     cut by the context end, splits of one or two pages, of a length that is
-    not a whole number of tiles per wave, and above the 64-page cap."""
+    not a whole number of tiles per wave, and above the 128-page cap (pages
+    64-127 of a split come from the second table register)."""
     ctx = [1, 15, 16, 17, 300, 1030, 5000]
     qls = [min(ql, c) for c in ctx]
     pi = make_gqa(ctx, qls, H, H_kv, d=d, bs=bs, seed=H + 3 * H_kv + ql + bs + d)
