@@ -14,7 +14,9 @@ measured with HIP events on the launch stream), the decode KV GB/s
 (algorithmic bytes: K and V of every context token read once, plus q, o and
 the block table) under "decode", the chunked prefill under "c5", and, timed
 after the steps, the small causal prefill B=1 H=32 N=2048 under "c2" (warm,
-and cold: 1 GiB written between launches).  The oracle (fp64, CPU) is timed
+and cold: 1 GiB written between launches), then a few calls each of the
+grouped-query prefill and decode (32 query heads on 4 K/V heads) under "gqa8"
+and of the prefill's backward under "bwd".  The oracle (fp64, CPU) is timed
 on a bounded sample of the same prefill and decode workloads as
 `cpu_baseline`.
 
@@ -295,6 +297,50 @@ def cpu_baseline_bwd(q, k, v, do, cfg, budget_s, oracle):
                       "time" % (done_rows, done_heads, t_total)}
 
 
+
+def time_bwd(torch, attn, inputs, dev, key, cfg, steps, warmup, keep=False):
+    """One backward variant ("mha" or "gqa8"): the forward's O and LSE and dO
+    resident in HBM, then `steps` calls of attn_prefill_bwd timed with HIP
+    events on their stream.  Returns (entry, wall seconds of the timed calls,
+    (q, k, v, dO) if keep else None)."""
+    q, k, v = inputs.prefill_inputs(cfg, dev)
+    do = inputs.grad_output(cfg, dev)
+    o, lse = attn.prefill(q, k, v, True, cfg.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(attn.attn_prefill_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N), dtype=torch.uint8, device=dev)
+    timer = EventTimer(torch)
+    for _ in range(warmup):
+        attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        e = timer.start()
+        attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
+        timer.stop(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = timer.mean_ms()
+    fl = bwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
+    tf = fl / (ms * 1e-3) / 1e12
+    entry = {"launch_ms": round(ms, 4), "TFLOP/s": round(tf, 2),
+             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "traffic": read_traffic("bwd_c3") if key == "mha" else None,
+                          "kernels": "bwd_dq_kernel<128, true> + bwd_dkdv_kernel<128, true>",
+                          "flops_per_launch": fl,
+                          "executed_flops_per_launch": fl * 7 / 5,
+                          "algorithmic_bytes_per_launch": bwd_bytes(cfg.B, cfg.H, cfg.N, cfg.d, H_kv=cfg.H_kv)}}
+    if key == "gqa8":
+        entry["workload"] = "causal prefill backward bf16 16x32x8192x128, 32 query heads on 4 K/V heads"
+    else:
+        entry["workload"] = "causal prefill backward bf16 16x32x8192x128, dO iid N(0,1)"
+    del o, lse, dq, dk, dv, ws
+    kept = (q, k, v, do) if keep else None
+    if not keep:
+        del q, k, v, do
+    torch.cuda.empty_cache()
+    return entry, wall, kept
+
 def bench_bwd(args):
     """Backward of the causal 16x32x8192x128 prefill (attn_prefill_bwd: dQ
     kernel + dK/dV kernel) and of its grouped-query variant (4 K/V heads);
@@ -325,48 +371,22 @@ def bench_bwd(args):
     if args.bwd_mha_only:
         variants = variants[:1]
     for key, cfg in variants:
-        q, k, v = inputs.prefill_inputs(cfg, dev)
-        do = inputs.grad_output(cfg, dev)
-        o, lse = attn.prefill(q, k, v, True, cfg.scale)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(attn.attn_prefill_bwd_workspace_bytes(cfg.B, cfg.H, cfg.N), dtype=torch.uint8, device=dev)
-        timer = EventTimer(torch)
-        for _ in range(args.warmup):
-            attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            e = timer.start()
-            attn.prefill_bwd(q, k, v, o, lse, do, True, cfg.scale, dq=dq, dk=dk, dv=dv, workspace=ws)
-            timer.stop(e)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        ms = timer.mean_ms()
-        fl = bwd_flops(cfg.B, cfg.H, cfg.N, cfg.d, True)
-        tf = fl / (ms * 1e-3) / 1e12
-        entry = {"launch_ms": round(ms, 4), "TFLOP/s": round(tf, 2),
-                 "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
-                              "traffic": read_traffic("bwd_c3") if key == "mha" else None,
-                              "kernels": "bwd_dq_kernel<128, true> + bwd_dkdv_kernel<128, true>",
-                              "flops_per_launch": fl,
-                              "executed_flops_per_launch": fl * 7 / 5,
-                              "algorithmic_bytes_per_launch": bwd_bytes(cfg.B, cfg.H, cfg.N, cfg.d,
-                                                                        H_kv=cfg.H_kv)}}
+        entry, wall, kept = time_bwd(torch, attn, inputs, dev, key, cfg, args.steps, args.warmup,
+                                     keep=(key == "mha" and not args.no_cpu_baseline))
         if key == "mha":
             res["value"] = entry["TFLOP/s"]
             res["ms_per_step"] = round(wall * 1e3 / args.steps, 4)
             res["roofline"] = entry["roofline"]
             res["launch_ms"] = entry["launch_ms"]
-            if not args.no_cpu_baseline:
+            if kept is not None:
                 import oracle
                 print("timing the fp64 oracle on the host", file=sys.stderr, flush=True)
+                q, k, v, do = kept
                 res["cpu_baseline"] = cpu_baseline_bwd(q, k, v, do, cfg, args.cpu_seconds, oracle)
+                del q, k, v, do, kept
+                torch.cuda.empty_cache()
         else:
-            res["gqa8"] = dict(entry, workload="causal prefill backward bf16 16x32x8192x128, 32 query heads on "
-                                                "4 K/V heads")
-        del q, k, v, do, o, lse, dq, dk, dv, ws
-        torch.cuda.empty_cache()
+            res["gqa8"] = entry
     print(json.dumps(res), flush=True)
 
 
@@ -438,6 +458,49 @@ def bench_append(args):
     print(json.dumps(res), flush=True)
 
 
+
+def time_gqa(torch, attn, inputs, dev, steps, warmup):
+    """Grouped-query variants (32 query heads on 4 K/V heads), inputs resident
+    in HBM: the causal 16x32x8192x128 prefill (TFLOP/s) and the 64-request
+    decode batch (KV GB/s, K/V of the 4 shared heads counted once), each call
+    timed with HIP events on its stream."""
+    c3, c4 = inputs.C3_GQA8, inputs.C4_GQA8
+    q, k, v = inputs.prefill_inputs(c3, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((c3.B, c3.H, c3.N), dtype=torch.float32, device=dev)
+    pi = inputs.paged_inputs(c4, dev)
+    ctx_list, ql_list = pi.ctx_lens.cpu().tolist(), pi.q_lens.cpu().tolist()
+    ws = torch.empty(max(1, attn.paged_attn_gqa_workspace_bytes(pi.num_seqs, c4.H, c4.H_kv, c4.d, c4.block_size, 1,
+                                                                max(ctx_list))), dtype=torch.uint8, device=dev)
+    od = torch.empty_like(pi.q)
+    lsed = torch.empty(pi.q.shape[:2], dtype=torch.float32, device=dev)
+    t_pre, t_dec = EventTimer(torch), EventTimer(torch)
+    for i in range(warmup + steps):
+        e = t_pre.start() if i >= warmup else None
+        attn.prefill(q, k, v, True, c3.scale, out=o, lse=lse)
+        if e is not None:
+            t_pre.stop(e)
+        e = t_dec.start() if i >= warmup else None
+        attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
+                             max_q_len=1, max_ctx_len=max(ctx_list), out=od, lse=lsed, workspace=ws)
+        if e is not None:
+            t_dec.stop(e)
+    torch.cuda.synchronize()
+    ms_p, ms_d = t_pre.mean_ms(), t_dec.mean_ms()
+    fl = prefill_flops(c3.B, c3.H, c3.N, c3.d, True)
+    nb = paged_bytes(ctx_list, ql_list, c4.H, c4.d, c4.block_size, H_kv=c4.H_kv)
+    tf, gbs = fl / (ms_p * 1e-3) / 1e12, nb / (ms_d * 1e-3) / 1e9
+    del q, k, v, o, lse, pi, ws, od, lsed
+    torch.cuda.empty_cache()
+    return {"workload": "causal prefill bf16 16x32x8192x128 with 4 K/V heads + paged decode bf16 64 req x "
+                        "1 query, ctx U[512,16384], 16-token pages, 32 query heads on 4 K/V heads",
+            "prefill": {"launch_ms": round(ms_p, 4), "TFLOP/s": round(tf, 2),
+                        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}},
+            "decode": {"launch_ms": round(ms_d, 4), "bytes_per_call": nb, "GB/s": round(gbs, 1),
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                    "frac": round(gbs / PEAK_HBM_GBPS, 4)}}}
+
 def bench_gqa(args):
     """Grouped-query variants (32 query heads on 4 K/V heads): the causal
     16x32x8192x128 prefill (TFLOP/s) and the 64-request decode batch (KV GB/s,
@@ -454,43 +517,11 @@ def bench_gqa(args):
         sys.exit(1)
     attn.library()
     dev = torch.device("cuda:0")
-    c3, c4 = inputs.C3_GQA8, inputs.C4_GQA8
-    q, k, v = inputs.prefill_inputs(c3, dev)
-    o = torch.empty_like(q)
-    lse = torch.empty((c3.B, c3.H, c3.N), dtype=torch.float32, device=dev)
-    pi = inputs.paged_inputs(c4, dev)
-    ctx_list, ql_list = pi.ctx_lens.cpu().tolist(), pi.q_lens.cpu().tolist()
-    ws = torch.empty(max(1, attn.paged_attn_gqa_workspace_bytes(pi.num_seqs, c4.H, c4.H_kv, c4.d, c4.block_size, 1,
-                                                                max(ctx_list))), dtype=torch.uint8, device=dev)
-    od = torch.empty_like(pi.q)
-    lsed = torch.empty(pi.q.shape[:2], dtype=torch.float32, device=dev)
-    t_pre, t_dec = EventTimer(torch), EventTimer(torch)
-    for i in range(args.warmup + args.steps):
-        e = t_pre.start() if i >= args.warmup else None
-        attn.prefill(q, k, v, True, c3.scale, out=o, lse=lse)
-        if e is not None:
-            t_pre.stop(e)
-        e = t_dec.start() if i >= args.warmup else None
-        attn.paged_attention(pi.q, pi.pool, pi.block_table, pi.ctx_lens, pi.q_lens, pi.block_size, pi.scale,
-                             max_q_len=1, max_ctx_len=max(ctx_list), out=od, lse=lsed, workspace=ws)
-        if e is not None:
-            t_dec.stop(e)
-    torch.cuda.synchronize()
-    ms_p, ms_d = t_pre.mean_ms(), t_dec.mean_ms()
-    fl = prefill_flops(c3.B, c3.H, c3.N, c3.d, True)
-    nb = paged_bytes(ctx_list, ql_list, c4.H, c4.d, c4.block_size, H_kv=c4.H_kv)
-    tf, gbs = fl / (ms_p * 1e-3) / 1e12, nb / (ms_d * 1e-3) / 1e9
-    res = {"metric": "GQA-8 causal prefill TFLOP/s + paged-decode KV GB/s", "value": round(tf, 2),
+    g = time_gqa(torch, attn, inputs, dev, args.steps, args.warmup)
+    res = {"metric": "GQA-8 causal prefill TFLOP/s + paged-decode KV GB/s", "value": g["prefill"]["TFLOP/s"],
            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "causal prefill bf16 16x32x8192x128 with 4 K/V heads + paged decode bf16 64 req x "
-                                  "1 query, ctx U[512,16384], 16-token pages, 32 query heads on 4 K/V heads"},
-           "prefill": {"launch_ms": round(ms_p, 4),
-                       "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
-                                    "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}},
-           "decode": {"launch_ms": round(ms_d, 4), "bytes_per_call": nb, "GB/s": round(gbs, 1),
-                      "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                   "frac": round(gbs / PEAK_HBM_GBPS, 4)}}}
+           "config": {"workload": g["workload"]}, "prefill": g["prefill"], "decode": g["decode"]}
     print(json.dumps(res), flush=True)
 
 
@@ -512,6 +543,10 @@ def single_gpu_or_exit(args):
               file=sys.stderr)
         sys.exit(2)
 
+
+# timed calls (and untimed warm-up calls) of the GQA-8 and backward entries of
+# the default run
+EXTRA_STEPS, EXTRA_WARMUP = 5, 2
 
 # warm C2 launches per timed block (time_c2)
 C2_BLOCK = 50
@@ -587,6 +622,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-c2", action="store_true", help="skip the small-prefill timing after the steps")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the GQA-8 and backward timings after the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
@@ -742,6 +779,13 @@ def main():
     if args.only == "all" and not args.no_c2:
         print("timing the 1x32x2048x128 prefill", file=sys.stderr, flush=True)
         res["c2"] = time_c2(torch, attn, inputs, dev, 2000, 200)
+    if args.only == "all" and not args.no_extra:
+        # the grouped-query prefill and decode and the backward, a few calls
+        # each (their own --only modes time more and add the backward's oracle)
+        print("timing the GQA-8 prefill and decode", file=sys.stderr, flush=True)
+        res["gqa8"] = time_gqa(torch, attn, inputs, dev, EXTRA_STEPS, EXTRA_WARMUP)
+        print("timing the backward", file=sys.stderr, flush=True)
+        res["bwd"], _, _ = time_bwd(torch, attn, inputs, dev, "mha", inputs.C3, EXTRA_STEPS, EXTRA_WARMUP)
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill", "decode"):
         import oracle
