@@ -16,7 +16,7 @@ the block table) under "decode", the chunked prefill under "c5", and, timed
 after the steps, the small causal prefill B=1 H=32 N=2048 under "c2" (warm,
 and cold: 1 GiB written between launches), then a few calls each of the
 grouped-query prefill and decode (32 query heads on 4 K/V heads) under "gqa8"
-and of the prefill's backward under "bwd".  The oracle (fp64, CPU) is timed
+and of the prefill's backward under "bwd", and the KV append under "append".  The oracle (fp64, CPU) is timed
 on a bounded sample of the same prefill and decode workloads as
 `cpu_baseline`.
 
@@ -397,6 +397,48 @@ def append_bytes(new_lens, H, d, elem=2):
     return 2 * t * H * d * elem * 2 + len(new_lens) * 12
 
 
+
+def time_append(torch, attn, inputs, dev, steps, warmup):
+    """KV append on the chunked-prefill shape and on one decode step; each
+    timed call (HIP events on its stream) starts from the same cache state
+    (table and free count restored, untimed).  Returns {"chunk_c5": ...,
+    "decode_c4": ...}."""
+    res = {}
+    for name, cfg in (("chunk_c5", inputs.C5), ("decode_c4", inputs.C4)):
+        ctx, ql, _ = inputs.draw_lengths(cfg)
+        ctx, ql = [int(c) for c in ctx], [int(q) for q in ql]
+        ctx_old = [c - q for c, q in zip(ctx, ql)]
+        ai = inputs.append_inputs(ctx_old, ql, cfg.H, cfg.d, cfg.block_size, cfg.seed, device=dev)
+        table0 = ai.block_table.clone()
+        free = torch.tensor(ai.free_list + [0] * (ai.pool.shape[0] - len(ai.free_list)), dtype=torch.int32,
+                            device=dev)
+        count = torch.empty(1, dtype=torch.int32, device=dev)
+        ctx_d = torch.tensor(ctx_old, dtype=torch.int32, device=dev)
+        new_d = torch.tensor(ql, dtype=torch.int32, device=dev)
+        nctx = torch.empty_like(ctx_d)
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+        timer = EventTimer(torch)
+        for i in range(warmup + steps):
+            ai.block_table.copy_(table0)
+            count.fill_(len(ai.free_list))
+            e = timer.start() if i >= warmup else None
+            attn.kv_append(ai.k_new, ai.v_new, ctx_d, new_d, ai.pool, ai.block_table, free, count,
+                           cfg.block_size, max_new_len=max(ql), new_ctx_lens=nctx, status=status, check=False)
+            if e is not None:
+                timer.stop(e)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        ms = timer.mean_ms()
+        nb = append_bytes(ql, cfg.H, cfg.d)
+        res[name] = {"launch_ms": round(ms, 4), "bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                     "new_tokens": sum(ql), "requests": len(ql),
+                     "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                  "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
+        del ai, table0, free
+        torch.cuda.empty_cache()
+    return res
+
 def bench_append(args):
     """KV append (paged_kv_append: allocation launch + copy launch) on the
     chunked-prefill shape (8 requests x 512 tokens onto U[4096, 32768], 32-token
@@ -419,39 +461,7 @@ def bench_append(args):
     res = {"metric": "paged KV append GB/s", "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16", "data": "synthetic"}
-    for name, cfg in (("chunk_c5", inputs.C5), ("decode_c4", inputs.C4)):
-        ctx, ql, _ = inputs.draw_lengths(cfg)
-        ctx, ql = [int(c) for c in ctx], [int(q) for q in ql]
-        ctx_old = [c - q for c, q in zip(ctx, ql)]
-        ai = inputs.append_inputs(ctx_old, ql, cfg.H, cfg.d, cfg.block_size, cfg.seed, device=dev)
-        table0 = ai.block_table.clone()
-        free = torch.tensor(ai.free_list + [0] * (ai.pool.shape[0] - len(ai.free_list)), dtype=torch.int32,
-                            device=dev)
-        count = torch.empty(1, dtype=torch.int32, device=dev)
-        ctx_d = torch.tensor(ctx_old, dtype=torch.int32, device=dev)
-        new_d = torch.tensor(ql, dtype=torch.int32, device=dev)
-        nctx = torch.empty_like(ctx_d)
-        status = torch.empty(1, dtype=torch.int32, device=dev)
-        timer = EventTimer(torch)
-        for i in range(args.warmup + args.steps):
-            ai.block_table.copy_(table0)
-            count.fill_(len(ai.free_list))
-            e = timer.start() if i >= args.warmup else None
-            attn.kv_append(ai.k_new, ai.v_new, ctx_d, new_d, ai.pool, ai.block_table, free, count,
-                           cfg.block_size, max_new_len=max(ql), new_ctx_lens=nctx, status=status, check=False)
-            if e is not None:
-                timer.stop(e)
-        torch.cuda.synchronize()
-        assert int(status.item()) == 0
-        ms = timer.mean_ms()
-        nb = append_bytes(ql, cfg.H, cfg.d)
-        res[name] = {"launch_ms": round(ms, 4), "bytes": nb, "GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
-                     "new_tokens": sum(ql), "requests": len(ql),
-                     "roofline": {"bound": "hbm", "achieved": round(nb / (ms * 1e-3) / 1e9, 1),
-                                  "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                                  "frac": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}}
-        del ai, table0, free
-        torch.cuda.empty_cache()
+    res.update(time_append(torch, attn, inputs, dev, args.steps, args.warmup))
     res["value"] = res["chunk_c5"]["GB/s"]
     res["config"] = {"workload": "KV append: 8 x 512 tokens (32-token pages) and 64 x 1 token (16-token pages), "
                                  "H=32, d=128"}
@@ -623,7 +633,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-c2", action="store_true", help="skip the small-prefill timing after the steps")
     ap.add_argument("--no-extra", action="store_true",
-                    help="skip the GQA-8 and backward timings after the steps")
+                    help="skip the GQA-8, backward and KV-append timings after the steps")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--probe-copy", action="store_true",
                     help="also run one 1 GiB device copy (reference kernel for PMC byte counters)")
@@ -786,6 +796,8 @@ def main():
         res["gqa8"] = time_gqa(torch, attn, inputs, dev, EXTRA_STEPS, EXTRA_WARMUP)
         print("timing the backward", file=sys.stderr, flush=True)
         res["bwd"], _, _ = time_bwd(torch, attn, inputs, dev, "mha", inputs.C3, EXTRA_STEPS, EXTRA_WARMUP)
+        print("timing the KV append", file=sys.stderr, flush=True)
+        res["append"] = time_append(torch, attn, inputs, dev, 20, 5)
 
     if not args.no_cpu_baseline and args.only in ("all", "prefill", "decode"):
         import oracle
