@@ -92,7 +92,7 @@ enum {
  *                    kernel (only for max_q_len * H / H_kv <= 16).
  *   paged_split_tokens : 0 auto; otherwise the keys per context split
  *                    (rounded up to whole pages, 64-key units on the tile
- *                    kernel; at most 8192 there and 64 pages on the decode
+ *                    kernel; at most 8192 there and 128 pages on the decode
  *                    MFMA kernel).
  *   paged_decode_heads : 0 auto; 1, 2, 4 or 8 query heads of one K/V group
  *                    per vector-decode workgroup (must divide H / H_kv; at

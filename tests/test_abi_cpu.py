@@ -341,7 +341,7 @@ def test_split_option_sets_the_workspace():
     s256 = attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384, opts(paged_split_tokens=256))
     assert s256 == (64 * 32 * 64 * 128 * 4 + 255) // 256 * 256 + 64 * 32 * 64 * 4
     # on the vector kernel a split longer than every context is one split (the
-    # decode MFMA kernel, this shape's default, caps a split at 64 pages)
+    # decode MFMA kernel, this shape's default, caps a split at 128 pages)
     assert attn.paged_attn_gqa_workspace_bytes(64, 32, 32, 128, 16, 1, 16384,
                                                opts(paged_split_tokens=1 << 20, paged_path=0)) == 0
 
