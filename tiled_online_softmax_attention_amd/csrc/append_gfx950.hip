@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include "append_internal.h"
+#include "attn_internal.h"
 
 namespace attn {
 
@@ -195,13 +196,13 @@ __global__ __launch_bounds__(kAllocThreads) void kv_release_kernel(ReleaseArgs a
 
 int launch_append(const AppendArgs& a, hipStream_t stream)
 {
+    // the write grid is checked before the allocation is launched
+    const int tiles = (a.max_new_len + kTokPerGroup - 1) / kTokPerGroup;
+    const int64_t grid = (int64_t)a.num_seqs * tiles;
+    if (a.max_new_len > 0 && !grid_fits(grid, kWriteThreads)) return -2;
     hipLaunchKernelGGL(kv_alloc_kernel, dim3(1), dim3(kAllocThreads), 0, stream, a);
-    if (a.max_new_len > 0) {
-        const int tiles = (a.max_new_len + kTokPerGroup - 1) / kTokPerGroup;
-        const int64_t grid = (int64_t)a.num_seqs * tiles;
-        if (grid > INT32_MAX) return -2;
+    if (a.max_new_len > 0)
         hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)grid), dim3(kWriteThreads), 0, stream, a, tiles);
-    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

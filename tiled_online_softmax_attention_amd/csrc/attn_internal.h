@@ -11,6 +11,13 @@
 
 namespace attn {
 
+// A dispatch's grid size is a 32-bit count of work-items: `blocks`
+// workgroups of `threads` each must fit in it (and in a positive int).
+inline bool grid_fits(int64_t blocks, int threads)
+{
+    return blocks > 0 && blocks <= (int64_t)INT32_MAX && blocks * threads <= (int64_t)UINT32_MAX;
+}
+
 struct PrefillArgs {
     const void* q;
     const void* k;

@@ -52,6 +52,7 @@
 
 #include "attn_mfma_core.h"
 #include "bwd_internal.h"
+#include "attn_internal.h"
 
 namespace attn {
 
@@ -752,7 +753,8 @@ int launch_bwd(const BwdArgs& a, hipStream_t stream)
     const int64_t nkb = (a.N + 32 * kRoleKB - 1) / (32 * kRoleKB);
     const bool pair_kv = (a.pair_kv < 0 ? a.causal != 0 : a.pair_kv != 0) && nkb > 1;
     const int64_t n_kv = (int64_t)a.B * a.H_kv * (pair_kv ? (nkb + 1) / 2 : nkb);
-    if (n_dq > (int64_t)INT32_MAX - 8 || n_kv > (int64_t)INT32_MAX - 8) return -2;
+    if (!grid_fits((n_dq + 7) / 8 * 8, BwdCfg<128>::kThreads) || !grid_fits((n_kv + 7) / 8 * 8, 64 * kRoleWaves))
+        return -2;
     const int grid_dq = (int)((n_dq + 7) / 8 * 8);
     const int grid_kv = (int)((n_kv + 7) / 8 * 8);
     if (a.d == 128) {

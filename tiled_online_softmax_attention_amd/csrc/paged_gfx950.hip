@@ -1099,13 +1099,19 @@ PagedPlan plan_paged(int num_seqs, int H, int H_kv, int d, int block_size, int m
 template <int D, int BS>
 static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t stream)
 {
+    // the combine's grid is checked before the partial kernel is launched
+    const int64_t comb_items = (int64_t)a.num_seqs * a.max_q_len * a.H;
+    const int64_t comb_waves = (int64_t)a.num_seqs * a.max_q_len * ((a.H + 64 / (D / 8) - 1) / (64 / (D / 8)));
+    if (a.max_splits > kCombineHeadsMaxSplits && !grid_fits((comb_items + 3) / 4, 256)) return -2;
+    if (a.max_splits > 1 && a.max_splits <= kCombineHeadsMaxSplits && !grid_fits((comb_waves + 3) / 4, 256))
+        return -2;
     if (plan.path == 2) {
         const int64_t grid = (int64_t)a.num_seqs * a.H_kv * a.max_splits;
-        if (grid > (int64_t)INT32_MAX) return -2;
+        if (!grid_fits(grid, 256)) return -2;
         hipLaunchKernelGGL((paged_decode_mfma_kernel<D, BS>), dim3((unsigned)grid), dim3(256), 0, stream, a);
     } else if (plan.path == 0) {
         const int64_t grid = (int64_t)a.num_seqs * a.max_q_len * a.H_kv * plan.n_chunks * a.max_splits;
-        if (grid > (int64_t)INT32_MAX) return -2;
+        if (!grid_fits(grid, 256)) return -2;
         const dim3 g((unsigned)grid), b(256);
         if (plan.gc == 8) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 8>), g, b, 0, stream, a);
         else if (plan.gc == 4) hipLaunchKernelGGL((paged_decode_kernel<D, BS, 4>), g, b, 0, stream, a);
@@ -1119,7 +1125,7 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
         if (a.tile_map >= kMapRanges && a.tile_map <= kMapItems) map = a.tile_map;
         const int64_t grid = (map == kMapPairs) ? (pairs + 7) / 8 * 8 * per_pair
                            : (map == kMapRanges) ? (n_work + 7) / 8 * 8 : n_work;
-        if (grid > (int64_t)INT32_MAX) return -2;
+        if (n_work > (int64_t)INT32_MAX || !grid_fits(grid, plan.tile_kernel == 2 ? 512 : 256)) return -2;
         if (plan.tile_kernel == 2)
             hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 2>), dim3((unsigned)grid), dim3(512), 0, stream, a,
                                (int)n_work, map);
@@ -1130,15 +1136,11 @@ static int launch_paged_t(const PagedArgs& a, const PagedPlan& plan, hipStream_t
             hipLaunchKernelGGL((paged_chunk_kernel<D, BS, 0>), dim3((unsigned)grid), dim3(256), 0, stream, a,
                                (int)n_work, map);
     }
-    if (a.max_splits > kCombineHeadsMaxSplits) {
-        const int64_t items = (int64_t)a.num_seqs * a.max_q_len * a.H;
-        if ((items + 3) / 4 > (int64_t)UINT32_MAX) return -2;
-        hipLaunchKernelGGL((paged_combine_kernel<D>), dim3((unsigned)((items + 3) / 4)), dim3(256), 0, stream, a);
-    } else if (a.max_splits > 1) {
-        const int64_t waves = (int64_t)a.num_seqs * a.max_q_len * ((a.H + 64 / (D / 8) - 1) / (64 / (D / 8)));
-        if ((waves + 3) / 4 > (int64_t)UINT32_MAX) return -2;
-        hipLaunchKernelGGL((paged_combine_heads_kernel<D>), dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
-    }
+    if (a.max_splits > kCombineHeadsMaxSplits)
+        hipLaunchKernelGGL((paged_combine_kernel<D>), dim3((unsigned)((comb_items + 3) / 4)), dim3(256), 0, stream, a);
+    else if (a.max_splits > 1)
+        hipLaunchKernelGGL((paged_combine_heads_kernel<D>), dim3((unsigned)((comb_waves + 3) / 4)), dim3(256), 0,
+                           stream, a);
     return 0;
 }
 
@@ -1160,7 +1162,7 @@ int launch_gather(const GatherArgs& a, hipStream_t stream)
 {
     const int max_pages = (a.max_ctx_len + a.block_size - 1) / a.block_size;
     const int64_t grid = (int64_t)a.num_seqs * max_pages * a.H;
-    if (grid > (int64_t)INT32_MAX) return -2;
+    if (!grid_fits(grid, 256)) return -2;
     hipLaunchKernelGGL(paged_gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
     return hipGetLastError() == hipSuccess ? 0 : -8;
 }

@@ -286,6 +286,7 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
         const int64_t n_work = bh * per_bh;
         if (n_work > (int64_t)INT32_MAX - 8) return -2;
         a.n_work = (int)n_work;
+        if (!grid_fits((n_work + 7) / 8 * 8, TileCfg<128>::kThreads)) return -2;
         const int grid = (int)((n_work + 7) / 8 * 8);
 #define ATTN_LAUNCH_PREFILL(DD, PP, KK) \
     hipLaunchKernelGGL((prefill_bf16_kernel<DD, PP, KK>), dim3(grid), dim3(TileCfg<DD>::kThreads), 0, stream, a)
@@ -306,7 +307,7 @@ int launch_prefill(const PrefillArgs& in, hipStream_t stream)
     } else {
         const int nqt = (a.N + 63) / 64;
         const int64_t grid = (int64_t)a.B * a.H * nqt;
-        if (grid > (int64_t)INT32_MAX) return -2;
+        if (!grid_fits(grid, 256)) return -2;
         if (a.d == 128)
             hipLaunchKernelGGL(prefill_f32_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a);
         else
