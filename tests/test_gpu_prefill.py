@@ -229,3 +229,21 @@ def test_c3_full_size_sampled_rows():
     og = torch.stack([o[b, h, r] for b, h, r in trip])
     lg = torch.stack([lse[b, h, r] for b, h, r in trip])
     check_close("c3 sampled", og, o_ref, lg, l_ref, torch.bfloat16)
+
+
+def test_grid_past_32bit_work_items_is_a_shape_error():
+    """A grid is a 32-bit count of work-items: 2^25 heads of one row need
+    2^25 workgroups of 256 threads, 2^33 work-items, which the launcher
+    rejects as ATTN_ERR_SHAPE (-2) before launching anything (the buffers are
+    real, so a launch would still be a valid one)."""
+    B, H, N, d = 1 << 17, 256, 1, 128
+    log("grid guard: B=%d H=%d N=%d d=%d (32 GiB of buffers)" % (B, H, N, d))
+    q = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=DEV)
+    k, v, o = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=DEV)
+    rc = attn.attn_prefill_fwd(attn._ptr(q), attn._ptr(k), attn._ptr(v), attn._ptr(o), attn._ptr(lse), B, H, N, d,
+                               1.0 / math.sqrt(d), 1, attn._dtype_code(q), attn._stream(None))
+    torch.cuda.synchronize()
+    assert rc == -2, rc
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
